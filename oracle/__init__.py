@@ -1,0 +1,207 @@
+"""CPU oracle for the tiled dense matrix product (test infrastructure only).
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. It shares no code with the HIP library
+and never imports it.
+
+What it computes, and the passage each function follows:
+
+* ``gemm`` / ``gemm_block`` -- the product itself, C[i,j] = sum_k A[i,k]B[k,j],
+  accumulated in fp64 by a plain C triple loop (``oracle.c``). Definition:
+  "09 计算受限还是访存受限" (compute- vs memory-bound), section on counting a
+  matrix multiply (each output is a sum of N products, N multiplies and N
+  adds); CS336 Lecture 5 GPU notes, §4.2, naive snippet. Row-major layout:
+  CS336 Lecture 5 GPU notes, §4.1 (warning on row-major storage).
+* ``roofline`` -- FLOPs = 2MNK and the ideal byte count (each matrix crosses
+  HBM once: read A and B, write C); intensity = FLOPs / bytes. Same section
+  of the compute- vs memory-bound lesson (2N^3, 12N^2 bytes, N/6), and
+  CS336 Lecture 5 GPU notes, §2.1 (bf16 N = 8192 example).
+* ``attainable`` -- the roofline bound P = min(peak, bandwidth * intensity)
+  and the ridge point peak / bandwidth: CS336 Lecture 5 GPU notes, §2.2.
+* ``parity`` -- the error metrics the tests report: the normalized max error
+  max|C - R| / (max|A| max|B| K) and the relative Frobenius error.
+* ``freivalds`` -- a full-coverage probabilistic check of a product
+  (C x against A (B x) for a random +-1 vector x), used where the full
+  product is too large for the triple loop.
+
+Every function is pinned by tests in ``tests/test_oracle.py`` against values
+the pages print, closed forms (identity, permutation, all-ones, rank-1),
+integer inputs and brute force on tiny shapes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+# gcc flags: no FMA contraction so the arithmetic is exactly the C text.
+CFLAGS = ["-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc. Returns the path."""
+    if force or not os.path.exists(_LIB_PATH) or (
+        os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)
+    ):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build()
+            lib = ctypes.CDLL(_LIB_PATH)
+            i64 = ctypes.c_int64
+            for name in ("oracle_gemm_f32", "oracle_gemm_bf16"):
+                fn = getattr(lib, name)
+                fn.restype = ctypes.c_int
+                fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                               i64, i64, i64, i64, i64, i64, i64, ctypes.c_int]
+            lib.oracle_max_threads.restype = ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def default_threads() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _check_operands(A: np.ndarray, B: np.ndarray):
+    if A.ndim != 2 or B.ndim != 2:
+        raise ValueError("A and B must be 2-D")
+    if A.dtype != B.dtype or A.dtype not in (np.float32, np.uint16):
+        raise TypeError("A and B must both be float32, or both uint16 bf16 bits")
+    if A.shape[1] != B.shape[0]:
+        raise ValueError(f"inner dimensions differ: {A.shape} @ {B.shape}")
+
+
+def gemm_block(A: np.ndarray, B: np.ndarray, rows: tuple[int, int], cols: tuple[int, int],
+               threads: int | None = None) -> np.ndarray:
+    """fp64 block R[i0:i1, j0:j1] of A @ B.
+
+    A[M,K], B[K,N] are row-major float32 arrays, or uint16 arrays of bf16 bits
+    (widened exactly inside the C code).
+    """
+    _check_operands(A, B)
+    A = np.ascontiguousarray(A)
+    B = np.ascontiguousarray(B)
+    M, K = A.shape
+    N = B.shape[1]
+    i0, i1 = rows
+    j0, j1 = cols
+    R = np.empty((max(i1 - i0, 0), max(j1 - j0, 0)), dtype=np.float64)
+    lib = _load()
+    fn = lib.oracle_gemm_f32 if A.dtype == np.float32 else lib.oracle_gemm_bf16
+    rc = fn(A.ctypes.data, B.ctypes.data, R.ctypes.data, M, N, K, i0, i1, j0, j1,
+            int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle rejected block rows={rows} cols={cols} for {A.shape}@{B.shape}")
+    return R
+
+
+def gemm(A: np.ndarray, B: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """Full fp64 product A @ B (see ``gemm_block``)."""
+    _check_operands(A, B)
+    return gemm_block(A, B, (0, A.shape[0]), (0, B.shape[1]), threads)
+
+
+def gemm_tiles(A: np.ndarray, B: np.ndarray, tiles, tile: int = 32,
+               threads: int | None = None) -> list[np.ndarray]:
+    """fp64 tiles of A @ B at the given (row0, col0) corners."""
+    M, N = A.shape[0], B.shape[1]
+    return [gemm_block(A, B, (r, min(r + tile, M)), (c, min(c + tile, N)), threads)
+            for r, c in tiles]
+
+
+def widen(X: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of a float32 array or of an array of bf16 bits."""
+    if X.dtype == np.uint16:
+        return (X.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return X.astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Cost model
+# ---------------------------------------------------------------------------
+
+def roofline(M: int, N: int, K: int, in_bytes: int, out_bytes: int):
+    """(flops, bytes, intensity) of one product with every matrix crossing HBM once.
+
+    flops = 2*M*N*K (a multiply-add counts as two floating-point operations);
+    bytes = (M*K + K*N) * in_bytes + M*N * out_bytes (read A and B, write C).
+    """
+    flops = 2 * M * N * K
+    nbytes = (M * K + K * N) * in_bytes + M * N * out_bytes
+    return flops, nbytes, (flops / nbytes if nbytes else 0.0)
+
+
+def attainable(peak: float, bandwidth: float, intensity: float) -> float:
+    """Roofline: attainable rate = min(peak, bandwidth * intensity)."""
+    return min(peak, bandwidth * intensity)
+
+
+def ridge(peak: float, bandwidth: float) -> float:
+    """Intensity at which the bandwidth slope meets the compute roof."""
+    return peak / bandwidth
+
+
+# ---------------------------------------------------------------------------
+# Checks
+# ---------------------------------------------------------------------------
+
+def parity(C: np.ndarray, R: np.ndarray, max_a: float, max_b: float, K: int) -> dict:
+    """Error metrics of a computed product C against the fp64 oracle R.
+
+    ``norm_max_err`` = max|C - R| / (max|A| * max|B| * K) (0 when that
+    denominator is 0 and C == R); ``rel_fro`` = ||C - R||_F / ||R||_F.
+    """
+    C64 = np.asarray(C, dtype=np.float64)
+    R64 = np.asarray(R, dtype=np.float64)
+    if C64.shape != R64.shape:
+        raise ValueError(f"shape mismatch {C64.shape} vs {R64.shape}")
+    diff = np.abs(C64 - R64)
+    max_abs = float(diff.max()) if diff.size else 0.0
+    denom = float(max_a) * float(max_b) * float(K)
+    if denom > 0:
+        norm = max_abs / denom
+    else:
+        norm = 0.0 if max_abs == 0.0 else float("inf")
+    rn = float(np.linalg.norm(R64)) if R64.size else 0.0
+    dn = float(np.linalg.norm(C64 - R64)) if R64.size else 0.0
+    rel = dn / rn if rn > 0 else (0.0 if dn == 0.0 else float("inf"))
+    return {"norm_max_err": norm, "rel_fro": rel, "max_abs_err": max_abs}
+
+
+def freivalds(A: np.ndarray, B: np.ndarray, C: np.ndarray, x: np.ndarray) -> dict:
+    """Compare C @ x with A @ (B @ x) in fp64 for a +-1 vector x.
+
+    Returns the largest row residual and the scale sum_j |C[i,j]| (max over
+    rows) a caller can turn into a tolerance. Cost O(MK + KN + MN).
+    """
+    A64 = widen(np.asarray(A))
+    B64 = widen(np.asarray(B))
+    C64 = np.asarray(C, dtype=np.float64)
+    x = np.asarray(x, dtype=np.float64)
+    lhs = C64 @ x
+    rhs = A64 @ (B64 @ x)
+    res = np.abs(lhs - rhs)
+    return {
+        "max_residual": float(res.max()) if res.size else 0.0,
+        "max_row_abs_sum": float(np.abs(C64).sum(axis=1).max()) if C64.size else 0.0,
+    }

@@ -1,0 +1,91 @@
+"""Checks of the seeded input generator (shared by the oracle's and the GPU's tests)."""
+import json
+import os
+
+import numpy as np
+import torch
+
+from tiled_dense_matrix_amd import inputs
+
+DIGESTS = os.path.join(os.path.dirname(__file__), "golden", "input_digests.json")
+
+
+def test_digests_are_stable():
+    with open(DIGESTS) as fh:
+        want = json.load(fh)
+    for name, d in want.items():
+        A, B = inputs.make_inputs(name)
+        assert inputs.digest(A) == d["A"], name
+        assert inputs.digest(B) == d["B"], name
+
+
+def test_workload_shapes_and_types():
+    w = inputs.WORKLOADS
+    assert (w["f32_4096"].M, w["f32_4096"].N, w["f32_4096"].K) == (4096, 4096, 4096)
+    assert (w["bf16_mlp"].M, w["bf16_mlp"].N, w["bf16_mlp"].K) == (8192, 14336, 4096)
+    assert (w["bf16_skinny"].M, w["bf16_skinny"].N, w["bf16_skinny"].K) == (16, 8192, 8192)
+    A, B = inputs.make_inputs("f32_256")
+    assert A.dtype == np.float32 and A.shape == (256, 256) and B.shape == (256, 256)
+    A, B = inputs.make_inputs("bf16_skinny")
+    assert A.dtype == np.uint16 and A.shape == (16, 8192) and B.shape == (8192, 8192)
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100_000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-38).astype(np.float32),  # subnormal range
+        np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, -0.0,
+                  3.4e38, -3.4e38], dtype=np.float32),  # exact ties and extremes
+    ])
+    mine = inputs.fp32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+
+
+def test_bf16_ties_go_to_even():
+    # 1 + 2^-8 lies halfway between bf16 1.0 (even) and 1 + 2^-7 (odd).
+    assert inputs.fp32_to_bf16_bits(np.array([1.0 + 2.0 ** -8], np.float32))[0] == 0x3F80
+    # 1 + 3*2^-8 lies halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+    assert inputs.fp32_to_bf16_bits(np.array([1.0 + 3 * 2.0 ** -8], np.float32))[0] == 0x3F82
+    assert inputs.bf16_bits_to_fp32(np.array([0x3F82], np.uint16))[0] == 1.0 + 2.0 ** -6
+
+
+def test_distributions():
+    A, B = inputs.make_inputs("f32_256")
+    assert A.min() >= -1.0 and A.max() < 1.0
+    assert abs(float(A.mean())) < 0.01 and abs(float(A.var()) - 1.0 / 3.0) < 0.01
+    A, B = inputs.make_inputs("bf16_skinny")
+    a = inputs.bf16_bits_to_fp32(A).astype(np.float64)
+    b = inputs.bf16_bits_to_fp32(B[:512]).astype(np.float64)
+    assert abs(a.std() - 1.0) < 0.01
+    assert abs(b.std() - 0.02) < 0.0005
+
+
+def test_seeds_and_draw_order():
+    A1, B1 = inputs.make_inputs(inputs.Workload("x", "f32", 8, 9, 10, 5, "uniform"))
+    A2, B2 = inputs.make_inputs(inputs.Workload("x", "f32", 8, 9, 10, 5, "uniform"))
+    A3, _ = inputs.make_inputs(inputs.Workload("x", "f32", 8, 9, 10, 6, "uniform"))
+    assert np.array_equal(A1, A2) and np.array_equal(B1, B2)
+    assert not np.array_equal(A1, A3)
+    # A is drawn first from the seed's stream, then B.
+    rng = np.random.default_rng(5)
+    assert np.array_equal(A1, rng.uniform(-1.0, 1.0, (8, 10)).astype(np.float32))
+    assert np.array_equal(B1, rng.uniform(-1.0, 1.0, (10, 9)).astype(np.float32))
+
+
+def test_sample_tiles():
+    t = inputs.sample_tiles(8192, 14336)
+    assert len(t) == 64 and len(set(t)) == 64
+    assert all(r % 32 == 0 and c % 32 == 0 and 0 <= r < 8192 and 0 <= c < 14336 for r, c in t)
+    assert t == inputs.sample_tiles(8192, 14336)
+    assert len(inputs.sample_tiles(64, 64)) == 4
+
+
+def test_small_int_and_pm_one():
+    rng = np.random.default_rng(1)
+    X = inputs.small_int_matrix(rng, (50, 60), kind="bf16")
+    v = inputs.bf16_bits_to_fp32(X)
+    assert set(np.unique(v).tolist()) <= set(range(-3, 4))
+    x = inputs.pm_one_vector(rng, 1000)
+    assert set(np.unique(x).tolist()) == {-1.0, 1.0}

@@ -1,0 +1,376 @@
+"""Pins of the CPU oracle against facts fixed outside the oracle itself.
+
+The oracle computes C[i,j] = sum_k A[i,k] B[k,j] in fp64 ("09 计算受限还是访存受限",
+section on counting a matrix multiply; CS336 Lecture 5 GPU notes, §4.2). It is
+pinned here by:
+
+* closed forms that hold exactly in fp64: identity and permutation operands,
+  all-ones (every element equals K), rank-1 integer outer products;
+* integer inputs, whose exact product is known from integer arithmetic;
+* brute force on tiny shapes against an exactly rounded sum (math.fsum),
+  within the fp64 summation bound;
+* NumPy's fp64 matmul as an independent library routine;
+* the bf16 bit patterns of known values;
+* the worked numbers the pages print for the cost model and the roofline
+  (tests/golden/pages_worked_numbers.json).
+
+The last test plants plausible mistakes in small pure-Python copies of the
+oracle (a dropped term, a sign error, a transposed operand, swapped indices,
+a wrong bf16 widening, shifted block offsets) and checks that the pins catch
+every one of them.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from tiled_dense_matrix_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_worked_numbers.json")
+U = 2.0 ** -53
+
+TINY = [1, 2, 3, 5, 7, 8, 16, 17, 31, 33]
+
+
+def _f32(rng, shape):
+    return inputs.uniform_fp32(rng, shape)
+
+
+def _as_kind(X64, kind):
+    """Store exact small values as fp32 or as bf16 bits."""
+    X32 = np.asarray(X64, dtype=np.float32)
+    return X32 if kind == "f32" else inputs.fp32_to_bf16_bits(X32)
+
+
+# ---------------------------------------------------------------------------
+# Pin suites: each takes a product function f(A, B) -> fp64 array and raises
+# AssertionError when f disagrees with the fact it checks.
+# ---------------------------------------------------------------------------
+
+def pin_identity(f, kind="f32", shapes=((5, 7, 3), (16, 4, 9), (1, 8, 1))):
+    rng = np.random.default_rng(11)
+    for M, N, K in shapes:
+        B = _as_kind(rng.integers(-50, 50, size=(M, N)), kind)  # K == M for A = I
+        R = f(_as_kind(np.eye(M), kind), B)
+        assert np.array_equal(R, oracle.widen(B)), "I @ B != B"
+        A = _as_kind(rng.integers(-50, 50, size=(M, K)), kind)
+        R = f(A, _as_kind(np.eye(K), kind))
+        assert np.array_equal(R, oracle.widen(A)), "A @ I != A"
+
+
+def pin_permutation(f, kind="f32"):
+    rng = np.random.default_rng(12)
+    for M, N in ((6, 9), (17, 3)):
+        perm = rng.permutation(M)
+        P = np.zeros((M, M))
+        P[np.arange(M), perm] = 1.0  # (P @ B)[i] = B[perm[i]]
+        Bv = rng.integers(-100, 100, size=(M, N))
+        R = f(_as_kind(P, kind), _as_kind(Bv, kind))
+        assert np.array_equal(R, Bv[perm].astype(np.float64)), "P @ B != rows of B permuted"
+        Av = rng.integers(-100, 100, size=(N, M))
+        R = f(_as_kind(Av, kind), _as_kind(P, kind))  # (A @ P)[:, perm[i]] = A[:, i]
+        expect = np.empty_like(Av)
+        expect[:, perm] = Av
+        assert np.array_equal(R, expect.astype(np.float64)), "A @ P != columns of A permuted"
+
+
+def pin_all_ones(f, kind="f32", shapes=((3, 4, 5), (1, 1, 1), (7, 2, 129), (2, 3, 1000))):
+    for M, N, K in shapes:
+        R = f(_as_kind(np.ones((M, K)), kind), _as_kind(np.ones((K, N)), kind))
+        assert R.shape == (M, N)
+        assert np.all(R == K), "all-ones product is not K everywhere"
+
+
+def pin_rank1(f, kind="f32"):
+    rng = np.random.default_rng(13)
+    for M, N, K in ((4, 6, 5), (9, 3, 12)):
+        u, s = rng.integers(-4, 5, size=M), rng.integers(-4, 5, size=K)
+        t, v = rng.integers(-4, 5, size=K), rng.integers(-4, 5, size=N)
+        A, B = np.outer(u, s), np.outer(t, v)
+        R = f(_as_kind(A, kind), _as_kind(B, kind))
+        expect = float(np.dot(s, t)) * np.outer(u, v).astype(np.float64)
+        assert np.array_equal(R, expect), "rank-1 closed form violated"
+
+
+def pin_integers(f, kind="f32"):
+    rng = np.random.default_rng(14)
+    for M, N, K in ((5, 6, 7), (16, 17, 31), (3, 2, 257)):
+        A = rng.integers(-3, 4, size=(M, K))
+        B = rng.integers(-3, 4, size=(K, N))
+        R = f(_as_kind(A, kind), _as_kind(B, kind))
+        assert np.array_equal(R, (A.astype(np.int64) @ B.astype(np.int64)).astype(np.float64)), \
+            "integer product differs from exact integer arithmetic"
+
+
+def pin_brute_force(f, sizes=TINY, count=40):
+    """Random fp32 inputs on tiny shapes vs an exactly rounded sum (math.fsum)."""
+    rng = np.random.default_rng(15)
+    for _ in range(count):
+        M, N, K = (int(rng.choice(sizes)) for _ in range(3))
+        A = _f32(rng, (M, K))
+        B = _f32(rng, (K, N))
+        R = f(A, B)
+        assert R.shape == (M, N)
+        A64, B64 = A.astype(np.float64), B.astype(np.float64)
+        for i in range(M):
+            for j in range(N):
+                terms = [A64[i, k] * B64[k, j] for k in range(K)]  # exact in fp64
+                exact = math.fsum(terms)
+                bound = (K + 1) * U * math.fsum(abs(x) for x in terms)
+                assert abs(R[i, j] - exact) <= bound, (M, N, K, i, j)
+
+
+def pin_bf16_values(f):
+    """Known bf16 bit patterns through a 1x1x1 product with 1.0."""
+    cases = {
+        0x3F80: 1.0, 0xBF80: -1.0, 0xC040: -3.0, 0x3F81: 1.0 + 2.0 ** -7,
+        0x4049: 3.140625, 0x0001: 2.0 ** -133, 0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,
+        0x0000: 0.0, 0x3C00: 2.0 ** -7,
+    }
+    one = np.array([[0x3F80]], dtype=np.uint16)
+    for bits, value in cases.items():
+        R = f(np.array([[bits]], dtype=np.uint16), one)
+        assert R[0, 0] == value, hex(bits)
+
+
+ALL_PINS = [pin_identity, pin_permutation, pin_all_ones, pin_rank1, pin_integers]
+
+
+# ---------------------------------------------------------------------------
+# The real oracle passes every pin.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+@pytest.mark.parametrize("pin", ALL_PINS, ids=lambda p: p.__name__)
+def test_closed_forms(pin, kind):
+    pin(oracle.gemm, kind)
+
+
+def test_brute_force_fsum():
+    pin_brute_force(oracle.gemm)
+
+
+def test_bf16_widening():
+    pin_bf16_values(oracle.gemm)
+
+
+def test_matches_numpy_fp64():
+    rng = np.random.default_rng(16)
+    for M, N, K in ((64, 48, 200), (33, 65, 129), (128, 96, 1024)):
+        A, B = _f32(rng, (M, K)), _f32(rng, (K, N))
+        R = oracle.gemm(A, B)
+        ref = A.astype(np.float64) @ B.astype(np.float64)
+        scale = np.abs(A.astype(np.float64)) @ np.abs(B.astype(np.float64))
+        assert np.all(np.abs(R - ref) <= 2 * (K + 1) * U * scale)
+
+
+def test_bf16_matches_numpy_fp64():
+    rng = np.random.default_rng(17)
+    A = inputs.normal_bf16(rng, (40, 300), 1.0)
+    B = inputs.normal_bf16(rng, (300, 50), 0.02)
+    R = oracle.gemm(A, B)
+    A64, B64 = oracle.widen(A), oracle.widen(B)
+    scale = np.abs(A64) @ np.abs(B64)
+    assert np.all(np.abs(R - A64 @ B64) <= 2 * 301 * U * scale)
+
+
+def test_blocks_equal_full_product():
+    rng = np.random.default_rng(18)
+    A, B = _f32(rng, (70, 90)), _f32(rng, (90, 110))
+    full = oracle.gemm(A, B)
+    for (i0, i1), (j0, j1) in (((0, 70), (0, 110)), ((3, 40), (17, 18)), ((69, 70), (0, 32)),
+                               ((32, 64), (96, 110))):
+        assert np.array_equal(oracle.gemm_block(A, B, (i0, i1), (j0, j1)), full[i0:i1, j0:j1])
+    tiles = [(0, 0), (32, 64), (64, 96)]
+    for (r, c), T in zip(tiles, oracle.gemm_tiles(A, B, tiles)):
+        assert np.array_equal(T, full[r:r + 32, c:c + 32])
+
+
+def test_thread_count_does_not_change_bits():
+    rng = np.random.default_rng(19)
+    A, B = _f32(rng, (97, 300)), _f32(rng, (300, 61))
+    assert np.array_equal(oracle.gemm(A, B, threads=1), oracle.gemm(A, B, threads=8))
+
+
+def test_empty_shapes():
+    z = np.zeros((0, 5), np.float32)
+    assert oracle.gemm(z, np.zeros((5, 3), np.float32)).shape == (0, 3)
+    R = oracle.gemm(np.zeros((4, 0), np.float32), np.zeros((0, 6), np.float32))
+    assert R.shape == (4, 6) and np.all(R == 0.0)  # empty sum
+
+
+def test_rejects_bad_operands():
+    with pytest.raises(ValueError):
+        oracle.gemm(np.zeros((2, 3), np.float32), np.zeros((4, 2), np.float32))
+    with pytest.raises(TypeError):
+        oracle.gemm(np.zeros((2, 3), np.float64), np.zeros((3, 2), np.float64))
+    with pytest.raises(ValueError):
+        oracle.gemm_block(np.zeros((2, 3), np.float32), np.zeros((3, 2), np.float32), (0, 3), (0, 2))
+
+
+# ---------------------------------------------------------------------------
+# Cost model and roofline against the pages' printed numbers.
+# ---------------------------------------------------------------------------
+
+def _golden():
+    with open(GOLDEN) as fh:
+        return json.load(fh)
+
+
+def _close(got, want, rel):
+    return abs(got - want) <= rel * abs(want)
+
+
+def test_roofline_cost_matches_pages():
+    for e in _golden()["matmul_cost"]:
+        flops, nbytes, ai = oracle.roofline(e["M"], e["N"], e["K"], e["in_bytes"], e["out_bytes"])
+        if "flops" in e:
+            assert _close(flops, e["flops"], e["flops_rel_tol"]), e["cite"]
+        if "bytes" in e:
+            assert _close(nbytes, e["bytes"], e["bytes_rel_tol"]), e["cite"]
+        assert _close(ai, e["intensity"], e["intensity_rel_tol"]), e["cite"]
+
+
+def test_square_fp32_intensity_is_n_over_6():
+    for n in (1, 6, 256, 4096, 12345):
+        assert math.isclose(oracle.roofline(n, n, n, 4, 4)[2], n / 6)
+
+
+def test_ridge_and_attainable_match_pages():
+    g = _golden()
+    for e in g["roofline"]:
+        assert _close(oracle.ridge(e["peak"], e["bandwidth"]), e["ridge"], e["ridge_rel_tol"]), e["cite"]
+    for e in g["attainable"]:
+        got = oracle.attainable(e["peak"], e["bandwidth"], e["flops"] / e["bytes"])
+        assert _close(got, e["attained"], e["rel_tol"]), e["cite"]
+
+
+def test_times_and_classification_match_pages():
+    g = _golden()
+    for e in g["times"]:
+        if "M" in e:
+            flops, nbytes, ai = oracle.roofline(e["M"], e["N"], e["K"], e["in_bytes"], e["out_bytes"])
+            assert _close(flops / e["peak"], e["compute_s"], e["compute_rel_tol"]), e["cite"]
+            assert _close(nbytes / e["bandwidth"], e["data_s"], e["data_rel_tol"]), e["cite"]
+            bound = "compute" if ai > oracle.ridge(e["peak"], e["bandwidth"]) else "memory"
+            assert bound == e["bound"], e["cite"]
+        else:
+            assert _close(e["bytes"] / e["bandwidth"], e["data_s"], e["data_rel_tol"]), e["cite"]
+    for e in g["classification"]:
+        ai = oracle.roofline(e["M"], e["N"], e["K"], e["in_bytes"], e["out_bytes"])[2]
+        bound = "compute" if ai > oracle.ridge(e["peak"], e["bandwidth"]) else "memory"
+        assert bound == e["bound"], e["cite"]
+
+
+# ---------------------------------------------------------------------------
+# Error metrics and Freivalds check.
+# ---------------------------------------------------------------------------
+
+def test_parity_metric_hand_values():
+    R = np.arange(12, dtype=np.float64).reshape(3, 4)
+    p = oracle.parity(R.copy(), R, 2.0, 3.0, 5)
+    assert p["norm_max_err"] == 0.0 and p["rel_fro"] == 0.0
+    C = R.copy()
+    C[1, 2] += 0.3
+    p = oracle.parity(C, R, 2.0, 3.0, 5)
+    assert math.isclose(p["norm_max_err"], 0.3 / 30.0)
+    assert math.isclose(p["rel_fro"], 0.3 / math.sqrt(float((R ** 2).sum())))
+    assert oracle.parity(np.zeros_like(R), R, 2.0, 3.0, 5)["rel_fro"] == 1.0
+    # A zero denominator demands an exact zero result.
+    assert oracle.parity(np.zeros((2, 2)), np.zeros((2, 2)), 0.0, 1.0, 4)["norm_max_err"] == 0.0
+    assert oracle.parity(np.ones((2, 2)), np.zeros((2, 2)), 0.0, 1.0, 4)["norm_max_err"] == math.inf
+
+
+def test_freivalds_detects_a_corrupted_element():
+    rng = np.random.default_rng(20)
+    A, B = _f32(rng, (50, 70)), _f32(rng, (70, 40))
+    R = oracle.gemm(A, B)
+    x = inputs.pm_one_vector(rng, 40)
+    good = oracle.freivalds(A, B, R, x)
+    assert good["max_residual"] <= 1e-12 * good["max_row_abs_sum"]
+    bad = R.copy()
+    bad[7, 11] += 0.5
+    assert math.isclose(oracle.freivalds(A, B, bad, x)["max_residual"], 0.5, rel_tol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: small pure-Python oracles with one plausible bug each.
+# Every one must fail at least one pin.
+# ---------------------------------------------------------------------------
+
+def _py_oracle(bug=None):
+    def widen(X):
+        if X.dtype == np.uint16:
+            shift = 15 if bug == "bf16_shift" else 16
+            return ((X.astype(np.uint64) << shift) & 0xFFFFFFFF).astype(np.uint32).view(np.float32) \
+                .astype(np.float64)
+        return X.astype(np.float64)
+
+    def f(A, B):
+        A64, B64 = widen(A), widen(B)
+        M, K = A64.shape
+        N = B64.shape[1]
+        R = np.zeros((M, N))
+        for i in range(M):
+            for j in range(N):
+                s = 0.0
+                kmax = K - 1 if bug == "drop_last_term" else K
+                for k in range(kmax):
+                    if bug == "transpose_b":
+                        b = B64[j, k] if j < B64.shape[0] and k < B64.shape[1] else 0.0
+                    else:
+                        b = B64[k, j]
+                    if bug == "swap_a_index":
+                        a = A64[k, i] if k < M and i < K else 0.0
+                    else:
+                        a = A64[i, k]
+                    term = a * b
+                    if bug == "sign_last" and k == K - 1:
+                        term = -term
+                    s += term
+                R[i, j] = s
+        if bug == "first_row_zero":
+            R[0, :] = 0.0
+        return R
+    return f
+
+
+BUGS = ["drop_last_term", "transpose_b", "swap_a_index", "sign_last", "bf16_shift",
+        "first_row_zero"]
+
+
+def _run_pins(f):
+    failures = 0
+    small = [1, 2, 3, 5]
+    for pin in ALL_PINS:
+        for kind in ("f32", "bf16"):
+            try:
+                pin(f, kind)
+            except (AssertionError, IndexError, ValueError):
+                failures += 1
+    for pin in (lambda g: pin_brute_force(g, sizes=small, count=8), pin_bf16_values):
+        try:
+            pin(f)
+        except (AssertionError, IndexError, ValueError):
+            failures += 1
+    return failures
+
+
+def test_correct_python_copy_passes_pins():
+    assert _run_pins(_py_oracle()) == 0
+
+
+@pytest.mark.parametrize("bug", BUGS)
+def test_planted_mistake_is_caught(bug):
+    assert _run_pins(_py_oracle(bug)) > 0, bug
+
+
+def test_block_offset_mistake_is_caught():
+    rng = np.random.default_rng(21)
+    A, B = _f32(rng, (40, 50)), _f32(rng, (50, 60))
+    full = oracle.gemm(A, B)
+    shifted = oracle.gemm_block(A, B, (1, 33), (0, 32))  # a block taken one row off
+    assert not np.array_equal(shifted, full[0:32, 0:32])
