@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Throughput of the tiled dense product on one MI355X, against its roofline.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one call of the library's C ABI (gemm_f32 / gemm_bf16_f32acc) on
+one set of synthetic inputs already resident in HBM: cost model and path
+choice on the host, then the tiled kernel (tile schedule, coalesced loads,
+LDS staging, pipelined K loop, MFMA/FMA accumulation, C write-back).
+Consecutive steps rotate over several copies of (A, B, C) whose total size
+exceeds the 256 MB last-level cache, so every step reads its operands from
+HBM.
+
+The timed region is bracketed by device synchronisation, with HIP events
+recorded on the stream the kernels are launched on. One JSON line is
+printed; besides the throughput it carries:
+  roofline      achieved rate of the product's kernel (algorithmic FLOPs or
+                bytes per launch / average launch time) against MI355X's
+                published peak for the bound that applies; `traffic` is the
+                measured HBM bytes per launch from rocprofv3 counters when a
+                counter record for the current kernel source exists;
+  cpu_baseline  the CPU oracle (plain fp64 triple loop) timed on a bounded
+                sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+# MI355X published peaks (dense).
+PEAK = {
+    "mfma_bf16": 2516.6,  # TFLOP/s
+    "mfma_f32": 157.3,    # TFLOP/s
+    "alu_f32": 157.3,     # TFLOP/s, fp32 vector
+    "hbm": 8000.0,        # GB/s
+}
+KERNEL = {  # path -> (kernel symbol, source file)
+    "edge": ("edge_kernel", "gemm_edge.hip"),
+    "valu": ("valu_f32_kernel", "gemm_valu_f32.hip"),
+    "mfma": ("mfma_bf16_kernel", "gemm_mfma_bf16.hip"),
+    "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip"),
+}
+DEFAULT_WORKLOAD = "f32_4096"
+ROTATE_BYTES = 640 << 20  # working set across rotated copies
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--path", default="auto", help="force a path (edge/valu/mfma/skinny)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the product, run a plain device copy of this many MiB "
+                         "(reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def src_digest(fname: str) -> str:
+    path = os.path.join(ROOT, "tiled_dense_matrix_amd", "csrc", fname)
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def traffic_record(kernel: str, src: str, workload: str):
+    """HBM bytes per launch from a committed counter record, if still valid."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha") != src_digest(src):
+        return None  # the kernel changed since the counters were taken
+    return float(rec["hbm_bytes_per_launch"])
+
+
+def copy_probe(mib: int):
+    import torch
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_read": n * 4, "copy_probe_bytes_written": n * 4,
+                      "launches": 5}), flush=True)
+
+
+def cpu_baseline(w, A, B, C_gpu, target_s: float):
+    """Time the oracle on the first rows of C; also check those rows."""
+    import oracle
+    threads = oracle.default_threads()
+    rows = 1
+    t0 = time.perf_counter()
+    oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
+    t1 = max(time.perf_counter() - t0, 1e-6)
+    rows = int(min(w.M, max(1, math.floor(target_s / t1))))
+    rows = max(1, min(rows, w.M))
+    t0 = time.perf_counter()
+    R = oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    ma = float(np.abs(oracle.widen(A)).max())
+    mb = float(np.abs(oracle.widen(B)).max())
+    p = oracle.parity(C_gpu[:rows], R, ma, mb, w.K)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, {flops / 1e9:.1f} GFLOP) "
+                  f"in {dt:.1f} s, fp64 triple loop",
+        "sample_parity": {k: float(f"{v:.3e}") for k, v in p.items()},
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported: this library has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_dense_matrix_amd as tdm
+    from tiled_dense_matrix_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+        return
+
+    w = inputs.WORKLOADS[args.workload]
+    kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
+    path = tdm.Path[args.path.upper()]
+    chosen = tdm.tdm_select_path(kind, w.M, w.N, w.K) if path == tdm.Path.AUTO else path
+    pname = tdm.path_name(chosen)
+    kernel, ksrc = KERNEL[pname]
+
+    A, B = inputs.make_inputs(w)
+
+    def dev(X):
+        if X.dtype == np.uint16:
+            X = X.view(np.int16)
+        return torch.from_numpy(X).cuda()
+
+    A0, B0 = dev(A), dev(B)
+    set_bytes = A0.numel() * A0.element_size() + B0.numel() * B0.element_size() + w.M * w.N * 4
+    rot = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    sets = [(A0, B0, torch.empty((w.M, w.N), dtype=torch.float32, device="cuda"))]
+    for _ in range(rot - 1):
+        sets.append((A0.clone(), B0.clone(), torch.empty_like(sets[0][2])))
+
+    fn = tdm.tdm_gemm_f32_path if w.kind == "f32" else tdm.tdm_gemm_bf16_f32acc_path
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        a, b, c = sets[i % rot]
+        fn(a, b, c, path=path, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    roof = tdm.gemm_roofline(kind, w.M, w.N, w.K)
+    tflops = roof.flops / (ms * 1e-3) / 1e12
+    gbs = roof.bytes / (ms * 1e-3) / 1e9
+    if pname == "skinny":
+        bound, unit, achieved, peak = "hbm", "GB/s", gbs, PEAK["hbm"]
+    elif pname == "mfma":
+        bound, unit, achieved, peak = "mfma", "TFLOP/s", tflops, PEAK["mfma_bf16"]
+    else:
+        bound, unit, achieved, peak = "alu", "TFLOP/s", tflops, PEAK["alu_f32"]
+    traffic = traffic_record(kernel, ksrc, w.name)
+
+    # Every rotated copy must hold the same product (spot check: first rows).
+    C_gpu = sets[(args.warmup + args.steps - 1) % rot][2].cpu().numpy()
+    if args.warmup + args.steps >= rot:
+        for a, b, c in sets[1:]:
+            assert torch.equal(c[:4], sets[0][2][:4]), "rotated copies disagree"
+
+    line = {
+        "metric": "GEMM TFLOP/s and % of MFMA/VALU/HBM roofline per shape, 1x MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.kind == "f32" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "inputs": f"seed {w.seed}, {w.dist}",
+                   "path": pname, "kernel": kernel, "rotated_copies": rot,
+                   "gbps_algorithmic": round(gbs, 1)},
+        "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "frac": round(achieved / peak, 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes": int(roof.bytes), "algorithmic_flops": int(roof.flops)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, A, B, C_gpu, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,147 @@
+/*
+ * tdm.h -- tiled dense matrix multiply for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libtdm.so. Plain pointers and sizes only.
+ *
+ * The operation is the dense matrix product C = A * B with
+ *   C[i,j] = sum_{k < K} A[i,k] * B[k,j],   0 <= i < M, 0 <= j < N,
+ * as defined in "09 计算受限还是访存受限" (compute- vs memory-bound lesson),
+ * section on counting a matrix multiply, and in the CS336 Lecture 5 GPU
+ * notes, §4.2 (C = AB for an M x K by K x N product).
+ *
+ * Layout contract (all GEMM entry points):
+ *   - A is M x K, B is K x N, C is M x N, all row-major and dense: element
+ *     (r, c) of an R x S matrix lives at base + r*S + c (CS336 Lecture 5 GPU
+ *     notes, §4.1, on row-major storage). There are no leading dimensions;
+ *     a strided or transposed view must be made contiguous by the caller.
+ *   - A, B and C are DEVICE pointers on the current HIP device, owned by the
+ *     caller. The library allocates no memory in these calls.
+ *   - A and B are read only. C is overwritten (there is no alpha/beta). C
+ *     must not overlap A or B.
+ *   - Element sizes: fp32 = 4 bytes; bf16 = 2 bytes passed as raw uint16_t
+ *     bits (the upper half of an IEEE fp32 word, CS336 Lecture 5 GPU notes,
+ *     §3.1). Pointers must be aligned to their element size.
+ *
+ * Execution: every GEMM call is asynchronous on `stream` (a hipStream_t;
+ * NULL means the default stream) and returns once the work is enqueued.
+ * Faults during execution surface at the caller's next synchronization.
+ *
+ * Errors: arguments are validated on the host before any HIP call.
+ *   - NULL pointer (with M*N > 0 and, for A/B, K > 0), negative size, or a
+ *     misaligned pointer                                -> TDM_ERROR_INVALID_VALUE
+ *   - a matrix with 2^31 or more elements, or a forced path that cannot run
+ *     the given shape/alignment                         -> TDM_ERROR_NOT_SUPPORTED
+ *   - no HIP device is visible                          -> TDM_ERROR_NO_DEVICE
+ *   - the kernel launch failed                          -> TDM_ERROR_LAUNCH
+ *   - M == 0 or N == 0: nothing to do, TDM_SUCCESS without any HIP call.
+ *   - K == 0: C is filled with zeros (the empty sum), TDM_SUCCESS.
+ *
+ * Threading: the calls keep no mutable global state and may be made from
+ * several host threads; work on one stream is ordered as usual.
+ */
+#ifndef TDM_H
+#define TDM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TDM_VERSION 1
+
+/* Symbols of the C ABI are the only ones libtdm.so exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define TDM_API __attribute__((visibility("default")))
+#else
+#define TDM_API
+#endif
+
+typedef enum tdm_status {
+  TDM_SUCCESS = 0,
+  TDM_ERROR_INVALID_VALUE = 1,
+  TDM_ERROR_NOT_SUPPORTED = 2,
+  TDM_ERROR_NO_DEVICE = 3,
+  TDM_ERROR_LAUNCH = 4
+} tdm_status;
+
+/* Which product a roofline query describes. */
+typedef enum tdm_kind {
+  TDM_KIND_F32 = 0,          /* fp32 in, fp32 accumulate, fp32 out         */
+  TDM_KIND_BF16_F32ACC = 1   /* bf16 in, fp32 accumulate, fp32 out         */
+} tdm_kind;
+
+/* Kernel families behind the GEMM calls. */
+typedef enum tdm_path {
+  TDM_PATH_AUTO = 0,   /* let the dispatcher choose (what gemm_* do)        */
+  TDM_PATH_EDGE = 1,   /* 32x32 LDS-tiled kernel: any shape and alignment    */
+  TDM_PATH_VALU = 2,   /* fp32 only: register- and LDS-tiled vector FMA      */
+  TDM_PATH_MFMA = 3,   /* bf16 only: matrix cores, fp32 accumulate           */
+  TDM_PATH_SKINNY = 4  /* bf16 only, M <= 16: streams B once at HBM rate     */
+} tdm_path;
+
+/* Cost of one call with every matrix crossing HBM exactly once. */
+typedef struct tdm_roofline {
+  double flops;      /* 2*M*N*K                                             */
+  double bytes;      /* (M*K + K*N)*in_size + M*N*4                         */
+  double intensity;  /* flops / bytes (0 when bytes == 0)                   */
+} tdm_roofline;
+
+/* C = A * B in fp32: fp32 inputs, fp32 accumulation, fp32 output.
+ * Definition: compute- vs memory-bound lesson, counting a matrix multiply. */
+TDM_API tdm_status gemm_f32(const float* A, const float* B, float* C, int64_t M,
+                    int64_t N, int64_t K, void* stream);
+
+/* C = A * B with bf16 inputs (uint16_t bits), fp32 accumulation and fp32
+ * output: the mixed-precision scheme of the CS336 Lecture 5 GPU notes, §3.2
+ * (low-precision matrix products, fp32 accumulation). Each product of two
+ * bf16 values is exact in fp32; only the sums round. */
+TDM_API tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C,
+                            int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Host-only cost query; touches no device. FLOPs = 2MNK (a multiply-add is
+ * two operations) and bytes = reading A and B once and writing C once
+ * (compute- vs memory-bound lesson, counting a matrix multiply; CS336
+ * Lecture 5 GPU notes, §2.1). C is fp32 (4 bytes) for both kinds.
+ * Errors: out == NULL, a negative size or an unknown kind ->
+ * TDM_ERROR_INVALID_VALUE; products overflowing double are not checked. */
+TDM_API tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K,
+                         tdm_roofline* out);
+
+/* Static, NUL-terminated description of a status code ("unknown status" for
+ * values outside the enum). Never NULL. */
+TDM_API const char* tdm_status_string(tdm_status s);
+
+/* Same as gemm_f32 / gemm_bf16_f32acc, but run the given path. Returns
+ * TDM_ERROR_NOT_SUPPORTED if that path cannot handle the dtype, shape or
+ * alignment (see tdm_path_supports); TDM_PATH_AUTO behaves like gemm_*. */
+TDM_API tdm_status tdm_gemm_f32_path(const float* A, const float* B, float* C,
+                             int64_t M, int64_t N, int64_t K, tdm_path path,
+                             void* stream);
+TDM_API tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B,
+                                     float* C, int64_t M, int64_t N, int64_t K,
+                                     tdm_path path, void* stream);
+
+/* Host-only: 1 if `path` can run this product with these pointer
+ * alignments (pass the byte offsets of A, B and C modulo 16, or 0), else 0. */
+TDM_API int tdm_path_supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N,
+                      int64_t K, int misalign_a, int misalign_b,
+                      int misalign_c);
+
+/* Host-only: the path gemm_* picks for this product (assuming 16-byte
+ * aligned pointers). The choice compares the product's arithmetic intensity
+ * with the ridge point of the target unit (CS336 Lecture 5 GPU notes, §2.2;
+ * compute- vs memory-bound lesson, the quick test against the ridge). */
+TDM_API tdm_path tdm_select_path(tdm_kind kind, int64_t M, int64_t N, int64_t K);
+
+/* Static name of a path ("auto", "edge", "valu", "mfma", "skinny"). */
+TDM_API const char* tdm_path_name(tdm_path p);
+
+/* TDM_VERSION of the built library. */
+TDM_API int tdm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TDM_H */

@@ -191,8 +191,10 @@ def parity(C: np.ndarray, R: np.ndarray, max_a: float, max_b: float, K: int) -> 
 def freivalds(A: np.ndarray, B: np.ndarray, C: np.ndarray, x: np.ndarray) -> dict:
     """Compare C @ x with A @ (B @ x) in fp64 for a +-1 vector x.
 
-    Returns the largest row residual and the scale sum_j |C[i,j]| (max over
-    rows) a caller can turn into a tolerance. Cost O(MK + KN + MN).
+    Returns the largest row residual, the residual's 2-norm, the scale
+    sum_j |C[i,j]| (max over rows) and ||C||_F, from which a caller forms a
+    tolerance. For random +-1 x, E||(C - R) x||^2 = ||C - R||_F^2 (R the exact
+    product). Cost O(MK + KN + MN).
     """
     A64 = widen(np.asarray(A))
     B64 = widen(np.asarray(B))
@@ -203,5 +205,7 @@ def freivalds(A: np.ndarray, B: np.ndarray, C: np.ndarray, x: np.ndarray) -> dic
     res = np.abs(lhs - rhs)
     return {
         "max_residual": float(res.max()) if res.size else 0.0,
+        "residual_norm": float(np.linalg.norm(res)),
         "max_row_abs_sum": float(np.abs(C64).sum(axis=1).max()) if C64.size else 0.0,
+        "c_fro": float(np.linalg.norm(C64)),
     }

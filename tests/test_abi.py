@@ -1,0 +1,165 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+libtdm.so must load without a GPU, export every function include/tdm.h
+declares, validate arguments before touching any device, and answer the
+host-only queries (cost model, path choice) correctly.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+import tiled_dense_matrix_amd as tdm
+from tiled_dense_matrix_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tdm.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"TDM_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for required in ("gemm_f32", "gemm_bf16_f32acc", "gemm_roofline", "tdm_status_string"):
+        assert required in names
+    assert set(names) == set(_lib.SIGNATURES), "binding and header disagree"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_the_c_abi_is_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(declared_functions())
+
+
+def test_version_and_strings():
+    assert tdm.version() == 1
+    assert tdm.status_string(0) == "success"
+    assert tdm.status_string(1) == "invalid value"
+    assert tdm.status_string(99) == "unknown status"
+    assert [tdm.path_name(p) for p in range(5)] == ["auto", "edge", "valu", "mfma", "skinny"]
+    assert tdm.path_name(42) == "unknown"
+
+
+# ---------------------------------------------------------------------------
+# Validation happens before any HIP call: these run identically without a GPU.
+# ---------------------------------------------------------------------------
+
+FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16_f32acc"])
+def test_validation(fn):
+    lib = tdm.load()
+    f = getattr(lib, fn)
+    S = tdm.Status
+    assert f(FAKE, FAKE, FAKE, -1, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, 4, -1, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE, 4, 4, -1, None) == S.ERROR_INVALID_VALUE
+    assert f(None, FAKE, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, None, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, None, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE, FAKE + 1, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # C misaligned
+    assert f(FAKE + 1, FAKE, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # A misaligned
+    # Empty outputs are a no-op, with or without pointers and device.
+    assert f(None, None, None, 0, 4, 4, None) == S.SUCCESS
+    assert f(None, None, None, 4, 0, 4, None) == S.SUCCESS
+    # 2^31 elements in one matrix is beyond 32-bit indexing.
+    assert f(FAKE, FAKE, FAKE, 1 << 16, 1 << 15, 1, None) == S.ERROR_NOT_SUPPORTED
+    assert f(FAKE, FAKE, FAKE, 1, 1 << 20, 1 << 11, None) == S.ERROR_NOT_SUPPORTED
+
+
+def test_validation_with_k_zero_needs_only_c():
+    lib = tdm.load()
+    # K == 0: A and B may be NULL; without a GPU the call stops at the device check.
+    st = lib.gemm_f32(None, None, FAKE, 3, 3, 0, None)
+    assert st in (tdm.Status.ERROR_NO_DEVICE, tdm.Status.SUCCESS)
+
+
+def test_bad_path_and_unsupported_paths():
+    lib = tdm.load()
+    S, P = tdm.Status, tdm.Path
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 4, 4, 4, 77, None) == S.ERROR_INVALID_VALUE
+    # dtype/path mismatches are rejected before any device work
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 64, 64, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 16, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 64, 64, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
+    # shape/alignment limits of the fast paths
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 64, 64, 60, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE + 2, FAKE, FAKE, 64, 64, 64, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 17, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 66, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
+
+
+def test_no_device_is_reported_not_crashed():
+    pytest.importorskip("torch")
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    lib = tdm.load()
+    assert lib.gemm_f32(FAKE, FAKE, FAKE, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
+    assert lib.gemm_bf16_f32acc(FAKE, FAKE, FAKE, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
+
+
+# ---------------------------------------------------------------------------
+# Cost model: the library's gemm_roofline against the oracle's definition and
+# the pages' printed worked numbers.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 4096), (256, 256, 256), (8192, 14336, 4096),
+                                   (16, 8192, 8192), (1, 1, 1), (0, 5, 7), (3, 0, 0)])
+def test_roofline_matches_oracle(M, N, K):
+    for kind, in_bytes in ((tdm.Kind.F32, 4), (tdm.Kind.BF16_F32ACC, 2)):
+        r = tdm.gemm_roofline(kind, M, N, K)
+        flops, nbytes, ai = oracle.roofline(M, N, K, in_bytes, 4)
+        assert r.flops == flops and r.bytes == nbytes
+        assert r.intensity == pytest.approx(ai, rel=1e-15)
+
+
+def test_roofline_pages_numbers():
+    r = tdm.gemm_roofline(tdm.Kind.F32, 4096, 4096, 4096)
+    # compute- vs memory-bound lesson, N = 4096 fp32 worked example
+    assert r.flops == 137_438_953_472
+    assert r.bytes == 201_326_592
+    assert round(r.intensity) == 683
+
+
+def test_roofline_errors():
+    lib = tdm.load()
+    out = _lib.Roofline()
+    assert lib.gemm_roofline(0, 1, 1, 1, None) == tdm.Status.ERROR_INVALID_VALUE
+    assert lib.gemm_roofline(0, -1, 1, 1, ctypes.byref(out)) == tdm.Status.ERROR_INVALID_VALUE
+    assert lib.gemm_roofline(7, 1, 1, 1, ctypes.byref(out)) == tdm.Status.ERROR_INVALID_VALUE
+
+
+def test_path_selection():
+    K, P = tdm.Kind, tdm.Path
+    assert tdm.tdm_select_path(K.BF16_F32ACC, 16, 8192, 8192) == P.SKINNY
+    assert tdm.tdm_select_path(K.BF16_F32ACC, 4096, 4096, 4096) == P.MFMA
+    assert tdm.tdm_select_path(K.BF16_F32ACC, 8192, 14336, 4096) == P.MFMA
+    assert tdm.tdm_select_path(K.F32, 4096, 4096, 4096) == P.VALU
+    assert tdm.tdm_select_path(K.F32, 256, 256, 256) == P.VALU
+    assert tdm.tdm_select_path(K.F32, 7, 5, 3) == P.EDGE
+    assert tdm.tdm_select_path(K.BF16_F32ACC, 64, 64, 60) == P.EDGE  # K % 8 != 0
+
+
+def test_path_supports():
+    K, P = tdm.Kind, tdm.Path
+    assert tdm.tdm_path_supports(K.BF16_F32ACC, P.MFMA, 300, 520, 136)
+    assert not tdm.tdm_path_supports(K.BF16_F32ACC, P.MFMA, 300, 520, 136, misalign_a=2)
+    assert tdm.tdm_path_supports(K.BF16_F32ACC, P.SKINNY, 16, 8192, 8192)
+    assert not tdm.tdm_path_supports(K.BF16_F32ACC, P.SKINNY, 17, 8192, 8192)
+    assert tdm.tdm_path_supports(K.F32, P.EDGE, 3, 5, 7, 1, 3, 5)
+    assert not tdm.tdm_path_supports(K.F32, 9, 3, 5, 7)

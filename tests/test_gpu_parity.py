@@ -1,0 +1,228 @@
+"""Parity of the HIP paths with the CPU oracle (needs an MI355X).
+
+Every case calls the library through its C ABI (via the ctypes binding) on
+seeded synthetic inputs and compares with the fp64 oracle:
+  * normalized error max|C - R| / (max|A| max|B| K) within 1e-5 (fp32 inputs)
+    or 4e-3 (bf16 inputs), and relative Frobenius error within 1e-5;
+  * integer-valued inputs, where every partial sum is exact in fp32 under any
+    summation order, must match bit for bit on every path;
+  * at the full workload sizes, sampled 32 x 32 tiles are compared one by one
+    and a Freivalds check covers every element.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import tiled_dense_matrix_amd as tdm
+from tiled_dense_matrix_amd import inputs
+
+from helpers import (check_freivalds, check_full, check_tiles, log, max_abs, run, to_device)
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU"),
+]
+
+P = tdm.Path
+KIND = {"f32": tdm.Kind.F32, "bf16": tdm.Kind.BF16_F32ACC}
+ALL_PATHS = [P.AUTO, P.EDGE, P.VALU, P.MFMA, P.SKINNY]
+
+
+def random_inputs(kind, M, N, K, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "f32":
+        return inputs.uniform_fp32(rng, (M, K)), inputs.uniform_fp32(rng, (K, N))
+    return inputs.normal_bf16(rng, (M, K), 1.0), inputs.normal_bf16(rng, (K, N), 1.0)
+
+
+def supported_paths(kind, M, N, K):
+    return [p for p in ALL_PATHS if tdm.tdm_path_supports(KIND[kind], p, M, N, K)]
+
+
+def gpu_product(kind, A, B, path=P.AUTO):
+    C = run(kind, to_device(A), to_device(B), path)
+    torch.cuda.synchronize()
+    return C.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# The small workload, every path.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("path", [P.AUTO, P.EDGE, P.VALU])
+def test_f32_256_workload(path):
+    log(f"case f32_256 path={path.name}")
+    A, B = inputs.make_inputs("f32_256")
+    check_full("f32", A, B, gpu_product("f32", A, B, path), f"f32_256/{path.name}")
+
+
+@pytest.mark.parametrize("path", [P.AUTO, P.EDGE, P.MFMA])
+def test_bf16_square_small(path):
+    log(f"case bf16 512^3 path={path.name}")
+    A, B = random_inputs("bf16", 512, 512, 512, 100)
+    check_full("bf16", A, B, gpu_product("bf16", A, B, path), f"bf16_512/{path.name}")
+
+
+@pytest.mark.parametrize("path", [P.AUTO, P.SKINNY, P.MFMA, P.EDGE])
+def test_bf16_skinny_small(path):
+    log(f"case bf16 16x1024x2048 path={path.name}")
+    rng = np.random.default_rng(101)
+    A = inputs.normal_bf16(rng, (16, 2048), 1.0)
+    B = inputs.normal_bf16(rng, (2048, 1024), 0.02)
+    check_full("bf16", A, B, gpu_product("bf16", A, B, path), f"skinny_small/{path.name}")
+
+
+# ---------------------------------------------------------------------------
+# Ragged shapes: partial tiles in M, N and K on every path that takes them.
+# ---------------------------------------------------------------------------
+
+RAGGED = [
+    (1, 1, 1), (1, 8, 8), (5, 7, 3), (33, 65, 17), (64, 64, 64), (100, 200, 48),
+    (255, 257, 264), (257, 255, 136), (300, 520, 136), (512, 512, 520), (129, 8, 4096),
+    (16, 264, 4104), (7, 1000, 72), (16, 64, 32), (3, 72, 8), (513, 264, 200),
+]
+
+
+def _ragged_cases():
+    for kind in ("f32", "bf16"):
+        for shape in RAGGED:
+            for p in supported_paths(kind, *shape):
+                yield pytest.param(kind, shape, p, id=f"{kind}-{shape[0]}x{shape[1]}x{shape[2]}-{p.name}")
+
+
+@pytest.mark.parametrize("kind,shape,path", list(_ragged_cases()))
+def test_ragged(kind, shape, path):
+    M, N, K = shape
+    log(f"case ragged {kind} {shape} path={path.name}")
+    A, B = random_inputs(kind, M, N, K, seed=M * 7 + N * 13 + K)
+    check_full(kind, A, B, gpu_product(kind, A, B, path), f"{kind}/{shape}/{path.name}")
+
+
+@pytest.mark.parametrize("kind,shape,path", list(_ragged_cases()))
+def test_integer_inputs_bit_exact(kind, shape, path):
+    """Small integers: every partial sum is an exactly representable integer."""
+    M, N, K = shape
+    log(f"case integer {kind} {shape} path={path.name}")
+    rng = np.random.default_rng(5 + M + N + K)
+    A = inputs.small_int_matrix(rng, (M, K), kind=kind)
+    B = inputs.small_int_matrix(rng, (K, N), kind=kind)
+    C = gpu_product(kind, A, B, path)
+    R = oracle.gemm(A, B)
+    assert np.array_equal(C.astype(np.float64), R), (kind, shape, path.name)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and edge cases on the GPU.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kind,path", [("f32", P.VALU), ("f32", P.EDGE), ("bf16", P.MFMA),
+                                       ("bf16", P.EDGE)])
+def test_closed_forms(kind, path):
+    log(f"case closed forms {kind} path={path.name}")
+    M, N, K = 512, 768, 4096
+    ones_a = np.ones((M, K), np.float32)
+    ones_b = np.ones((K, N), np.float32)
+    if kind == "bf16":
+        ones_a, ones_b = inputs.fp32_to_bf16_bits(ones_a), inputs.fp32_to_bf16_bits(ones_b)
+    C = gpu_product(kind, ones_a, ones_b, path)
+    assert np.all(C == K)
+    rng = np.random.default_rng(3)
+    Bv = random_inputs(kind, 1, 256, 256, 9)[1]
+    eye = np.eye(256, dtype=np.float32)
+    if kind == "bf16":
+        eye = inputs.fp32_to_bf16_bits(eye)
+    C = gpu_product(kind, eye, Bv, path)
+    assert np.array_equal(C.astype(np.float64), oracle.widen(Bv))
+    del rng
+
+
+def test_skinny_closed_forms():
+    log("case closed forms skinny")
+    ones_a = inputs.fp32_to_bf16_bits(np.ones((16, 8192), np.float32))
+    ones_b = inputs.fp32_to_bf16_bits(np.ones((8192, 512), np.float32))
+    assert np.all(gpu_product("bf16", ones_a, ones_b, P.SKINNY) == 8192)
+
+
+@pytest.mark.parametrize("kind", ["f32", "bf16"])
+def test_k_zero_and_empty(kind):
+    log(f"case empty {kind}")
+    dt = torch.float32 if kind == "f32" else torch.int16
+    A = torch.empty((5, 0), dtype=dt, device="cuda")
+    B = torch.empty((0, 7), dtype=dt, device="cuda")
+    C = torch.full((5, 7), 3.0, device="cuda")
+    run(kind, A, B, P.AUTO, C)
+    torch.cuda.synchronize()
+    assert torch.all(C == 0)
+    E = run(kind, torch.empty((0, 4), dtype=dt, device="cuda"),
+            torch.empty((4, 9), dtype=dt, device="cuda"))
+    assert E.shape == (0, 9)
+
+
+@pytest.mark.parametrize("kind,shape", [("f32", (1000, 1000, 1000)), ("bf16", (1024, 1024, 1024)),
+                                        ("bf16", (16, 4096, 4096))])
+def test_run_to_run_bitwise_determinism(kind, shape):
+    M, N, K = shape
+    log(f"case determinism {kind} {shape}")
+    A, B = random_inputs(kind, M, N, K, 55)
+    Ad, Bd = to_device(A), to_device(B)
+    for p in supported_paths(kind, M, N, K):
+        ref = run(kind, Ad, Bd, p).clone()
+        for _ in range(5):
+            assert torch.equal(run(kind, Ad, Bd, p), ref), p.name
+
+
+def test_nondefault_stream():
+    log("case stream")
+    A, B = random_inputs("bf16", 512, 512, 512, 77)
+    Ad, Bd = to_device(A), to_device(B)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        C = run("bf16", Ad, Bd, P.MFMA, stream=s)
+    s.synchronize()
+    check_full("bf16", A, B, C.cpu().numpy(), "stream")
+
+
+def test_misaligned_pointers():
+    log("case misaligned")
+    A, B = random_inputs("bf16", 64, 64, 64, 78)
+    Araw = to_device(np.concatenate([np.zeros(1, np.uint16), A.ravel()]))
+    Ad = Araw[1:].view(64, 64)  # 2-byte offset: not 16-byte aligned
+    Bd = to_device(B)
+    with pytest.raises(tdm.TdmError) as e:
+        run("bf16", Ad, Bd, P.MFMA)
+    assert e.value.status == tdm.Status.ERROR_NOT_SUPPORTED
+    C = run("bf16", Ad, Bd, P.AUTO)
+    torch.cuda.synchronize()
+    check_full("bf16", A, B, C.cpu().numpy(), "misaligned")
+
+
+# ---------------------------------------------------------------------------
+# Full-size workloads, in the launch configuration the benchmark times.
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["f32_4096", "bf16_4096", "bf16_8192", "bf16_mlp"])
+def test_full_size_workload(name):
+    w = inputs.WORKLOADS[name]
+    log(f"case workload {name} {w.M}x{w.N}x{w.K}")
+    A, B = inputs.make_inputs(w)
+    C = gpu_product(w.kind, A, B, P.AUTO)
+    tiles = inputs.sample_tiles(w.M, w.N)
+    # include the four corners so partial-tile logic and the last tile are seen
+    tiles = sorted(set(tiles) | {(0, 0), (0, w.N - 32), (w.M - 32, 0), (w.M - 32, w.N - 32)})
+    p = check_tiles(w.kind, A, B, C, tiles, what=name)
+    f = check_freivalds(A, B, C, what=name)
+    log(f"  {name}: tiles norm_max_err={p['norm_max_err']:.3e} rel_fro={p['rel_fro']:.3e} "
+        f"freivalds={f:.3e} maxA={max_abs(A):.3g} maxB={max_abs(B):.3g}")
+
+
+def test_full_size_skinny():
+    w = inputs.WORKLOADS["bf16_skinny"]
+    log(f"case workload bf16_skinny {w.M}x{w.N}x{w.K}")
+    A, B = inputs.make_inputs(w)
+    assert tdm.tdm_select_path(tdm.Kind.BF16_F32ACC, w.M, w.N, w.K) == P.SKINNY
+    C = gpu_product("bf16", A, B, P.AUTO)
+    p = check_full("bf16", A, B, C, "bf16_skinny")
+    log(f"  bf16_skinny: norm_max_err={p['norm_max_err']:.3e} rel_fro={p['rel_fro']:.3e}")

@@ -1,0 +1,25 @@
+"""tiled_dense_matrix_amd -- tiled dense matrix multiply for AMD MI355X (gfx950).
+
+The product C = A @ B runs in hand-written HIP kernels behind a C ABI
+(include/tdm.h, built into libtdm.so). This package is the thin Python
+binding over that ABI; the submodule ``inputs`` holds the seeded synthetic
+input generator used by tests and the benchmark.
+"""
+from ._lib import (  # noqa: F401
+    Kind,
+    Path,
+    Roofline,
+    Status,
+    TdmError,
+    gemm_bf16_f32acc,
+    gemm_f32,
+    gemm_roofline,
+    load,
+    path_name,
+    status_string,
+    tdm_gemm_bf16_f32acc_path,
+    tdm_gemm_f32_path,
+    tdm_path_supports,
+    tdm_select_path,
+    version,
+)

@@ -1,0 +1,221 @@
+"""ctypes binding of libtdm.so (the C ABI declared in include/tdm.h).
+
+Argument marshalling only: every step of the product runs in the HIP
+kernels behind the C ABI. Torch tensors supply device memory and the
+current stream. There is no CPU fallback; if libtdm.so cannot be loaded the
+calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import enum
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libtdm.so")
+
+# The C ABI, as (name, restype, argtypes). Tests check that libtdm.so exports
+# every function declared in include/tdm.h and nothing is missing here.
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+class Roofline(ctypes.Structure):
+    _fields_ = [("flops", ctypes.c_double), ("bytes", ctypes.c_double),
+                ("intensity", ctypes.c_double)]
+
+
+SIGNATURES = {
+    "gemm_f32": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "gemm_bf16_f32acc": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, _p]),
+    "gemm_roofline": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(Roofline)]),
+    "tdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "tdm_gemm_f32_path": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]),
+    "tdm_gemm_bf16_f32acc_path": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]),
+    "tdm_path_supports": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int]),
+    "tdm_select_path": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64]),
+    "tdm_path_name": (ctypes.c_char_p, [ctypes.c_int]),
+    "tdm_version": (ctypes.c_int, []),
+}
+
+
+class Status(enum.IntEnum):
+    SUCCESS = 0
+    ERROR_INVALID_VALUE = 1
+    ERROR_NOT_SUPPORTED = 2
+    ERROR_NO_DEVICE = 3
+    ERROR_LAUNCH = 4
+
+
+class Kind(enum.IntEnum):
+    F32 = 0
+    BF16_F32ACC = 1
+
+
+class Path(enum.IntEnum):
+    AUTO = 0
+    EDGE = 1
+    VALU = 2
+    MFMA = 3
+    SKINNY = 4
+
+
+class TdmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = Status(status) if status in Status._value2member_map_ else status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libtdm.so (building it first if it has never been built)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            lib_path = path or LIB_PATH
+            if not os.path.exists(lib_path):
+                from . import build as _build
+                _build.build(verbose=False)
+            lib = ctypes.CDLL(lib_path)
+            for name, (res, args) in SIGNATURES.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load().tdm_status_string(int(status)).decode()
+
+
+def path_name(path: int) -> str:
+    return load().tdm_path_name(int(path)).decode()
+
+
+def version() -> int:
+    return load().tdm_version()
+
+
+def gemm_roofline(kind: int, M: int, N: int, K: int) -> Roofline:
+    out = Roofline()
+    st = load().gemm_roofline(int(kind), M, N, K, ctypes.byref(out))
+    if st != Status.SUCCESS:
+        raise TdmError(st, "gemm_roofline")
+    return out
+
+
+def tdm_select_path(kind: int, M: int, N: int, K: int) -> Path:
+    return Path(load().tdm_select_path(int(kind), M, N, K))
+
+
+def tdm_path_supports(kind: int, path: int, M: int, N: int, K: int,
+                      misalign_a: int = 0, misalign_b: int = 0, misalign_c: int = 0) -> bool:
+    return bool(load().tdm_path_supports(int(kind), int(path), M, N, K,
+                                         misalign_a, misalign_b, misalign_c))
+
+
+# ---------------------------------------------------------------------------
+# Torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream) -> int | None:
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return stream or None
+    return stream.cuda_stream or None
+
+
+def _check_matrix(name: str, t, dtypes, rows: int | None = None, cols: int | None = None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got shape {tuple(t.shape)}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major); call .contiguous()")
+    if rows is not None and t.shape[0] != rows:
+        raise ValueError(f"{name} has {t.shape[0]} rows, expected {rows}")
+    if cols is not None and t.shape[1] != cols:
+        raise ValueError(f"{name} has {t.shape[1]} columns, expected {cols}")
+
+
+def _prep(A, B, C, in_dtypes):
+    torch = _torch()
+    _check_matrix("A", A, in_dtypes)
+    M, K = A.shape
+    _check_matrix("B", B, in_dtypes, rows=K)
+    N = B.shape[1]
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check_matrix("C", C, (torch.float32,), rows=M, cols=N)
+        if C.device != A.device:
+            raise ValueError("C is on another device than A and B")
+    return M, N, K, C
+
+
+def _call(fname: str, A, B, C, M, N, K, stream, path=None):
+    torch = _torch()
+    lib = load()
+    fn = getattr(lib, fname)
+    with torch.cuda.device(A.device):
+        args = [A.data_ptr() or None, B.data_ptr() or None, C.data_ptr() or None, M, N, K]
+        if path is not None:
+            args.append(int(path))
+        args.append(_stream_handle(stream))
+        st = fn(*args)
+    if st != Status.SUCCESS:
+        raise TdmError(st, fname)
+    return C
+
+
+def gemm_f32(A, B, C=None, stream=None):
+    """C = A @ B for fp32 A[M,K], B[K,N] (row-major CUDA tensors). Returns C."""
+    torch = _torch()
+    M, N, K, C = _prep(A, B, C, (torch.float32,))
+    return _call("gemm_f32", A, B, C, M, N, K, stream)
+
+
+def gemm_bf16_f32acc(A, B, C=None, stream=None):
+    """C = A @ B for bf16 A, B (torch.bfloat16 or raw int16/uint16 bits); fp32 C."""
+    torch = _torch()
+    M, N, K, C = _prep(A, B, C, _bf16_dtypes())
+    return _call("gemm_bf16_f32acc", A, B, C, M, N, K, stream)
+
+
+def tdm_gemm_f32_path(A, B, C=None, path=Path.AUTO, stream=None):
+    torch = _torch()
+    M, N, K, C = _prep(A, B, C, (torch.float32,))
+    return _call("tdm_gemm_f32_path", A, B, C, M, N, K, stream, path)
+
+
+def tdm_gemm_bf16_f32acc_path(A, B, C=None, path=Path.AUTO, stream=None):
+    M, N, K, C = _prep(A, B, C, _bf16_dtypes())
+    return _call("tdm_gemm_bf16_f32acc_path", A, B, C, M, N, K, stream, path)
+
+
+def _bf16_dtypes():
+    torch = _torch()
+    dts = [torch.bfloat16, torch.int16]
+    if hasattr(torch, "uint16"):
+        dts.append(torch.uint16)
+    return tuple(dts)

@@ -1,0 +1,190 @@
+// fp32 product on the vector ALUs: LDS tiling plus register blocking.
+//
+// Method (CS336 Lecture 5 GPU notes, §4.2: tiling, register blocking and a
+// double-buffered pipeline; §4.1: coalesced loads, then any access pattern
+// from shared memory):
+//   * one workgroup of 256 lanes owns a 128 x 128 tile of C and walks K in
+//     steps of 16;
+//   * each step the lanes copy a 128 x 16 slice of A and a 16 x 128 slice of
+//     B from HBM with 16-byte row-contiguous loads; A is written to LDS
+//     transposed (As[k][m]) so that the inner loop reads both operands as
+//     16-byte vectors;
+//   * every lane keeps an 8 x 8 block of C in registers (rows 4*ty..+3 and
+//     64+4*ty..+3, columns 4*tx..+3 and 64+4*tx..+3) and per k does 64
+//     fused multiply-adds from four 16-byte LDS reads;
+//   * LDS is double-buffered with one barrier per step.
+// Each output is accumulated in fp32 with k ascending.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tdm_internal.h"
+#include "tile_map.h"
+
+namespace tdm {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kBM = 128;
+constexpr int kBN = 128;
+constexpr int kBK = 16;
+constexpr int kThreads = 256;
+constexpr int kPitch = kBM + 4;  // floats per LDS row (keeps 16-byte alignment)
+constexpr int kStage = 2 * kBK * kPitch;  // As then Bs, floats
+constexpr int kGroupM = 8;
+
+template <bool kGuard>
+__device__ __forceinline__ void load_tiles(const float* __restrict__ A,
+                                           const float* __restrict__ B, int M,
+                                           int N, int K, int m0, int n0, int k0,
+                                           int tid, f32x4 (&ra)[2],
+                                           f32x4 (&rb)[2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int gm = m0 + (tid >> 2) + 64 * i;
+    int gk = k0 + (tid & 3) * 4;
+    if (!kGuard) {
+      ra[i] = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
+    } else {
+      const bool ok = gm < M && gk < K;
+      gm = gm < M ? gm : M - 1;
+      gk = gk < K ? gk : K - 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
+      ra[i] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int gk = k0 + (tid >> 5) + 8 * i;
+    int gn = n0 + (tid & 31) * 4;
+    if (!kGuard) {
+      rb[i] = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+    } else {
+      const bool ok = gk < K && gn < N;
+      gk = gk < K ? gk : K - 1;
+      gn = gn < N ? gn : N - 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+      rb[i] = ok ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+}
+
+__device__ __forceinline__ void store_tiles(float* __restrict__ stage, int tid,
+                                            const f32x4 (&ra)[2],
+                                            const f32x4 (&rb)[2]) {
+  float* as = stage;
+  float* bs = stage + kBK * kPitch;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int m = (tid >> 2) + 64 * i;
+    const int k = (tid & 3) * 4;
+    as[(k + 0) * kPitch + m] = ra[i].x;
+    as[(k + 1) * kPitch + m] = ra[i].y;
+    as[(k + 2) * kPitch + m] = ra[i].z;
+    as[(k + 3) * kPitch + m] = ra[i].w;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k = (tid >> 5) + 8 * i;
+    const int n = (tid & 31) * 4;
+    *reinterpret_cast<f32x4*>(bs + k * kPitch + n) = rb[i];
+  }
+}
+
+template <bool kGuard>
+__device__ __forceinline__ void tile_product(const float* __restrict__ A,
+                                             const float* __restrict__ B,
+                                             float* __restrict__ C, int M,
+                                             int N, int K, int m0, int n0,
+                                             float* __restrict__ lds) {
+  const int tid = threadIdx.x;
+  const int ty = tid >> 4, tx = tid & 15;
+
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+
+  const int steps = (K + kBK - 1) / kBK;
+  f32x4 ra[2], rb[2];
+  load_tiles<kGuard>(A, B, M, N, K, m0, n0, 0, tid, ra, rb);
+  store_tiles(lds, tid, ra, rb);
+  __syncthreads();
+
+  for (int t = 0; t < steps; ++t) {
+    const float* cur = lds + (t & 1) * kStage;
+    float* nxt = lds + ((t + 1) & 1) * kStage;
+    const bool more = t + 1 < steps;
+    if (more) load_tiles<kGuard>(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, ra, rb);
+    const float* as = cur;
+    const float* bs = cur + kBK * kPitch;
+    // Unrolling all 16 steps lets the scheduler hoist every LDS read and
+    // spill; four keeps 121 VGPRs (4 waves per SIMD).
+#pragma unroll 4
+    for (int k = 0; k < kBK; ++k) {
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(as + k * kPitch + ty * 4);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(as + k * kPitch + 64 + ty * 4);
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + k * kPitch + tx * 4);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + k * kPitch + 64 + tx * 4);
+      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    if (more) store_tiles(nxt, tid, ra, rb);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int col = n0 + h * 64 + tx * 4;
+      const f32x4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
+      if (!kGuard) {
+        *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * N + col) = v;
+      } else if (row < M && col < N) {
+        // N % 4 == 0, so a 4-wide column group is entirely in or out.
+        *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * N + col) = v;
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void valu_f32_kernel(
+    const float* __restrict__ A, const float* __restrict__ B,
+    float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  __shared__ float lds[2 * kStage];
+  int tm, tn;
+  xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+  const bool full = (m0 + kBM <= M) && (n0 + kBN <= N) && (K % kBK == 0);
+  if (full)
+    tile_product<false>(A, B, C, M, N, K, m0, n0, lds);
+  else
+    tile_product<true>(A, B, C, M, N, K, m0, n0, lds);
+}
+
+}  // namespace
+
+bool valu_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
+                       int mis_c) {
+  (void)M;
+  return K % 4 == 0 && N % 4 == 0 && K >= 4 && mis_a == 0 && mis_b == 0 &&
+         mis_c == 0;
+}
+
+hipError_t launch_valu_f32(const float* A, const float* B, float* C, int M,
+                           int N, int K, hipStream_t s) {
+  const int tiles_m = (M + kBM - 1) / kBM;
+  const int tiles_n = (N + kBN - 1) / kBN;
+  hipLaunchKernelGGL(valu_f32_kernel, dim3(tiles_m * tiles_n), dim3(kThreads),
+                     0, s, A, B, C, M, N, K, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+}  // namespace tdm

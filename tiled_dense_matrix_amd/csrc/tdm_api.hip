@@ -1,0 +1,219 @@
+// C ABI of libtdm.so: argument validation, path choice, cost model.
+//
+// The declarations and the contract (layouts, ownership, errors) are in
+// include/tdm.h. Every check here runs on the host before any HIP call, so
+// invalid calls are rejected identically with or without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tdm.h"
+#include "tdm_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t{1} << 31;  // per matrix (32-bit indexing)
+
+// MI355X figures used by the dispatcher (AMD's published peaks).
+constexpr double kPeakMfmaBf16 = 2.5166e15;  // FLOP/s, dense
+constexpr double kHbmBandwidth = 8.0e12;     // B/s
+
+int misalign(const void* p) { return static_cast<int>(reinterpret_cast<uintptr_t>(p) & 15u); }
+
+bool too_big(int64_t M, int64_t N, int64_t K) {
+  auto over = [](int64_t a, int64_t b) {
+    if (a == 0 || b == 0) return false;
+    if (a > kMaxElems || b > kMaxElems) return true;
+    return a > (kMaxElems - 1) / b;
+  };
+  return over(M, K) || over(K, N) || over(M, N);
+}
+
+tdm_status check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return TDM_ERROR_NO_DEVICE;
+  return TDM_SUCCESS;
+}
+
+// Shape/alignment admission of each path for one kind.
+bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
+              int ma, int mb, int mc) {
+  const bool kind_ok =
+      (path != TDM_PATH_VALU || kind == TDM_KIND_F32) &&
+      (path != TDM_PATH_MFMA || kind == TDM_KIND_BF16_F32ACC) &&
+      (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC);
+  if (!kind_ok) return false;
+  if (M == 0 || N == 0 || K == 0) return true;  // nothing to run, or a zero fill
+  switch (path) {
+    case TDM_PATH_AUTO:
+    case TDM_PATH_EDGE:
+      return true;
+    case TDM_PATH_VALU:
+      return kind == TDM_KIND_F32 && tdm::valu_f32_supports(M, N, K, ma, mb, mc);
+    case TDM_PATH_MFMA:
+      return kind == TDM_KIND_BF16_F32ACC && tdm::mfma_bf16_supports(M, N, K, ma, mb, mc);
+    case TDM_PATH_SKINNY:
+      return kind == TDM_KIND_BF16_F32ACC && tdm::skinny_bf16_supports(M, N, K, ma, mb, mc);
+  }
+  return false;
+}
+
+// Dispatcher: compare the product's intensity with the ridge point of the
+// unit that would run it. Below the ridge the product is memory-bound and
+// the small-M streaming path is used; above it the compute paths are used.
+// Very small products (under one 32x32 tile's worth of work per CU) go to
+// the edge kernel, whose launch is cheapest.
+tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc) {
+  if (M <= 0 || N <= 0 || K <= 0) return TDM_PATH_EDGE;
+  const double flops = 2.0 * M * N * K;
+  const double in = kind == TDM_KIND_F32 ? 4.0 : 2.0;
+  const double bytes = (double(M) * K + double(K) * N) * in + double(M) * N * 4.0;
+  const double intensity = flops / bytes;
+  if (kind == TDM_KIND_BF16_F32ACC) {
+    const double ridge = kPeakMfmaBf16 / kHbmBandwidth;
+    if (intensity < ridge && supports(kind, TDM_PATH_SKINNY, M, N, K, ma, mb, mc))
+      return TDM_PATH_SKINNY;
+    if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc)) return TDM_PATH_MFMA;
+    return TDM_PATH_EDGE;
+  }
+  if (M * N <= 64 * 64) return TDM_PATH_EDGE;
+  if (supports(kind, TDM_PATH_VALU, M, N, K, ma, mb, mc)) return TDM_PATH_VALU;
+  return TDM_PATH_EDGE;
+}
+
+tdm_status to_status(hipError_t e) { return e == hipSuccess ? TDM_SUCCESS : TDM_ERROR_LAUNCH; }
+
+template <typename T>
+tdm_status validate(const T* A, const T* B, const float* C, int64_t M, int64_t N, int64_t K) {
+  if (M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return TDM_SUCCESS;
+  if (C == nullptr) return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && (A == nullptr || B == nullptr)) return TDM_ERROR_INVALID_VALUE;
+  if ((reinterpret_cast<uintptr_t>(C) % alignof(float)) != 0) return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && ((reinterpret_cast<uintptr_t>(A) % alignof(T)) != 0 ||
+                (reinterpret_cast<uintptr_t>(B) % alignof(T)) != 0))
+    return TDM_ERROR_INVALID_VALUE;
+  if (too_big(M, N, K)) return TDM_ERROR_NOT_SUPPORTED;
+  return TDM_SUCCESS;
+}
+
+tdm_status run_f32(const float* A, const float* B, float* C, int64_t M, int64_t N,
+                   int64_t K, tdm_path path, void* stream) {
+  tdm_status st = validate(A, B, C, M, N, K);
+  if (st != TDM_SUCCESS || M == 0 || N == 0) return st;
+  const int ma = misalign(A), mb = misalign(B), mc = misalign(C);
+  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_F32, path, M, N, K, ma, mb, mc))
+    return TDM_ERROR_NOT_SUPPORTED;
+  if ((st = check_device()) != TDM_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return to_status(tdm::launch_fill_zero_f32(C, M * N, s));  // empty sum
+  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_F32, M, N, K, ma, mb, mc);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  switch (path) {
+    case TDM_PATH_VALU: return to_status(tdm::launch_valu_f32(A, B, C, m, n, k, s));
+    default: return to_status(tdm::launch_edge_f32(A, B, C, m, n, k, s));
+  }
+}
+
+tdm_status run_bf16(const uint16_t* A, const uint16_t* B, float* C, int64_t M,
+                    int64_t N, int64_t K, tdm_path path, void* stream) {
+  tdm_status st = validate(A, B, C, M, N, K);
+  if (st != TDM_SUCCESS || M == 0 || N == 0) return st;
+  const int ma = misalign(A), mb = misalign(B), mc = misalign(C);
+  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, mc))
+    return TDM_ERROR_NOT_SUPPORTED;
+  if ((st = check_device()) != TDM_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) return to_status(tdm::launch_fill_zero_f32(C, M * N, s));  // empty sum
+  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, mc);
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  switch (path) {
+    case TDM_PATH_MFMA: return to_status(tdm::launch_mfma_bf16(A, B, C, m, n, k, s));
+    case TDM_PATH_SKINNY: return to_status(tdm::launch_skinny_bf16(A, B, C, m, n, k, s));
+    default: return to_status(tdm::launch_edge_bf16(A, B, C, m, n, k, s));
+  }
+}
+
+bool valid_path(tdm_path p) {
+  return p == TDM_PATH_AUTO || p == TDM_PATH_EDGE || p == TDM_PATH_VALU ||
+         p == TDM_PATH_MFMA || p == TDM_PATH_SKINNY;
+}
+
+}  // namespace
+
+extern "C" {
+
+tdm_status gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N,
+                    int64_t K, void* stream) {
+  return run_f32(A, B, C, M, N, K, TDM_PATH_AUTO, stream);
+}
+
+tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C, int64_t M,
+                            int64_t N, int64_t K, void* stream) {
+  return run_bf16(A, B, C, M, N, K, TDM_PATH_AUTO, stream);
+}
+
+tdm_status tdm_gemm_f32_path(const float* A, const float* B, float* C, int64_t M,
+                             int64_t N, int64_t K, tdm_path path, void* stream) {
+  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  return run_f32(A, B, C, M, N, K, path, stream);
+}
+
+tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B, float* C,
+                                     int64_t M, int64_t N, int64_t K, tdm_path path,
+                                     void* stream) {
+  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  return run_bf16(A, B, C, M, N, K, path, stream);
+}
+
+tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roofline* out) {
+  if (out == nullptr || M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
+  double in_size;
+  switch (kind) {
+    case TDM_KIND_F32: in_size = 4.0; break;
+    case TDM_KIND_BF16_F32ACC: in_size = 2.0; break;
+    default: return TDM_ERROR_INVALID_VALUE;
+  }
+  const double m = double(M), n = double(N), k = double(K);
+  out->flops = 2.0 * m * n * k;
+  out->bytes = (m * k + k * n) * in_size + m * n * 4.0;
+  out->intensity = out->bytes > 0.0 ? out->flops / out->bytes : 0.0;
+  return TDM_SUCCESS;
+}
+
+const char* tdm_status_string(tdm_status s) {
+  switch (s) {
+    case TDM_SUCCESS: return "success";
+    case TDM_ERROR_INVALID_VALUE: return "invalid value";
+    case TDM_ERROR_NOT_SUPPORTED: return "not supported";
+    case TDM_ERROR_NO_DEVICE: return "no HIP device";
+    case TDM_ERROR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int tdm_path_supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
+                      int misalign_a, int misalign_b, int misalign_c) {
+  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return 0;
+  if (!valid_path(path) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
+  return supports(kind, path, M, N, K, misalign_a, misalign_b, misalign_c) ? 1 : 0;
+}
+
+tdm_path tdm_select_path(tdm_kind kind, int64_t M, int64_t N, int64_t K) {
+  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
+  return choose(kind, M, N, K, 0, 0, 0);
+}
+
+const char* tdm_path_name(tdm_path p) {
+  switch (p) {
+    case TDM_PATH_AUTO: return "auto";
+    case TDM_PATH_EDGE: return "edge";
+    case TDM_PATH_VALU: return "valu";
+    case TDM_PATH_MFMA: return "mfma";
+    case TDM_PATH_SKINNY: return "skinny";
+  }
+  return "unknown";
+}
+
+int tdm_version(void) { return TDM_VERSION; }
+
+}  // extern "C"
