@@ -57,8 +57,8 @@ ROTATE_BYTES = 640 << 20  # working set across rotated copies
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--path", default="auto", help="force a path (edge/valu/mfma/skinny)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,

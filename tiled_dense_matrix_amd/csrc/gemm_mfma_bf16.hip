@@ -4,26 +4,33 @@
 // double buffering; §3.2 low-precision products with fp32 accumulation;
 // LLM course ch. 15 "GPU", §15.6 table of GEMM techniques):
 //   * one workgroup owns a 256 x 256 tile of C and walks K in steps of 64;
-//   * each step it copies a 256 x 64 slice of A and a 64 x 256 slice of B
-//     from HBM into LDS with 16-byte, row-contiguous loads (coalesced);
+//   * each step copies a 256 x 64 slice of A and a 64 x 256 slice of B from
+//     HBM into LDS with 16-byte row-contiguous loads that write LDS directly
+//     (global_load_lds), so the copy costs no registers and no LDS stores;
 //   * the four waves (2 x 2) each hold a 128 x 128 block of C in registers
-//     (4 x 4 blocks of 32 x 32) and feed v_mfma_f32_32x32x16_bf16 from LDS;
-//   * LDS is double-buffered: while the waves multiply slice t, the loads of
-//     slice t+1 are in flight, and a single barrier per step separates them.
+//     (4 x 4 accumulators of 32 x 32) fed by v_mfma_f32_32x32x16_bf16;
+//   * LDS is double-buffered: the copy of step t+1 runs while the waves
+//     multiply step t; one barrier per step separates the two.
 //
-// MFMA wants, in every lane, eight consecutive K values of one row of A and
-// of one column of B. A is row-major, so its rows are already K-contiguous.
-// B is row-major [K, N] (N-contiguous), so each lane loads an 8 x 8 block of
-// B (8 rows, 8 adjacent columns), transposes it in registers, and writes it
-// to LDS as Bt[n][k]. Both LDS tiles are therefore [row][64 k] arrays of
-// eight 16-byte chunks, and chunk c of row r is stored at c ^ swz(r), an XOR
-// swizzle that keeps 8 consecutive rows (the MFMA read) and 8 rows 8 apart
-// (the transposed write) on distinct LDS banks.
+// Operand layouts. MFMA wants, in every lane, eight consecutive K values of
+// one row of A and of one column of B.
+//   A stays row-major in LDS, As[m][k] (128 bytes per row), and is read with
+//   16-byte loads. Chunk c (8 k values) of row m sits at chunk c ^ swz_a(m).
+//   B stays row-major too, Bs[k][n] (512 bytes per row), and is read with
+//   ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
+//   element e from the address of lane 4e + j/4, so lanes that point at four
+//   consecutive n of rows k..k+3 come back holding four consecutive k of one
+//   column. Chunk c of row k sits at chunk c ^ swz_b(k).
+// Both swizzles spread the rows each read touches over distinct LDS banks.
 //
-// Partial tiles (M or N not a multiple of 256, K not a multiple of 64) run the
-// same loop with clamped, zero-masked loads and masked stores.
+// Partial tiles in M or N load clamped (in-bounds) rows/columns whose
+// products only reach outputs that are not stored. A K that is not a
+// multiple of 64 has its last step loaded through registers with the
+// out-of-range elements set to zero.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "tdm_internal.h"
 #include "tile_map.h"
@@ -33,114 +40,158 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-// Native 16-byte vector: HIP's uint4 is a struct, which kept the staging
-// arrays out of registers.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
 constexpr int kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kChunks = kBK / 8;                  // 16-byte chunks per row
-constexpr int kBufChunks = (kBM + kBN) * kChunks; // one stage: A then Bt
-constexpr int kLdsBytes = 2 * kBufChunks * 16;    // double-buffered
-constexpr int kWaveM = 128, kWaveN = 128;         // per-wave block of C
+constexpr int kRowA = kBK * 2;                 // bytes per LDS row of A
+constexpr int kRowB = kBN * 2;                 // bytes per LDS row of B
+constexpr int kStageA = kBM * kRowA;           // 32 KB
+constexpr int kStageB = kBK * kRowB;           // 32 KB
+constexpr int kStage = kStageA + kStageB;      // 64 KB
+constexpr int kLdsBytes = 2 * kStage;          // double-buffered
+constexpr int kWaveM = 128, kWaveN = 128;      // per-wave block of C
 constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
 constexpr int kGroupM = 4;
+// Instruction classes of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
-__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_a(int m) { return (m ^ (m >> 3)) & 7; }
+__device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+// One 16-byte-per-lane global -> LDS copy from sbase + voff: lane l's 16
+// bytes land at lds_addr + 16*l. Issued as inline assembly so that the
+// compiler does not treat it as an LDS write of unknown address and stall
+// every later LDS read on it; completion is awaited explicitly
+// (wait_copies) before the barrier that publishes the buffer. M0 carries the
+// LDS address; nothing else in these kernels uses M0.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Per-lane byte offsets of this wave's 8 + 8 copy instructions; the K step
+// only moves the scalar base pointers.
+struct CopyPlan {
+  uint32_t a[8];
+  uint32_t b[8];
+};
+
+__device__ __forceinline__ CopyPlan make_plan(int M, int N, int K, int m0, int n0, int wave,
+                                              int lane) {
+  CopyPlan p;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // A: 32 blocks of 8 rows, wave w owns 8w..8w+7
+    const int row = (wave * 8 + j) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ swz_a(row);
+    const int gm = min(m0 + row, M - 1);
+    p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(gm) * K + c * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {  // B: 32 blocks of 2 rows
+    const int row = (wave * 8 + j) * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ swz_b(row);
+    const int gn = min(n0 + c * 8, N - 8);
+    p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + gn) * 2);
+  }
+  return p;
+}
+
+// --- global -> LDS copy of one full K step (clamped M/N) -----------------
+// Each wave instruction writes 1 KB of LDS.
+__device__ __forceinline__ void copy_step_dma(const uint16_t* __restrict__ A,
+                                              const uint16_t* __restrict__ B, int N,
+                                              int k0, int wave, const CopyPlan& p,
+                                              uint32_t stage) {
+  const uint16_t* a_base = A + k0;
+  const uint16_t* b_base = B + static_cast<int64_t>(k0) * N;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma16(a_base, p.a[j], stage + (wave * 8 + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma16(b_base, p.b[j], stage + kStageA + (wave * 8 + j) * 1024);
+}
+
+// Same layout, through registers, with zeros beyond K (the partial last step).
+__device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
+                                                 const uint16_t* __restrict__ B,
+                                                 int M, int N, int K, int m0, int n0,
+                                                 int k0, int tid,
+                                                 LDS_PTR(uint8_t) stage) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // A: 2048 chunks, 8 per lane
+    const int id = tid + kThreads * i;
+    const int row = id >> 3, c = id & 7;
+    const int gk = k0 + c * 8;
+    const int gm = min(m0 + row, M - 1);
+    u32x4 v = zero;
+    if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
+    *(LDS_PTR(u32x4))(stage + row * kRowA + ((c ^ swz_a(row)) << 4)) = v;
+  }
+  LDS_PTR(uint8_t) sb = stage + kStageA;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {  // B: 2048 chunks, 8 per lane
+    const int id = tid + kThreads * i;
+    const int row = id >> 5, c = id & 31;
+    const int gk = k0 + row;
+    const int gn = min(n0 + c * 8, N - 8);
+    u32x4 v = zero;
+    if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+    *(LDS_PTR(u32x4))(sb + row * kRowB + ((c ^ swz_b(row)) << 4)) = v;
+  }
+}
+
+__device__ __forceinline__ void wait_copies() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int chunk) {
+  const u32x4 v = *(LDS_PTR(const u32x4))(sa + row * kRowA + ((chunk ^ swz_a(row)) << 4));
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// 16-bit element e (0..7) of a 16-byte chunk.
-__device__ __forceinline__ uint32_t elem(const u32x4& v, int e) {
-  const uint32_t d = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y
-                   : (e >> 1) == 2 ? v.z : v.w;
-  return (e & 1) ? (d >> 16) : (d & 0xffffu);
+// Eight consecutive k (16s + 8*(lane/32) + 0..7) of column n_base + lane%32.
+__device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, int s,
+                                         int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = n_base + 16 * (g & 1) + 4 * (i & 3);
+  const int c = col >> 3, half = (col & 7) << 1;
+  const int r0 = 16 * s + 8 * (g >> 1) + (i >> 2);
+  const int r1 = r0 + 4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(s16x4))(sb + r0 * kRowB + ((c ^ swz_b(r0)) << 4) + half));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(s16x4))(sb + r1 * kRowB + ((c ^ swz_b(r1)) << 4) + half));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-template <bool kGuard>
-__device__ __forceinline__ void load_a(const uint16_t* __restrict__ A, int M,
-                                       int K, int m0, int k0, int tid,
-                                       u32x4 (&ra)[8]) {
-  const int c = tid & 7;
-  const int r = tid >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    int gm = m0 + r + 32 * i;
-    int gk = k0 + c * 8;
-    if (!kGuard) {
-      ra[i] = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-    } else {
-      const bool ok = gm < M && gk < K;
-      gm = gm < M ? gm : M - 1;
-      gk = gk < K ? gk : K - 8;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-      ra[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-template <bool kGuard>
-__device__ __forceinline__ void load_b(const uint16_t* __restrict__ B, int N,
-                                       int K, int n0, int k0, int tid,
-                                       u32x4 (&rb)[8]) {
-  const int nc = tid & 31;
-  const int kb = tid >> 5;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    int gk = k0 + kb * 8 + r;
-    int gn = n0 + nc * 8;
-    if (!kGuard) {
-      rb[r] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    } else {
-      const bool ok = gk < K && gn < N;
-      gk = gk < K ? gk : K - 1;
-      gn = gn < N ? gn : N - 8;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-      rb[r] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-}
-
-__device__ __forceinline__ void store_a(u32x4* __restrict__ stage, int tid,
-                                        const u32x4 (&ra)[8]) {
-  const int c = tid & 7;
-  const int r = tid >> 3;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = r + 32 * i;
-    stage[row * kChunks + (c ^ swz(row))] = ra[i];
-  }
-}
-
-// Transpose the lane's 8 (k) x 8 (n) block and store it as Bt[n][k].
-__device__ __forceinline__ void store_bt(u32x4* __restrict__ stage, int tid,
-                                         const u32x4 (&rb)[8]) {
-  const int nc = tid & 31;
-  const int kb = tid >> 5;
-  u32x4* bt = stage + kBM * kChunks;
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    u32x4 o;
-    o.x = elem(rb[0], c) | (elem(rb[1], c) << 16);
-    o.y = elem(rb[2], c) | (elem(rb[3], c) << 16);
-    o.z = elem(rb[4], c) | (elem(rb[5], c) << 16);
-    o.w = elem(rb[6], c) | (elem(rb[7], c) << 16);
-    const int n = nc * 8 + c;
-    bt[n * kChunks + (kb ^ swz(n))] = o;
-  }
-}
-
-template <bool kGuard>
-__device__ __forceinline__ void tile_product(
+__global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-    float* __restrict__ C, int M, int N, int K, int m0, int n0,
-    u32x4* __restrict__ lds) {
+    float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
+
+  int tm, tn;
+  xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
+  const int m0 = tm * kBM, n0 = tn * kBN;
+
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
@@ -154,52 +205,73 @@ __device__ __forceinline__ void tile_product(
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int steps = (K + kBK - 1) / kBK;
-  u32x4 ra[8], rb[8];
-  load_a<kGuard>(A, M, K, m0, 0, tid, ra);
-  load_b<kGuard>(B, N, K, n0, 0, tid, rb);
-  store_a(lds, tid, ra);
-  store_bt(lds, tid, rb);
+  const int full_steps = K / kBK;  // steps whose 64 k are all in range
+  const CopyPlan plan = make_plan(M, N, K, m0, n0, wave, lane);
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+
+  if (full_steps > 0)
+    copy_step_dma(A, B, N, 0, wave, plan, lds0);
+  else
+    copy_step_masked(A, B, M, N, K, m0, n0, 0, tid, lds);
+  wait_copies();
   __syncthreads();
 
   for (int t = 0; t < steps; ++t) {
-    u32x4* cur = lds + (t & 1) * kBufChunks;
-    u32x4* nxt = lds + ((t + 1) & 1) * kBufChunks;
-    const bool more = t + 1 < steps;
-    if (more) {
-      load_a<kGuard>(A, M, K, m0, (t + 1) * kBK, tid, ra);
-      load_b<kGuard>(B, N, K, n0, (t + 1) * kBK, tid, rb);
-    }
-    const u32x4* as = cur;
-    const u32x4* bt = cur + kBM * kChunks;
+    const int cur = t & 1;
+    LDS_PTR(const uint8_t) sa = lds + cur * kStage;
+    LDS_PTR(const uint8_t) sb = sa + kStageA;
+    LDS_PTR(uint8_t) nxt = lds + (cur ^ 1) * kStage;
+
+    if (t + 1 < full_steps)
+      copy_step_dma(A, B, N, (t + 1) * kBK, wave, plan, lds0 + (cur ^ 1) * kStage);
+
+    bf16x8 a[2][kFragM], b[2][kFragN];
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i) a[0][i] = read_a(sa, wm * kWaveM + i * 32 + lr, lg);
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j) b[0][j] = read_b(sb, wn * kWaveN + j * 32, 0, lane);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
-      const int chunk = 2 * s + lg;
-      bf16x8 a[kFragM], b[kFragN];
+      const int c = s & 1, n = c ^ 1;
+      if (s + 1 < kBK / 16) {
 #pragma unroll
-      for (int i = 0; i < kFragM; ++i) {
-        const int row = wm * kWaveM + i * 32 + lr;
-        a[i] = as_bf16x8(as[row * kChunks + (chunk ^ swz(row))]);
-      }
+        for (int i = 0; i < kFragM; ++i)
+          a[n][i] = read_a(sa, wm * kWaveM + i * 32 + lr, 2 * (s + 1) + lg);
 #pragma unroll
-      for (int j = 0; j < kFragN; ++j) {
-        const int n = wn * kWaveN + j * 32 + lr;
-        b[j] = as_bf16x8(bt[n * kChunks + (chunk ^ swz(n))]);
+        for (int j = 0; j < kFragN; ++j) b[n][j] = read_b(sb, wn * kWaveN + j * 32, s + 1, lane);
       }
 #pragma unroll
       for (int i = 0; i < kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      store_a(nxt, tid, ra);
-      store_bt(nxt, tid, rb);
+    // Instruction order for the scheduler: the 12 reads of sub-step 0, then
+    // for sub-steps 0..2 one read of the next sub-step after each of the
+    // first 12 MFMAs, then the remaining MFMAs.
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+#pragma unroll
+    for (int s = 0; s + 1 < kBK / 16; ++s) {
+#pragma unroll
+      for (int r = 0; r < 12; ++r) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
     }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+
+    // A partial last K step is copied through registers (zeros beyond K).
+    if (t + 1 >= full_steps && t + 1 < steps)
+      copy_step_masked(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, nxt);
+
+    wait_copies();
     __syncthreads();
   }
 
   // Epilogue: element v of a 32 x 32 accumulator sits at
   // row 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
+  const bool full = (m0 + kBM <= M) && (n0 + kBN <= N);
 #pragma unroll
   for (int i = 0; i < kFragM; ++i) {
 #pragma unroll
@@ -208,25 +280,11 @@ __device__ __forceinline__ void tile_product(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * kWaveM + i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3);
-        if (!kGuard || (row < M && col < N))
+        if (full || (row < M && col < N))
           C[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
       }
     }
   }
-}
-
-__global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-    float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-  extern __shared__ u32x4 lds[];
-  int tm, tn;
-  xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * kBM, n0 = tn * kBN;
-  const bool full = (m0 + kBM <= M) && (n0 + kBN <= N) && (K % kBK == 0);
-  if (full)
-    tile_product<false>(A, B, C, M, N, K, m0, n0, lds);
-  else
-    tile_product<true>(A, B, C, M, N, K, m0, n0, lds);
 }
 
 }  // namespace
@@ -235,7 +293,9 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                         int mis_c) {
   (void)M;
   (void)mis_c;
-  return K % 8 == 0 && N % 8 == 0 && K >= 8 && mis_a == 0 && mis_b == 0;
+  // 32-bit per-lane copy offsets: 130 rows of B stay below 4 GiB.
+  return K % 8 == 0 && N % 8 == 0 && K >= 8 && N <= (1 << 24) && mis_a == 0 &&
+         mis_b == 0;
 }
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,

@@ -1,26 +1,36 @@
 // Small-M bf16 product (M <= 16): a bandwidth path.
 //
-// With a handful of rows in A the product does ~2*M FLOPs per byte of B, far
-// below the ridge point, so its time is the time to stream B from HBM once
-// (CS336 Lecture 5 GPU notes, §2.2 roofline; compute- vs memory-bound lesson,
-// what to optimise when memory-bound: read every byte once, in large aligned
-// coalesced blocks; LLM course ch. 15, §15.9 on decode-like steps).
+// With a handful of rows in A the product does about 2*M FLOPs per byte of
+// B, far below the ridge point, so its time is the time to stream B from HBM
+// once (CS336 Lecture 5 GPU notes, §2.2 roofline; compute- vs memory-bound
+// lesson, what to optimise when memory-bound: read every byte once, in large
+// aligned coalesced blocks; LLM course ch. 15, §15.9 on decode-like steps).
 //
-// Layout of the work:
-//   * a workgroup of 16 waves owns a 64-column panel of C (all M rows) and
-//     the whole K range; wave w takes a contiguous 1/16 of K;
-//   * per step of 32 rows of K a wave loads a 32 x 64 block of B with 16-byte
-//     row-contiguous loads (8 lanes per 128-byte row), keeping the next
-//     step's loads in flight while it works on the current one;
-//   * the block is transposed through a wave-private LDS buffer (16-byte
-//     chunks XOR-swizzled so the transposed 2-byte reads hit distinct banks)
-//     into the K-contiguous operand layout of v_mfma_f32_16x16x32_bf16;
-//     four MFMAs cover the 64 columns, with the rows of A (zero beyond M)
-//     as the other operand, read straight from L2 (A is tiny);
-//   * the 16 per-wave partial sums are added in LDS in fixed wave order, so
-//     results are bitwise reproducible.
+// HBM streams well only when neighbouring lanes, waves and workgroups read
+// long contiguous runs, so B is cut into blocks of 256 columns (512-byte row
+// pieces) by a slice of K, sized so that about 512 workgroups run (two per
+// CU):
+//   * a workgroup of 4 waves owns one block. Per step of 32 rows each wave
+//     copies 8 rows straight into an LDS ring of kStages stages
+//     (global_load_lds, 1 KB per instruction, no registers), kStages-1 steps
+//     ahead of the arithmetic;
+//   * each wave then reads its 64 columns back with ds_read_b64_tr_b16,
+//     which hands every lane four consecutive k of one column (the operand
+//     layout of v_mfma_f32_16x16x32_bf16), and runs four MFMAs against the
+//     rows of A (zero beyond M; A is tiny and read from L2);
+//   * the workgroups of one column block each produce a partial 16 x 256
+//     sum and write it to a workspace; a second, small kernel adds the
+//     partials of each output in slice order and writes C, so the result is
+//     bitwise reproducible. (Combining them inside the first kernel would
+//     need device-scope fences, which write back and invalidate whole L2
+//     caches on this chip and cost far more than a second launch.) With a
+//     single slice the partial goes straight to C.
+// A K that is not a multiple of 32 has its last step loaded through
+// registers with the rows beyond K set to zero.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "tdm_internal.h"
 
@@ -30,159 +40,274 @@ namespace {
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 16;
+#define LDS_PTR(T) __attribute__((address_space(3))) T*
+
+constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kPanel = 64;      // columns of C per workgroup
-constexpr int kStepK = 32;      // K rows per MFMA step
+constexpr int kBlockN = 256;                     // columns per workgroup
+constexpr int kRowBytes = kBlockN * 2;           // 512
+constexpr int kStepK = 32;                       // K rows per step
+constexpr int kStageBytes = kStepK * kRowBytes;  // 16 KB
+constexpr int kStages = 4;                       // LDS ring: 64 KB, two workgroups per CU
+constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kMaxM = 16;
-constexpr int kStageBytes = kStepK * kPanel * 2;  // one wave's staging block
+constexpr int kTargetGroups = 512;               // two per CU
+constexpr int kCopiesPerWave = 16 / kWaves;      // 1-KB copies per wave per step
 
-// Physical 16-byte chunk of logical chunk c in staging row k.
-__device__ __forceinline__ int chunk_pos(int k, int c) {
-  return c ^ (((k >> 3) & 3) << 1);
+// Chunk swizzle of the staged rows: the four rows and two chunks that one
+// 16-lane group of a transposed read touches land on distinct banks.
+__device__ __forceinline__ int swz(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
+
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
+  // global -> LDS, 16 bytes per lane, lane l at lds_addr + 16*l. Inline
+  // assembly keeps the compiler from stalling later LDS reads on it; the
+  // wait is explicit (wait_copies_upto) before the barrier that publishes
+  // the stage. M0 carries the LDS address; nothing else here uses M0.
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gptr), "s"(lds_addr)
+               : "memory", "m0");
 }
 
-template <bool kGuard>
-__device__ __forceinline__ void load_step(const uint16_t* __restrict__ B,
-                                          int N, int K, int n0, int k0,
-                                          int lane, u32x4 (&rb)[4]) {
-  const int c = lane & 7;
+template <int N>
+__device__ __forceinline__ void wait_copies_upto() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
+}
+
+// Copy step rows [k0, k0+32) x columns [n0, n0+256) into a stage. Wave w
+// copies rows 8w..8w+7, two rows per instruction; columns past N are
+// clamped (their sums are never stored).
+__device__ __forceinline__ void copy_step(const uint16_t* __restrict__ B, int N, int k0,
+                                          int n0, int wave, int lane, uint32_t stage) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    int gk = k0 + (lane >> 3) + 8 * i;
-    int gn = n0 + c * 8;
-    if (!kGuard) {
-      rb[i] = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    } else {
-      const bool ok = gk < K && gn < N;
-      gk = gk < K ? gk : K - 1;
-      gn = gn < N ? gn : N - 8;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-      rb[i] = ok ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < kCopiesPerWave; ++j) {
+    const int row = (wave * kCopiesPerWave + j) * 2 + (lane >> 5);
+    const int c = (lane & 31) ^ swz(row);
+    const int gn = min(n0 + c * 8, N - 8);
+    dma16(B + static_cast<int64_t>(k0 + row) * N + gn,
+          stage + (wave * kCopiesPerWave + j) * 1024);
   }
 }
 
-__device__ __forceinline__ u32x4 load_a(const uint16_t* __restrict__ A, int M,
-                                        int K, int k0, int lane) {
-  const int m = lane & 15;
-  const int k = k0 + (lane >> 4) * 8;
-  if (m < M && k < K)
-    return *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m) * K + k);
-  return u32x4{0u, 0u, 0u, 0u};
-}
-
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-template <bool kGuard>
-__device__ __forceinline__ void panel_product(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-    float* __restrict__ C, int M, int N, int K, int n0, uint8_t* lds) {
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-
-  // This wave's share of K, in whole steps.
-  const int steps_total = (K + kStepK - 1) / kStepK;
-  const int per_wave = (steps_total + kWaves - 1) / kWaves;
-  const int s_begin = wave * per_wave;
-  const int s_end = min(steps_total, s_begin + per_wave);
-
-  uint8_t* stage = lds + wave * kStageBytes;
-  f32x4 acc[4];
+// The same, through registers, with rows at or beyond K set to zero.
+__device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ B, int N, int K,
+                                                 int k0, int n0, int tid,
+                                                 LDS_PTR(uint8_t) stage) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 rb[4];
-  if (s_begin < s_end) load_step<kGuard>(B, N, K, n0, s_begin * kStepK, lane, rb);
-  for (int s = s_begin; s < s_end; ++s) {
-    const int k0 = s * kStepK;
-    // Stage this step's block; row k of the block, chunk c at chunk_pos.
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int k = (lane >> 3) + 8 * i;
-      const int c = lane & 7;
-      *reinterpret_cast<u32x4*>(stage + k * 128 + chunk_pos(k, c) * 16) = rb[i];
-    }
-    wave_sync();
-    if (s + 1 < s_end) load_step<kGuard>(B, N, K, n0, k0 + kStepK, lane, rb);
-    const bf16x8 a = __builtin_bit_cast(bf16x8, load_a(A, M, K, k0, lane));
-    // Operand of MFMA q: column 16q + lane%16, rows 8*(lane/16) .. +7.
-    const int kb = (lane >> 4) * 8;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = q * 16 + (lane & 15);
-      const int c = col >> 3, e = col & 7;
-      uint32_t w[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const int k_lo = kb + 2 * p, k_hi = kb + 2 * p + 1;
-        const uint32_t lo = *reinterpret_cast<const uint16_t*>(
-            stage + k_lo * 128 + chunk_pos(k_lo, c) * 16 + e * 2);
-        const uint32_t hi = *reinterpret_cast<const uint16_t*>(
-            stage + k_hi * 128 + chunk_pos(k_hi, c) * 16 + e * 2);
-        w[p] = lo | (hi << 16);
-      }
-      const u32x4 bw = {w[0], w[1], w[2], w[3]};
-      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw),
-                                                       acc[q], 0, 0, 0);
-    }
-    wave_sync();
+  for (int i = 0; i < kStageBytes / 16 / kThreads; ++i) {
+    const int id = tid + kThreads * i;
+    const int row = id >> 5, c = id & 31;
+    const int gk = k0 + row;
+    const int gn = min(n0 + c * 8, N - 8);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+    *(LDS_PTR(u32x4))(stage + row * kRowBytes + ((c ^ swz(row)) << 4)) = v;
   }
+}
 
-  // Cross-wave sum in LDS: wave w writes its 16 x 64 partial block.
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(lds);
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = (lane >> 4) * 4 + v;
-      const int col = q * 16 + (lane & 15);
-      red[(wave * kMaxM + row) * kPanel + col] = acc[q][v];
-    }
-  __syncthreads();
-  const int row = tid / kPanel, col = tid % kPanel;
-  float sum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) sum += red[(w * kMaxM + row) * kPanel + col];
-  if (row < M && n0 + col < N) C[static_cast<int64_t>(row) * N + n0 + col] = sum;
+// Four consecutive k (k_base + 0..3) of column n_base + lane%16 (lane j of each
+// 16-lane group receives element e from the address of lane 4e + j/4).
+__device__ __forceinline__ s16x4 read_tr(LDS_PTR(const uint8_t) stage, int k_base, int n_base,
+                                         int lane) {
+  const int i = lane & 15;
+  const int k = k_base + (i >> 2);
+  const int col = n_base + 4 * (i & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(s16x4))(stage + k * kRowBytes + (((col >> 3) ^ swz(k)) << 4) + ((col & 7) << 1)));
 }
 
 __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-    float* __restrict__ C, int M, int N, int K) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * kStageBytes];
-  const int n0 = blockIdx.x * kPanel;
-  const bool full = (n0 + kPanel <= N) && (K % kStepK == 0);
-  if (full)
-    panel_product<false>(A, B, C, M, N, K, n0, lds);
-  else
-    panel_product<true>(A, B, C, M, N, K, n0, lds);
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C,
+    int M, int N, int K, int slices, int slice_steps, float* __restrict__ partials) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int block = blockIdx.x / slices;  // column block
+  const int slice = blockIdx.x - block * slices;
+  const int n0 = block * kBlockN;
+
+  const int steps_total = (K + kStepK - 1) / kStepK;
+  const int full_steps = K / kStepK;
+  const int s_begin = min(steps_total, slice * slice_steps);
+  const int s_end = min(steps_total, s_begin + slice_steps);
+  const int nsteps = s_end - s_begin;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+
+  auto issue = [&](int j) {  // step s_begin + j into stage j % kStages
+    const int st = s_begin + j;
+    if (j >= nsteps) return;
+    const int stage = j % kStages;
+    if (st < full_steps)
+      copy_step(B, N, st * kStepK, n0, wave, lane, lds0 + stage * kStageBytes);
+    else
+      copy_step_masked(B, N, K, st * kStepK, n0, tid, lds + stage * kStageBytes);
+  };
+
+#pragma unroll
+  for (int j = 0; j < kStages - 1; ++j) issue(j);
+
+  f32x4 acc[16 / kWaves];
+#pragma unroll
+  for (int q = 0; q < 16 / kWaves; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int g = lane >> 4;
+  const int m = lane & 15;
+
+  for (int j = 0; j < nsteps; ++j) {
+    // Step j's copies (this wave's) are done once at most the copies of the
+    // kStages-2 later steps are in flight; the barrier makes every wave's
+    // copies visible and frees the stage step j-1 used.
+    // (Only when all of those are copies; near a register-loaded tail step
+    // wait for everything.)
+    if (j + kStages - 2 < nsteps && s_begin + j + kStages - 2 < full_steps)
+      wait_copies_upto<kCopiesPerWave * (kStages - 2)>();
+    else
+      wait_copies_upto<0>();
+    __syncthreads();
+    issue(j + kStages - 1);
+
+    const int k0 = (s_begin + j) * kStepK;
+    const int ka = k0 + 8 * g;
+    const bool a_ok = m < M && ka < K;
+    const u32x4 av = *reinterpret_cast<const u32x4*>(
+        A + static_cast<int64_t>(a_ok ? m : 0) * K + (a_ok ? ka : 0));
+    const bf16x8 a = __builtin_bit_cast(bf16x8, a_ok ? av : u32x4{0u, 0u, 0u, 0u});
+    LDS_PTR(const uint8_t) stage = lds + (j % kStages) * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < 16 / kWaves; ++q) {
+      const int nb = wave * (256 / kWaves) + q * 16;
+      const s16x4 lo = read_tr(stage, 8 * g, nb, lane);
+      const s16x4 hi = read_tr(stage, 8 * g + 4, nb, lane);
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      const u32x4 bw = {l2.x, l2.y, h2.x, h2.y};
+      acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw),
+                                                       acc[q], 0, 0, 0);
+    }
+  }
+
+  // Element v of accumulator q: row 4*(lane/16) + v, column 64*wave + 16q + lane%16.
+  if (slices == 1) {
+#pragma unroll
+    for (int q = 0; q < 16 / kWaves; ++q)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = 4 * g + v, col = n0 + wave * (256 / kWaves) + q * 16 + m;
+        if (row < M && col < N) C[static_cast<int64_t>(row) * N + col] = acc[q][v];
+      }
+    return;
+  }
+
+  // Partial sums: workspace[block][slice][16][256].
+  float* mine = partials + (static_cast<int64_t>(block) * slices + slice) * (kMaxM * kBlockN);
+#pragma unroll
+  for (int q = 0; q < 16 / kWaves; ++q)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      mine[(4 * g + v) * kBlockN + wave * (256 / kWaves) + q * 16 + m] = acc[q][v];
 }
 
-static_assert(kWaves * kMaxM * kPanel * 4 <= kWaves * kStageBytes,
-              "reduction buffer must fit in the staging LDS");
-static_assert(kThreads == kMaxM * kPanel, "one thread per output of the panel");
+// C[row][col] = sum over slices (in slice order) of the partials; four
+// adjacent columns per lane, all slices' loads in flight together.
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partials,
+                                                            float* __restrict__ C, int M, int N,
+                                                            int slices) {
+  constexpr int kPer = kMaxM * kBlockN;           // floats per partial block
+  constexpr int kGroups = kPer / (256 * 4);       // workgroups per column block
+  const int block = blockIdx.x / kGroups;
+  const int e = ((blockIdx.x - block * kGroups) * 256 + threadIdx.x) * 4;
+  const int row = e / kBlockN, col = block * kBlockN + (e - row * kBlockN);
+  if (row >= M || col >= N) return;
+  const f32x4* p = reinterpret_cast<const f32x4*>(partials + static_cast<int64_t>(block) * slices * kPer + e);
+  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  int s = 0;
+  for (; s + 8 <= slices; s += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * (kPer / 4)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sum += v[u];
+  }
+  for (; s < slices; ++s) sum += p[s * (kPer / 4)];
+  float* c = C + static_cast<int64_t>(row) * N + col;
+  // N % 8 == 0 and col % 4 == 0: the four columns are all in range.
+  c[0] = sum.x; c[1] = sum.y; c[2] = sum.z; c[3] = sum.w;
+}
+
+// Per-device workspace for the partial sums. It grows on
+// demand and is kept until the process ends (a kernel may still use the old
+// one when it grows, so that one is never freed).
+struct Workspace {
+  std::mutex mu;
+  void* ptr[64] = {};
+  size_t bytes[64] = {};
+};
+Workspace g_ws;
+
+hipError_t workspace(size_t need, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_ws.mu);
+  if (g_ws.bytes[dev] < need) {
+    void* p = nullptr;
+    const size_t bytes = need < (size_t{8} << 20) ? (size_t{8} << 20) : need;
+    if ((e = hipMalloc(&p, bytes)) != hipSuccess) return e;
+    g_ws.ptr[dev] = p;
+    g_ws.bytes[dev] = bytes;
+  }
+  *out = g_ws.ptr[dev];
+  return hipSuccess;
+}
 
 }  // namespace
 
 bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
                           int mis_b, int mis_c) {
   (void)mis_c;
-  return M >= 1 && M <= kMaxM && N % 8 == 0 && K % 8 == 0 && K >= 8 &&
-         mis_a == 0 && mis_b == 0;
+  return M >= 1 && M <= kMaxM && N % 8 == 0 && K % 8 == 0 && K >= 8 && mis_a == 0 &&
+         mis_b == 0;
 }
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s) {
-  const int panels = (N + kPanel - 1) / kPanel;
-  hipLaunchKernelGGL(skinny_bf16_kernel, dim3(panels), dim3(kThreads), 0, s, A,
-                     B, C, M, N, K);
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(skinny_bf16_kernel),
+      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const int blocks = (N + kBlockN - 1) / kBlockN;
+  const int steps = (K + kStepK - 1) / kStepK;
+  int slices = (kTargetGroups + blocks - 1) / blocks;
+  if (slices > steps) slices = steps;
+  if (slices < 1) slices = 1;
+  const int slice_steps = (steps + slices - 1) / slices;
+  slices = (steps + slice_steps - 1) / slice_steps;  // no empty slices
+  float* partials = nullptr;
+  if (slices > 1) {
+    const size_t part_bytes =
+        static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
+    void* ws = nullptr;
+    hipError_t e = workspace(part_bytes, &ws);
+    if (e != hipSuccess) return e;
+    partials = static_cast<float*>(ws);
+  }
+  hipLaunchKernelGGL(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s,
+                     A, B, C, M, N, K, slices, slice_steps, partials);
+  if (slices > 1) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks * (kMaxM * kBlockN / 1024)), dim3(256),
+                       0, s, partials, C, M, N, slices);
+  }
   return hipGetLastError();
 }
 
