@@ -48,6 +48,7 @@ KERNEL = {  # path -> (kernel symbol, source file)
     "edge": ("edge_kernel", "gemm_edge.hip"),
     "valu": ("valu_f32_kernel", "gemm_valu_f32.hip"),
     "mfma": ("mfma_bf16_kernel", "gemm_mfma_bf16.hip"),
+    "mfma_f32": ("mfma_f32_kernel", "gemm_mfma_f32.hip"),
     "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip"),
 }
 DEFAULT_WORKLOAD = "f32_4096"
@@ -153,7 +154,7 @@ def main():
     path = tdm.Path[args.path.upper()]
     chosen = tdm.tdm_select_path(kind, w.M, w.N, w.K) if path == tdm.Path.AUTO else path
     pname = tdm.path_name(chosen)
-    kernel, ksrc = KERNEL[pname]
+    kernel, ksrc = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else pname]
 
     A, B = inputs.make_inputs(w)
 
@@ -194,7 +195,8 @@ def main():
     if pname == "skinny":
         bound, unit, achieved, peak = "hbm", "GB/s", gbs, PEAK["hbm"]
     elif pname == "mfma":
-        bound, unit, achieved, peak = "mfma", "TFLOP/s", tflops, PEAK["mfma_bf16"]
+        bound, unit, achieved, peak = "mfma", "TFLOP/s", tflops, PEAK[
+            "mfma_f32" if w.kind == "f32" else "mfma_bf16"]
     else:
         bound, unit, achieved, peak = "alu", "TFLOP/s", tflops, PEAK["alu_f32"]
     traffic = traffic_record(kernel, ksrc, w.name)

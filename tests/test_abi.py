@@ -93,7 +93,7 @@ def test_bad_path_and_unsupported_paths():
     S, P = tdm.Status, tdm.Path
     assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 4, 4, 4, 77, None) == S.ERROR_INVALID_VALUE
     # dtype/path mismatches are rejected before any device work
-    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 64, 64, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 64, 62, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
     assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 16, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
     assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 64, 64, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
     # shape/alignment limits of the fast paths
@@ -149,7 +149,7 @@ def test_path_selection():
     assert tdm.tdm_select_path(K.BF16_F32ACC, 16, 8192, 8192) == P.SKINNY
     assert tdm.tdm_select_path(K.BF16_F32ACC, 4096, 4096, 4096) == P.MFMA
     assert tdm.tdm_select_path(K.BF16_F32ACC, 8192, 14336, 4096) == P.MFMA
-    assert tdm.tdm_select_path(K.F32, 4096, 4096, 4096) == P.VALU
+    assert tdm.tdm_select_path(K.F32, 4096, 4096, 4096) == P.MFMA
     assert tdm.tdm_select_path(K.F32, 256, 256, 256) == P.VALU
     assert tdm.tdm_select_path(K.F32, 7, 5, 3) == P.EDGE
     assert tdm.tdm_select_path(K.BF16_F32ACC, 64, 64, 60) == P.EDGE  # K % 8 != 0

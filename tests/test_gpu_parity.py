@@ -51,7 +51,7 @@ def gpu_product(kind, A, B, path=P.AUTO):
 # The small workload, every path.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("path", [P.AUTO, P.EDGE, P.VALU])
+@pytest.mark.parametrize("path", [P.AUTO, P.EDGE, P.VALU, P.MFMA])
 def test_f32_256_workload(path):
     log(f"case f32_256 path={path.name}")
     A, B = inputs.make_inputs("f32_256")
@@ -117,8 +117,8 @@ def test_integer_inputs_bit_exact(kind, shape, path):
 # Closed forms and edge cases on the GPU.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("kind,path", [("f32", P.VALU), ("f32", P.EDGE), ("bf16", P.MFMA),
-                                       ("bf16", P.EDGE)])
+@pytest.mark.parametrize("kind,path", [("f32", P.VALU), ("f32", P.MFMA), ("f32", P.EDGE),
+                                       ("bf16", P.MFMA), ("bf16", P.EDGE)])
 def test_closed_forms(kind, path):
     log(f"case closed forms {kind} path={path.name}")
     M, N, K = 512, 768, 4096

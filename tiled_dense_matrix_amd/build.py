@@ -26,6 +26,7 @@ SOURCES = [
     "gemm_edge.hip",
     "gemm_valu_f32.hip",
     "gemm_mfma_bf16.hip",
+    "gemm_mfma_f32.hip",
     "gemm_skinny_bf16.hip",
 ]
 

@@ -39,7 +39,6 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
               int ma, int mb, int mc) {
   const bool kind_ok =
       (path != TDM_PATH_VALU || kind == TDM_KIND_F32) &&
-      (path != TDM_PATH_MFMA || kind == TDM_KIND_BF16_F32ACC) &&
       (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC);
   if (!kind_ok) return false;
   if (M == 0 || N == 0 || K == 0) return true;  // nothing to run, or a zero fill
@@ -50,7 +49,8 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
     case TDM_PATH_VALU:
       return kind == TDM_KIND_F32 && tdm::valu_f32_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_MFMA:
-      return kind == TDM_KIND_BF16_F32ACC && tdm::mfma_bf16_supports(M, N, K, ma, mb, mc);
+      return kind == TDM_KIND_BF16_F32ACC ? tdm::mfma_bf16_supports(M, N, K, ma, mb, mc)
+                                          : tdm::mfma_f32_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_SKINNY:
       return kind == TDM_KIND_BF16_F32ACC && tdm::skinny_bf16_supports(M, N, K, ma, mb, mc);
   }
@@ -58,10 +58,11 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
 }
 
 // Dispatcher: compare the product's intensity with the ridge point of the
-// unit that would run it. Below the ridge the product is memory-bound and
-// the small-M streaming path is used; above it the compute paths are used.
-// Very small products (under one 32x32 tile's worth of work per CU) go to
-// the edge kernel, whose launch is cheapest.
+// unit that would run it (CS336 Lecture 5 GPU notes, §2.2). Below the ridge a
+// small-M bf16 product is memory-bound and goes to the streaming path; above
+// it the compute paths are used. A product too small to give the matrix-core
+// kernel's 256 x 256 tiles to most CUs goes to the 128 x 128 VALU kernel (fp32)
+// or the edge kernel.
 tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc) {
   if (M <= 0 || N <= 0 || K <= 0) return TDM_PATH_EDGE;
   const double flops = 2.0 * M * N * K;
@@ -76,6 +77,9 @@ tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, 
     return TDM_PATH_EDGE;
   }
   if (M * N <= 64 * 64) return TDM_PATH_EDGE;
+  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  if (big_tiles >= 128 && supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc))
+    return TDM_PATH_MFMA;
   if (supports(kind, TDM_PATH_VALU, M, N, K, ma, mb, mc)) return TDM_PATH_VALU;
   return TDM_PATH_EDGE;
 }
@@ -110,6 +114,7 @@ tdm_status run_f32(const float* A, const float* B, float* C, int64_t M, int64_t 
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   switch (path) {
     case TDM_PATH_VALU: return to_status(tdm::launch_valu_f32(A, B, C, m, n, k, s));
+    case TDM_PATH_MFMA: return to_status(tdm::launch_mfma_f32(A, B, C, m, n, k, s));
     default: return to_status(tdm::launch_edge_f32(A, B, C, m, n, k, s));
   }
 }

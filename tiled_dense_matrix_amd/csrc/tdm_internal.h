@@ -18,6 +18,10 @@ inline bool edge_supports(int64_t, int64_t, int64_t) { return true; }
 bool valu_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                        int mis_c);
 
+// fp32 MFMA kernel: 16-byte chunks along K and N.
+bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
+                       int mis_c);
+
 // bf16 MFMA kernel: 16-byte chunks (8 elements) along K and N.
 bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                         int mis_c);
@@ -35,6 +39,9 @@ hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s);
 
 hipError_t launch_valu_f32(const float* A, const float* B, float* C, int M,
+                           int N, int K, hipStream_t s);
+
+hipError_t launch_mfma_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s);
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
