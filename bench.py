@@ -44,12 +44,13 @@ PEAK = {
     "alu_f32": 157.3,     # TFLOP/s, fp32 vector
     "hbm": 8000.0,        # GB/s
 }
-KERNEL = {  # path -> (kernel symbol, source file)
-    "edge": ("edge_kernel", "gemm_edge.hip"),
-    "valu": ("valu_f32_kernel", "gemm_valu_f32.hip"),
-    "mfma": ("mfma_bf16_kernel", "gemm_mfma_bf16.hip"),
-    "mfma_f32": ("mfma_f32_kernel", "gemm_mfma_f32.hip"),
-    "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip"),
+KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launches)
+    "edge": ("edge_kernel", "gemm_edge.hip", ["edge_kernel"]),
+    "valu": ("valu_f32_kernel", "gemm_valu_f32.hip", ["valu_f32_kernel"]),
+    "mfma": ("mfma_bf16_kernel", "gemm_mfma_bf16.hip", ["mfma_bf16_kernel"]),
+    "mfma_f32": ("mfma_f32_kernel", "gemm_mfma_f32.hip", ["mfma_f32_kernel"]),
+    "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip",
+               ["skinny_bf16_kernel", "skinny_reduce_kernel"]),
 }
 DEFAULT_WORKLOAD = "f32_4096"
 ROTATE_BYTES = 640 << 20  # working set across rotated copies
@@ -77,16 +78,22 @@ def src_digest(fname: str) -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def traffic_record(kernel: str, src: str, workload: str):
-    """HBM bytes per launch from a committed counter record, if still valid."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as fh:
-        rec = json.load(fh)
-    if rec.get("source_sha") != src_digest(src):
-        return None  # the kernel changed since the counters were taken
-    return float(rec["hbm_bytes_per_launch"])
+def traffic_record(kernels, src: str, workload: str):
+    """HBM bytes per call (all its kernels) from committed counter records.
+
+    None unless every kernel has a record taken from the current source.
+    """
+    total = 0.0
+    for kernel in kernels:
+        path = os.path.join(ROOT, "profiles", f"{kernel}.{workload}.traffic.json")
+        if not os.path.exists(path):
+            return None
+        with open(path) as fh:
+            rec = json.load(fh)
+        if rec.get("source_sha") != src_digest(src):
+            return None  # the kernel changed since the counters were taken
+        total += float(rec["hbm_bytes_per_launch"])
+    return total
 
 
 def copy_probe(mib: int):
@@ -106,12 +113,14 @@ def cpu_baseline(w, A, B, C_gpu, target_s: float):
     """Time the oracle on the first rows of C; also check those rows."""
     import oracle
     threads = oracle.default_threads()
-    rows = 1
+    # Calibrate on one row per thread, then size the sample to ~target_s.
+    rows = min(w.M, threads)
     t0 = time.perf_counter()
     oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
-    t1 = max(time.perf_counter() - t0, 1e-6)
-    rows = int(min(w.M, max(1, math.floor(target_s / t1))))
-    rows = max(1, min(rows, w.M))
+    per_row = max(time.perf_counter() - t0, 1e-6) / rows
+    rows = int(max(1, min(w.M, math.floor(target_s / per_row))))
+    if rows >= threads:
+        rows -= rows % threads  # whole rows per thread
     t0 = time.perf_counter()
     R = oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
     dt = time.perf_counter() - t0
@@ -154,7 +163,7 @@ def main():
     path = tdm.Path[args.path.upper()]
     chosen = tdm.tdm_select_path(kind, w.M, w.N, w.K) if path == tdm.Path.AUTO else path
     pname = tdm.path_name(chosen)
-    kernel, ksrc = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else pname]
+    kernel, ksrc, kernels = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else pname]
 
     A, B = inputs.make_inputs(w)
 
@@ -199,7 +208,7 @@ def main():
             "mfma_f32" if w.kind == "f32" else "mfma_bf16"]
     else:
         bound, unit, achieved, peak = "alu", "TFLOP/s", tflops, PEAK["alu_f32"]
-    traffic = traffic_record(kernel, ksrc, w.name)
+    traffic = traffic_record(kernels, ksrc, w.name)
 
     # Every rotated copy must hold the same product (spot check: first rows).
     C_gpu = sets[(args.warmup + args.steps - 1) % rot][2].cpu().numpy()
@@ -222,7 +231,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "inputs": f"seed {w.seed}, {w.dist}",
-                   "path": pname, "kernel": kernel, "rotated_copies": rot,
+                   "path": pname, "kernel": kernel, "kernels_per_call": kernels,
+                   "rotated_copies": rot,
                    "gbps_algorithmic": round(gbs, 1)},
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4),

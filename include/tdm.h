@@ -15,7 +15,11 @@
  *     notes, §4.1, on row-major storage). There are no leading dimensions;
  *     a strided or transposed view must be made contiguous by the caller.
  *   - A, B and C are DEVICE pointers on the current HIP device, owned by the
- *     caller. The library allocates no memory in these calls.
+ *     caller. The only memory the library allocates is the small-M path's
+ *     per-device workspace for partial sums (about 8 MB for M <= 16,
+ *     N = 8192), allocated on that path's first use and kept until the
+ *     process ends. Two small-M calls running at the same time on one device
+ *     (on different streams) share it and race.
  *   - A and B are read only. C is overwritten (there is no alpha/beta). C
  *     must not overlap A or B.
  *   - Element sizes: fp32 = 4 bytes; bf16 = 2 bytes passed as raw uint16_t
