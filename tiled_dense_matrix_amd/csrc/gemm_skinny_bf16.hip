@@ -62,11 +62,12 @@ constexpr int kCopiesPerWave = 16 / kWaves;      // 1-KB copies per wave per ste
 __device__ __forceinline__ int swz(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  // global -> LDS, 16 bytes per lane, lane l at lds_addr + 16*l. Inline
+  // global -> LDS, 16 bytes per lane, lane l at lds_addr + 16*l, marked
+  // non-temporal (B is read once and should not displace A in L2). Inline
   // assembly keeps the compiler from stalling later LDS reads on it; the
   // wait is explicit (wait_copies_upto) before the barrier that publishes
   // the stage. M0 carries the LDS address; nothing else here uses M0.
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(gptr), "s"(lds_addr)
                : "memory", "m0");
@@ -215,31 +216,28 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
       mine[(4 * g + v) * kBlockN + wave * (256 / kWaves) + q * 16 + m] = acc[q][v];
 }
 
-// C[row][col] = sum over slices (in slice order) of the partials; four
-// adjacent columns per lane, all slices' loads in flight together.
+// C[row][col] = sum over slices (in slice order) of the partials.
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partials,
                                                             float* __restrict__ C, int M, int N,
                                                             int slices) {
-  constexpr int kPer = kMaxM * kBlockN;           // floats per partial block
-  constexpr int kGroups = kPer / (256 * 4);       // workgroups per column block
+  constexpr int kPer = kMaxM * kBlockN;  // floats per partial block
+  constexpr int kGroups = kPer / 256;    // workgroups per column block
   const int block = blockIdx.x / kGroups;
-  const int e = ((blockIdx.x - block * kGroups) * 256 + threadIdx.x) * 4;
+  const int e = (blockIdx.x - block * kGroups) * 256 + threadIdx.x;
   const int row = e / kBlockN, col = block * kBlockN + (e - row * kBlockN);
   if (row >= M || col >= N) return;
-  const f32x4* p = reinterpret_cast<const f32x4*>(partials + static_cast<int64_t>(block) * slices * kPer + e);
-  f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+  const float* p = partials + static_cast<int64_t>(block) * slices * kPer + e;
+  float sum = 0.f;
   int s = 0;
   for (; s + 8 <= slices; s += 8) {
-    f32x4 v[8];
+    float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * (kPer / 4)];
+    for (int u = 0; u < 8; ++u) v[u] = p[(s + u) * kPer];
 #pragma unroll
     for (int u = 0; u < 8; ++u) sum += v[u];
   }
-  for (; s < slices; ++s) sum += p[s * (kPer / 4)];
-  float* c = C + static_cast<int64_t>(row) * N + col;
-  // N % 8 == 0 and col % 4 == 0: the four columns are all in range.
-  c[0] = sum.x; c[1] = sum.y; c[2] = sum.z; c[3] = sum.w;
+  for (; s < slices; ++s) sum += p[s * kPer];
+  C[static_cast<int64_t>(row) * N + col] = sum;
 }
 
 // Per-device workspace for the partial sums. It grows on
@@ -305,7 +303,7 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
   if (slices > 1) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks * (kMaxM * kBlockN / 1024)), dim3(256),
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks * (kMaxM * kBlockN / 256)), dim3(256),
                        0, s, partials, C, M, N, slices);
   }
   return hipGetLastError();
