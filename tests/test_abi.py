@@ -150,7 +150,9 @@ def test_path_selection():
     assert tdm.tdm_select_path(K.BF16_F32ACC, 4096, 4096, 4096) == P.MFMA
     assert tdm.tdm_select_path(K.BF16_F32ACC, 8192, 14336, 4096) == P.MFMA
     assert tdm.tdm_select_path(K.F32, 4096, 4096, 4096) == P.MFMA
-    assert tdm.tdm_select_path(K.F32, 256, 256, 256) == P.VALU
+    assert tdm.tdm_select_path(K.F32, 256, 256, 256) == P.EDGE   # 4 tiles of 128 x 128
+    assert tdm.tdm_select_path(K.F32, 512, 512, 512) == P.MFMA   # 16 tiles
+    assert tdm.tdm_select_path(K.F32, 512, 512, 510) == P.EDGE   # K % 4 != 0
     assert tdm.tdm_select_path(K.F32, 7, 5, 3) == P.EDGE
     assert tdm.tdm_select_path(K.BF16_F32ACC, 64, 64, 60) == P.EDGE  # K % 8 != 0
 

@@ -100,6 +100,30 @@ def test_ragged(kind, shape, path):
     check_full(kind, A, B, gpu_product(kind, A, B, path), f"{kind}/{shape}/{path.name}")
 
 
+# Shapes large enough that the matrix-core kernels take their 256 x 256 tiles
+# (the last round of tiles over the 256 CUs is at least 70% full for bf16,
+# 90% for fp32), with partial tiles in M, N and K.
+LARGE_TILE_RAGGED = [("bf16", (3600, 3000, 200)), ("f32", (3900, 4000, 100))]
+
+
+def _fill(M, N):
+    tiles = -(-M // 256) * -(-N // 256)
+    return tiles / (-(-tiles // 256) * 256)
+
+
+@pytest.mark.parametrize("kind,shape", LARGE_TILE_RAGGED)
+def test_large_tile_ragged(kind, shape):
+    M, N, K = shape
+    assert _fill(M, N) >= (0.7 if kind == "bf16" else 0.9)
+    log(f"case large-tile ragged {kind} {shape}")
+    A, B = random_inputs(kind, M, N, K, seed=M + N + K)
+    check_full(kind, A, B, gpu_product(kind, A, B, P.MFMA), f"{kind}/{shape}/MFMA")
+    rng = np.random.default_rng(17)
+    A = inputs.small_int_matrix(rng, (M, K), kind=kind)
+    B = inputs.small_int_matrix(rng, (K, N), kind=kind)
+    assert np.array_equal(gpu_product(kind, A, B, P.MFMA).astype(np.float64), oracle.gemm(A, B))
+
+
 @pytest.mark.parametrize("kind,shape,path", list(_ragged_cases()))
 def test_integer_inputs_bit_exact(kind, shape, path):
     """Small integers: every partial sum is an exactly representable integer."""
@@ -203,12 +227,14 @@ def test_misaligned_pointers():
 # Full-size workloads, in the launch configuration the benchmark times.
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["f32_4096", "bf16_4096", "bf16_8192", "bf16_mlp"])
-def test_full_size_workload(name):
+@pytest.mark.parametrize("name,path", [("f32_4096", P.AUTO), ("f32_4096", P.VALU),
+                                       ("bf16_4096", P.AUTO), ("bf16_8192", P.AUTO),
+                                       ("bf16_mlp", P.AUTO)])
+def test_full_size_workload(name, path):
     w = inputs.WORKLOADS[name]
-    log(f"case workload {name} {w.M}x{w.N}x{w.K}")
+    log(f"case workload {name} {w.M}x{w.N}x{w.K} path={path.name}")
     A, B = inputs.make_inputs(w)
-    C = gpu_product(w.kind, A, B, P.AUTO)
+    C = gpu_product(w.kind, A, B, path)
     tiles = inputs.sample_tiles(w.M, w.N)
     # include the four corners so partial-tile logic and the last tile are seen
     tiles = sorted(set(tiles) | {(0, 0), (0, w.N - 32), (w.M - 32, 0), (w.M - 32, w.N - 32)})

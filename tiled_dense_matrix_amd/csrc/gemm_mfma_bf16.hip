@@ -3,12 +3,14 @@
 // Method (CS336 Lecture 5 GPU notes, §4.2 tiling, register blocking and
 // double buffering; §3.2 low-precision products with fp32 accumulation;
 // LLM course ch. 15 "GPU", §15.6 table of GEMM techniques):
-//   * one workgroup owns a 256 x 256 tile of C and walks K in steps of 64;
-//   * each step copies a 256 x 64 slice of A and a 64 x 256 slice of B from
-//     HBM into LDS with 16-byte row-contiguous loads that write LDS directly
+//   * one workgroup owns a BM x BN tile of C (256 x 256, or 128 x 128 when a
+//     product has too few large tiles to occupy the CUs) and walks K in steps
+//     of 64;
+//   * each step copies a BM x 64 slice of A and a 64 x BN slice of B from HBM
+//     into LDS with 16-byte row-contiguous loads that write LDS directly
 //     (global_load_lds), so the copy costs no registers and no LDS stores;
-//   * the four waves (2 x 2) each hold a 128 x 128 block of C in registers
-//     (4 x 4 accumulators of 32 x 32) fed by v_mfma_f32_32x32x16_bf16;
+//   * the four waves (2 x 2) each hold a (BM/2) x (BN/2) block of C in
+//     registers as 32 x 32 accumulators fed by v_mfma_f32_32x32x16_bf16;
 //   * LDS is double-buffered: the copy of step t+1 runs while the waves
 //     multiply step t; one barrier per step separates the two.
 //
@@ -16,7 +18,7 @@
 // one row of A and of one column of B.
 //   A stays row-major in LDS, As[m][k] (128 bytes per row), and is read with
 //   16-byte loads. Chunk c (8 k values) of row m sits at chunk c ^ swz_a(m).
-//   B stays row-major too, Bs[k][n] (512 bytes per row), and is read with
+//   B stays row-major too, Bs[k][n] (2*BN bytes per row), and is read with
 //   ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
 //   element e from the address of lane 4e + j/4, so lanes that point at four
 //   consecutive n of rows k..k+3 come back holding four consecutive k of one
@@ -29,8 +31,6 @@
 // out-of-range elements set to zero.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "tdm_internal.h"
 #include "tile_map.h"
@@ -46,22 +46,32 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
-constexpr int kBM = 256;
-constexpr int kBN = 256;
-constexpr int kBK = 64;
 constexpr int kThreads = 256;
-constexpr int kRowA = kBK * 2;                 // bytes per LDS row of A
-constexpr int kRowB = kBN * 2;                 // bytes per LDS row of B
-constexpr int kStageA = kBM * kRowA;           // 32 KB
-constexpr int kStageB = kBK * kRowB;           // 32 KB
-constexpr int kStage = kStageA + kStageB;      // 64 KB
-constexpr int kLdsBytes = 2 * kStage;          // double-buffered
-constexpr int kWaveM = 128, kWaveN = 128;      // per-wave block of C
-constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
+constexpr int kBK = 64;
+constexpr int kRowA = kBK * 2;  // bytes per LDS row of A
 constexpr int kGroupM = 4;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+
+// Tile geometry. Copies move 1 KB of LDS per wave instruction.
+template <int BM, int BN>
+struct Tile {
+  static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kRowB = BN * 2;               // bytes per LDS row of B
+  static constexpr int kStageA = BM * kRowA;
+  static constexpr int kStageB = kBK * kRowB;
+  static constexpr int kStage = kStageA + kStageB;
+  static constexpr int kLdsBytes = 2 * kStage;       // double-buffered
+  static constexpr int kWaveM = BM / 2, kWaveN = BN / 2;
+  static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
+  static constexpr int kCopyA = kStageA / 1024 / 4;  // copies per wave
+  static constexpr int kCopyB = kStageB / 1024 / 4;
+  static constexpr int kRowsPerCopyB = 1024 / kRowB;
+  static constexpr int kLanesPerRowB = kRowB / 16;
+  static constexpr int kReads = kFragM + 2 * kFragN;  // LDS reads per k16 sub-step
+  static constexpr int kMfmas = kFragM * kFragN;      // MFMAs per k16 sub-step
+};
 
 __device__ __forceinline__ int swz_a(int m) { return (m ^ (m >> 3)) & 7; }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
@@ -83,27 +93,29 @@ __device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Per-lane byte offsets of this wave's 8 + 8 copy instructions; the K step
-// only moves the scalar base pointers.
+// Per-lane byte offsets of this wave's copy instructions; the K step only
+// moves the scalar base pointers.
+template <class T>
 struct CopyPlan {
-  uint32_t a[8];
-  uint32_t b[8];
+  uint32_t a[T::kCopyA];
+  uint32_t b[T::kCopyB];
 };
 
-__device__ __forceinline__ CopyPlan make_plan(int M, int N, int K, int m0, int n0, int wave,
-                                              int lane) {
-  CopyPlan p;
+template <class T>
+__device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, int n0, int wave,
+                                                 int lane) {
+  CopyPlan<T> p;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {  // A: 32 blocks of 8 rows, wave w owns 8w..8w+7
-    const int row = (wave * 8 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < T::kCopyA; ++j) {  // A: blocks of 8 rows
+    const int row = (wave * T::kCopyA + j) * 8 + (lane >> 3);
     const int c = (lane & 7) ^ swz_a(row);
     const int gm = min(m0 + row, M - 1);
     p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(gm) * K + c * 8) * 2);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {  // B: 32 blocks of 2 rows
-    const int row = (wave * 8 + j) * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ swz_b(row);
+  for (int j = 0; j < T::kCopyB; ++j) {  // B: blocks of kRowsPerCopyB rows
+    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kLanesPerRowB;
+    const int c = (lane % T::kLanesPerRowB) ^ swz_b(row);
     const int gn = min(n0 + c * 8, N - 8);
     p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + gn) * 2);
   }
@@ -111,28 +123,29 @@ __device__ __forceinline__ CopyPlan make_plan(int M, int N, int K, int m0, int n
 }
 
 // --- global -> LDS copy of one full K step (clamped M/N) -----------------
-// Each wave instruction writes 1 KB of LDS.
+template <class T>
 __device__ __forceinline__ void copy_step_dma(const uint16_t* __restrict__ A,
-                                              const uint16_t* __restrict__ B, int N,
-                                              int k0, int wave, const CopyPlan& p,
-                                              uint32_t stage) {
+                                              const uint16_t* __restrict__ B, int N, int k0,
+                                              int wave, const CopyPlan<T>& p, uint32_t stage) {
   const uint16_t* a_base = A + k0;
   const uint16_t* b_base = B + static_cast<int64_t>(k0) * N;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(a_base, p.a[j], stage + (wave * 8 + j) * 1024);
+  for (int j = 0; j < T::kCopyA; ++j)
+    dma16(a_base, p.a[j], stage + (wave * T::kCopyA + j) * 1024);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(b_base, p.b[j], stage + kStageA + (wave * 8 + j) * 1024);
+  for (int j = 0; j < T::kCopyB; ++j)
+    dma16(b_base, p.b[j], stage + T::kStageA + (wave * T::kCopyB + j) * 1024);
 }
 
 // Same layout, through registers, with zeros beyond K (the partial last step).
+template <class T>
 __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
-                                                 const uint16_t* __restrict__ B,
-                                                 int M, int N, int K, int m0, int n0,
-                                                 int k0, int tid,
+                                                 const uint16_t* __restrict__ B, int M, int N,
+                                                 int K, int m0, int n0, int k0, int tid,
                                                  LDS_PTR(uint8_t) stage) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // A: 2048 chunks, 8 per lane
+  for (int i = 0; i < T::kStageA / 16 / kThreads; ++i) {  // A chunks
     const int id = tid + kThreads * i;
     const int row = id >> 3, c = id & 7;
     const int gk = k0 + c * 8;
@@ -141,16 +154,16 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
     if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
     *(LDS_PTR(u32x4))(stage + row * kRowA + ((c ^ swz_a(row)) << 4)) = v;
   }
-  LDS_PTR(uint8_t) sb = stage + kStageA;
+  LDS_PTR(uint8_t) sb = stage + T::kStageA;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {  // B: 2048 chunks, 8 per lane
+  for (int i = 0; i < T::kStageB / 16 / kThreads; ++i) {  // B chunks
     const int id = tid + kThreads * i;
-    const int row = id >> 5, c = id & 31;
+    const int row = id / T::kLanesPerRowB, c = id % T::kLanesPerRowB;
     const int gk = k0 + row;
     const int gn = min(n0 + c * 8, N - 8);
     u32x4 v = zero;
     if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    *(LDS_PTR(u32x4))(sb + row * kRowB + ((c ^ swz_b(row)) << 4)) = v;
+    *(LDS_PTR(u32x4))(sb + row * T::kRowB + ((c ^ swz_b(row)) << 4)) = v;
   }
 }
 
@@ -164,6 +177,7 @@ __device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int
 }
 
 // Eight consecutive k (16s + 8*(lane/32) + 0..7) of column n_base + lane%32.
+template <class T>
 __device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, int s,
                                          int lane) {
   const int g = lane >> 4, i = lane & 15;
@@ -172,23 +186,25 @@ __device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, 
   const int r0 = 16 * s + 8 * (g >> 1) + (i >> 2);
   const int r1 = r0 + 4;
   const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LDS_PTR(s16x4))(sb + r0 * kRowB + ((c ^ swz_b(r0)) << 4) + half));
+      (LDS_PTR(s16x4))(sb + r0 * T::kRowB + ((c ^ swz_b(r0)) << 4) + half));
   const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LDS_PTR(s16x4))(sb + r1 * kRowB + ((c ^ swz_b(r1)) << 4) + half));
+      (LDS_PTR(s16x4))(sb + r1 * T::kRowB + ((c ^ swz_b(r1)) << 4) + half));
   const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
   const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
   return __builtin_bit_cast(bf16x8, v);
 }
 
+template <int BM, int BN>
 __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+  using T = Tile<BM, BN>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
 
   int tm, tn;
   xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * kBM, n0 = tn * kBN;
+  const int m0 = tm * BM, n0 = tn * BN;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
@@ -196,74 +212,79 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
   const int wm = wave >> 1, wn = wave & 1;
   const int lr = lane & 31, lg = lane >> 5;
 
-  f32x16 acc[kFragM][kFragN];
+  f32x16 acc[T::kFragM][T::kFragN];
 #pragma unroll
-  for (int i = 0; i < kFragM; ++i)
+  for (int i = 0; i < T::kFragM; ++i)
 #pragma unroll
-    for (int j = 0; j < kFragN; ++j)
+    for (int j = 0; j < T::kFragN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
   const int steps = (K + kBK - 1) / kBK;
   const int full_steps = K / kBK;  // steps whose 64 k are all in range
-  const CopyPlan plan = make_plan(M, N, K, m0, n0, wave, lane);
+  const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
 
   if (full_steps > 0)
-    copy_step_dma(A, B, N, 0, wave, plan, lds0);
+    copy_step_dma<T>(A, B, N, 0, wave, plan, lds0);
   else
-    copy_step_masked(A, B, M, N, K, m0, n0, 0, tid, lds);
+    copy_step_masked<T>(A, B, M, N, K, m0, n0, 0, tid, lds);
   wait_copies();
   __syncthreads();
 
   for (int t = 0; t < steps; ++t) {
     const int cur = t & 1;
-    LDS_PTR(const uint8_t) sa = lds + cur * kStage;
-    LDS_PTR(const uint8_t) sb = sa + kStageA;
-    LDS_PTR(uint8_t) nxt = lds + (cur ^ 1) * kStage;
+    LDS_PTR(const uint8_t) sa = lds + cur * T::kStage;
+    LDS_PTR(const uint8_t) sb = sa + T::kStageA;
+    LDS_PTR(uint8_t) nxt = lds + (cur ^ 1) * T::kStage;
 
     if (t + 1 < full_steps)
-      copy_step_dma(A, B, N, (t + 1) * kBK, wave, plan, lds0 + (cur ^ 1) * kStage);
+      copy_step_dma<T>(A, B, N, (t + 1) * kBK, wave, plan, lds0 + (cur ^ 1) * T::kStage);
 
-    bf16x8 a[2][kFragM], b[2][kFragN];
+    bf16x8 a[2][T::kFragM], b[2][T::kFragN];
 #pragma unroll
-    for (int i = 0; i < kFragM; ++i) a[0][i] = read_a(sa, wm * kWaveM + i * 32 + lr, lg);
+    for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a(sa, wm * T::kWaveM + i * 32 + lr, lg);
 #pragma unroll
-    for (int j = 0; j < kFragN; ++j) b[0][j] = read_b(sb, wn * kWaveN + j * 32, 0, lane);
+    for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(sb, wn * T::kWaveN + j * 32, 0, lane);
 #pragma unroll
     for (int s = 0; s < kBK / 16; ++s) {
       const int c = s & 1, n = c ^ 1;
       if (s + 1 < kBK / 16) {
 #pragma unroll
-        for (int i = 0; i < kFragM; ++i)
-          a[n][i] = read_a(sa, wm * kWaveM + i * 32 + lr, 2 * (s + 1) + lg);
+        for (int i = 0; i < T::kFragM; ++i)
+          a[n][i] = read_a(sa, wm * T::kWaveM + i * 32 + lr, 2 * (s + 1) + lg);
 #pragma unroll
-        for (int j = 0; j < kFragN; ++j) b[n][j] = read_b(sb, wn * kWaveN + j * 32, s + 1, lane);
+        for (int j = 0; j < T::kFragN; ++j)
+          b[n][j] = read_b<T>(sb, wn * T::kWaveN + j * 32, s + 1, lane);
       }
 #pragma unroll
-      for (int i = 0; i < kFragM; ++i)
+      for (int i = 0; i < T::kFragM; ++i)
 #pragma unroll
-        for (int j = 0; j < kFragN; ++j)
+        for (int j = 0; j < T::kFragN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
     }
-    // Instruction order for the scheduler: the 12 reads of sub-step 0, then
-    // for sub-steps 0..2 one read of the next sub-step after each of the
-    // first 12 MFMAs, then the remaining MFMAs.
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 12, 0);
+    // Instruction order for the scheduler: the reads of sub-step 0, then for
+    // each later sub-step one of its reads after each MFMA of the previous
+    // sub-step (leftover reads or MFMAs follow), then the last sub-step.
+    constexpr int kPairs = T::kReads < T::kMfmas ? T::kReads : T::kMfmas;
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads, 0);
 #pragma unroll
     for (int s = 0; s + 1 < kBK / 16; ++s) {
 #pragma unroll
-      for (int r = 0; r < 12; ++r) {
+      for (int r = 0; r < kPairs; ++r) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+      if (T::kMfmas > kPairs)
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas - kPairs, 0);
+      if (T::kReads > kPairs)
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads - kPairs, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 16, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas, 0);
 
     // A partial last K step is copied through registers (zeros beyond K).
     if (t + 1 >= full_steps && t + 1 < steps)
-      copy_step_masked(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, nxt);
+      copy_step_masked<T>(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, nxt);
 
     wait_copies();
     __syncthreads();
@@ -271,20 +292,36 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
 
   // Epilogue: element v of a 32 x 32 accumulator sits at
   // row 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
-  const bool full = (m0 + kBM <= M) && (n0 + kBN <= N);
+  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
 #pragma unroll
-  for (int i = 0; i < kFragM; ++i) {
+  for (int i = 0; i < T::kFragM; ++i) {
 #pragma unroll
-    for (int j = 0; j < kFragN; ++j) {
-      const int col = n0 + wn * kWaveN + j * 32 + lr;
+    for (int j = 0; j < T::kFragN; ++j) {
+      const int col = n0 + wn * T::kWaveN + j * 32 + lr;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * kWaveM + i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3);
+        const int row = m0 + wm * T::kWaveM + i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3);
         if (full || (row < M && col < N))
           C[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
       }
     }
   }
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K,
+                       hipStream_t s) {
+  using T = Tile<BM, BN>;
+  // Opt in to more than 64 KB of dynamic LDS (done once per process).
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(mfma_bf16_kernel<BM, BN>),
+      hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
+  if (attr != hipSuccess) return attr;
+  const int tiles_m = (M + BM - 1) / BM;
+  const int tiles_n = (N + BN - 1) / BN;
+  hipLaunchKernelGGL((mfma_bf16_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(kThreads),
+                     T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -300,16 +337,9 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
-  // Opt in to more than 64 KB of dynamic LDS (done once per process).
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(mfma_bf16_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (attr != hipSuccess) return attr;
-  const int tiles_m = (M + kBM - 1) / kBM;
-  const int tiles_n = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(mfma_bf16_kernel, dim3(tiles_m * tiles_n), dim3(kThreads),
-                     kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
-  return hipGetLastError();
+  if (use_large_tiles(M, N, kLargeTileFillBf16))
+    return launch_tile<256, 256>(A, B, C, M, N, K, s);
+  return launch_tile<128, 128>(A, B, C, M, N, K, s);
 }
 
 }  // namespace tdm

@@ -3,15 +3,15 @@
 // Method (CS336 Lecture 5 GPU notes, §4.2: tiling, register blocking and a
 // double-buffered pipeline; §4.1: coalesced loads, then any access pattern
 // from shared memory):
-//   * one workgroup of 256 lanes owns a 128 x 128 tile of C and walks K in
+//   * one workgroup of 256 lanes owns a 128 x 256 tile of C and walks K in
 //     steps of 16;
-//   * each step the lanes copy a 128 x 16 slice of A and a 16 x 128 slice of
+//   * each step the lanes copy a 128 x 16 slice of A and a 16 x 256 slice of
 //     B from HBM with 16-byte row-contiguous loads; A is written to LDS
 //     transposed (As[k][m]) so that the inner loop reads both operands as
 //     16-byte vectors;
-//   * every lane keeps an 8 x 8 block of C in registers (rows 4*ty..+3 and
-//     64+4*ty..+3, columns 4*tx..+3 and 64+4*tx..+3) and per k does 64
-//     fused multiply-adds from four 16-byte LDS reads;
+//   * every lane keeps an 8 x 16 block of C in registers (rows 4*ty + 64*g,
+//     columns 4*tx + 64*h, in groups of 4) and per k does 128 fused
+//     multiply-adds from six 16-byte LDS reads;
 //   * LDS is double-buffered with one barrier per step.
 // Each output is accumulated in fp32 with k ascending.
 #include <hip/hip_runtime.h>
@@ -25,24 +25,32 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
+// Each lane owns 4*kTMG rows (groups of 4, 64 rows apart) by 4*kTNG columns
+// (groups of 4, 64 columns apart) of the tile: 8 x 16 = 128 accumulators.
+constexpr int kTMG = 2, kTNG = 4;
+constexpr int kBM = 64 * kTMG;
+constexpr int kBN = 64 * kTNG;
 constexpr int kBK = 16;
 constexpr int kThreads = 256;
-constexpr int kPitch = kBM + 4;  // floats per LDS row (keeps 16-byte alignment)
-constexpr int kStage = 2 * kBK * kPitch;  // As then Bs, floats
+constexpr int kPitchA = kBM + 4;  // floats per LDS row (keeps 16-byte alignment)
+constexpr int kPitchB = kBN + 4;
+constexpr int kStage = kBK * (kPitchA + kPitchB);  // As then Bs, floats
+constexpr int kLA = kBM * kBK / 4 / kThreads;  // 16-byte A loads per lane
+constexpr int kLB = kBN * kBK / 4 / kThreads;
+constexpr int kAPerRow = kBK / 4;               // 16-byte chunks per A row
 constexpr int kGroupM = 8;
 
 template <bool kGuard>
 __device__ __forceinline__ void load_tiles(const float* __restrict__ A,
                                            const float* __restrict__ B, int M,
                                            int N, int K, int m0, int n0, int k0,
-                                           int tid, f32x4 (&ra)[2],
-                                           f32x4 (&rb)[2]) {
+                                           int tid, f32x4 (&ra)[kLA],
+                                           f32x4 (&rb)[kLB]) {
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int gm = m0 + (tid >> 2) + 64 * i;
-    int gk = k0 + (tid & 3) * 4;
+  for (int i = 0; i < kLA; ++i) {
+    const int id = tid + kThreads * i;
+    int gm = m0 + id / kAPerRow;
+    int gk = k0 + (id % kAPerRow) * 4;
     if (!kGuard) {
       ra[i] = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
     } else {
@@ -54,9 +62,10 @@ __device__ __forceinline__ void load_tiles(const float* __restrict__ A,
     }
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int gk = k0 + (tid >> 5) + 8 * i;
-    int gn = n0 + (tid & 31) * 4;
+  for (int i = 0; i < kLB; ++i) {
+    const int id = tid + kThreads * i;
+    int gk = k0 + id / (kBN / 4);
+    int gn = n0 + (id % (kBN / 4)) * 4;
     if (!kGuard) {
       rb[i] = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
     } else {
@@ -70,24 +79,26 @@ __device__ __forceinline__ void load_tiles(const float* __restrict__ A,
 }
 
 __device__ __forceinline__ void store_tiles(float* __restrict__ stage, int tid,
-                                            const f32x4 (&ra)[2],
-                                            const f32x4 (&rb)[2]) {
+                                            const f32x4 (&ra)[kLA],
+                                            const f32x4 (&rb)[kLB]) {
   float* as = stage;
-  float* bs = stage + kBK * kPitch;
+  float* bs = stage + kBK * kPitchA;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int m = (tid >> 2) + 64 * i;
-    const int k = (tid & 3) * 4;
-    as[(k + 0) * kPitch + m] = ra[i].x;
-    as[(k + 1) * kPitch + m] = ra[i].y;
-    as[(k + 2) * kPitch + m] = ra[i].z;
-    as[(k + 3) * kPitch + m] = ra[i].w;
+  for (int i = 0; i < kLA; ++i) {
+    const int id = tid + kThreads * i;
+    const int m = id / kAPerRow;
+    const int k = (id % kAPerRow) * 4;
+    as[(k + 0) * kPitchA + m] = ra[i].x;
+    as[(k + 1) * kPitchA + m] = ra[i].y;
+    as[(k + 2) * kPitchA + m] = ra[i].z;
+    as[(k + 3) * kPitchA + m] = ra[i].w;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int k = (tid >> 5) + 8 * i;
-    const int n = (tid & 31) * 4;
-    *reinterpret_cast<f32x4*>(bs + k * kPitch + n) = rb[i];
+  for (int i = 0; i < kLB; ++i) {
+    const int id = tid + kThreads * i;
+    const int k = id / (kBN / 4);
+    const int n = (id % (kBN / 4)) * 4;
+    *reinterpret_cast<f32x4*>(bs + k * kPitchB + n) = rb[i];
   }
 }
 
@@ -100,14 +111,15 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
   const int tid = threadIdx.x;
   const int ty = tid >> 4, tx = tid & 15;
 
-  float acc[8][8];
+  constexpr int RM = 4 * kTMG, RN = 4 * kTNG;
+  float acc[RM][RN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < RM; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
+    for (int j = 0; j < RN; ++j) acc[i][j] = 0.f;
 
   const int steps = (K + kBK - 1) / kBK;
-  f32x4 ra[2], rb[2];
+  f32x4 ra[kLA], rb[kLB];
   load_tiles<kGuard>(A, B, M, N, K, m0, n0, 0, tid, ra, rb);
   store_tiles(lds, tid, ra, rb);
   __syncthreads();
@@ -118,44 +130,43 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
     const bool more = t + 1 < steps;
     if (more) load_tiles<kGuard>(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, ra, rb);
     const float* as = cur;
-    const float* bs = cur + kBK * kPitch;
-    // Unrolling all 16 steps lets the scheduler hoist every LDS read and
-    // spill; four keeps 121 VGPRs (4 waves per SIMD).
-#pragma unroll 4
+    const float* bs = cur + kBK * kPitchA;
+#pragma unroll 2
     for (int k = 0; k < kBK; ++k) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4*>(as + k * kPitch + ty * 4);
-      const f32x4 a1 = *reinterpret_cast<const f32x4*>(as + k * kPitch + 64 + ty * 4);
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(bs + k * kPitch + tx * 4);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(bs + k * kPitch + 64 + tx * 4);
-      const float a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-      const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+      float a[RM], b[RN];
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int g = 0; g < kTMG; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(as + k * kPitchA + 64 * g + ty * 4);
+        a[4 * g] = v.x; a[4 * g + 1] = v.y; a[4 * g + 2] = v.z; a[4 * g + 3] = v.w;
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+      for (int g = 0; g < kTNG; ++g) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(bs + k * kPitchB + 64 * g + tx * 4);
+        b[4 * g] = v.x; b[4 * g + 1] = v.y; b[4 * g + 2] = v.z; b[4 * g + 3] = v.w;
+      }
+#pragma unroll
+      for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
     }
     if (more) store_tiles(nxt, tid, ra, rb);
     __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
+  for (int i = 0; i < RM; ++i) {
+    const int row = m0 + 64 * (i / 4) + ty * 4 + (i % 4);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < kTNG; ++h) {
       const int col = n0 + h * 64 + tx * 4;
       const f32x4 v = {acc[i][4 * h], acc[i][4 * h + 1], acc[i][4 * h + 2], acc[i][4 * h + 3]};
-      if (!kGuard) {
+      if (!kGuard || (row < M && col < N))
         *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * N + col) = v;
-      } else if (row < M && col < N) {
-        // N % 4 == 0, so a 4-wide column group is entirely in or out.
-        *reinterpret_cast<f32x4*>(C + static_cast<int64_t>(row) * N + col) = v;
-      }
     }
   }
 }
 
-__global__ __launch_bounds__(kThreads, 2) void valu_f32_kernel(
+__global__ __launch_bounds__(kThreads, 1) void valu_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B,
     float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
   __shared__ float lds[2 * kStage];

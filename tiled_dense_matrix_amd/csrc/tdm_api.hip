@@ -60,9 +60,7 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
 // Dispatcher: compare the product's intensity with the ridge point of the
 // unit that would run it (CS336 Lecture 5 GPU notes, §2.2). Below the ridge a
 // small-M bf16 product is memory-bound and goes to the streaming path; above
-// it the compute paths are used. A product too small to give the matrix-core
-// kernel's 256 x 256 tiles to most CUs goes to the 128 x 128 VALU kernel (fp32)
-// or the edge kernel.
+// it the compute paths are used.
 tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc) {
   if (M <= 0 || N <= 0 || K <= 0) return TDM_PATH_EDGE;
   const double flops = 2.0 * M * N * K;
@@ -76,10 +74,13 @@ tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, 
     if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc)) return TDM_PATH_MFMA;
     return TDM_PATH_EDGE;
   }
-  if (M * N <= 64 * 64) return TDM_PATH_EDGE;
-  const int64_t big_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  if (big_tiles >= 128 && supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc))
-    return TDM_PATH_MFMA;
+  // fp32 has no streaming path; the choice is about filling the CUs. With
+  // fewer than 16 tiles of 128 x 128 the 32 x 32 tiles of the edge kernel
+  // spread further. Otherwise the matrix cores, which outran the vector ALUs
+  // at every measured size; the VALU kernel takes what they cannot.
+  const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles128 < 16) return TDM_PATH_EDGE;
+  if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc)) return TDM_PATH_MFMA;
   if (supports(kind, TDM_PATH_VALU, M, N, K, ma, mb, mc)) return TDM_PATH_VALU;
   return TDM_PATH_EDGE;
 }

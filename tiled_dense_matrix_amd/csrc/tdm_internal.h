@@ -8,6 +8,23 @@
 
 namespace tdm {
 
+// Tile-size choice of the matrix-core kernels. A 256 x 256 tile moves half
+// the bytes per FLOP of a 128 x 128 tile, but one workgroup per CU holds it,
+// so a product with few of them leaves CUs idle in its last round. The large
+// tile is taken when its rounds over the 256 CUs are at least `min_fill`
+// full; below that the 128 x 128 tile (two per CU) balances better. The
+// thresholds were set from timings of both tile sizes on square and
+// rectangular products: the bandwidth-hungry bf16 kernel gains more from the
+// large tile than the fp32 kernel, which is bound by matrix-core issue.
+constexpr int kCUs = 256;
+constexpr double kLargeTileFillBf16 = 0.70;
+constexpr double kLargeTileFillF32 = 0.90;
+inline bool use_large_tiles(int64_t M, int64_t N, double min_fill) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t rounds = (tiles + kCUs - 1) / kCUs;
+  return static_cast<double>(tiles) >= min_fill * static_cast<double>(rounds * kCUs);
+}
+
 // --- shape requirements of each kernel family --------------------------
 // Sizes are already known to be >= 1 and each matrix < 2^31 elements.
 
