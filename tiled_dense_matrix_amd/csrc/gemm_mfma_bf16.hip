@@ -5,18 +5,24 @@
 // LLM course ch. 15 "GPU", §15.6 table of GEMM techniques):
 //   * one workgroup owns a BM x BN tile of C (256 x 256, or 128 x 128 when a
 //     product has too few large tiles to occupy the CUs) and walks K in steps
-//     of 64;
-//   * each step copies a BM x 64 slice of A and a 64 x BN slice of B from HBM
+//     of BK;
+//   * each step copies a BM x BK slice of A and a BK x BN slice of B from HBM
 //     into LDS with 16-byte row-contiguous loads that write LDS directly
 //     (global_load_lds), so the copy costs no registers and no LDS stores;
-//   * the four waves (2 x 2) each hold a (BM/2) x (BN/2) block of C in
-//     registers as 32 x 32 accumulators fed by v_mfma_f32_32x32x16_bf16;
-//   * LDS is double-buffered: the copy of step t+1 runs while the waves
-//     multiply step t; one barrier per step separates the two.
+//   * eight waves (2 x 4) each hold a (BM/2) x (BN/4) block of C in registers
+//     as 32 x 32 accumulators fed by v_mfma_f32_32x32x16_bf16; two waves per
+//     SIMD let one issue matrix instructions while the other waits;
+//   * LDS holds a ring of STAGES steps: the copy of step t+STAGES-1 is issued
+//     while the waves multiply step t, so a copy has STAGES-1 steps to land
+//     (data that misses the XCD's L2 comes from the last-level cache or HBM,
+//     whose latency one step does not cover); one barrier per step;
+//   * the fragments of the next sub-step are read while the current one is
+//     multiplied, across the step boundary too: the first reads of step t+1
+//     follow the barrier and overlap the last MFMAs of step t.
 //
 // Operand layouts. MFMA wants, in every lane, eight consecutive K values of
 // one row of A and of one column of B.
-//   A stays row-major in LDS, As[m][k] (128 bytes per row), and is read with
+//   A stays row-major in LDS, As[m][k] (2*BK bytes per row), and is read with
 //   16-byte loads. Chunk c (8 k values) of row m sits at chunk c ^ swz_a(m).
 //   B stays row-major too, Bs[k][n] (2*BN bytes per row), and is read with
 //   ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
@@ -27,7 +33,7 @@
 //
 // Partial tiles in M or N load clamped (in-bounds) rows/columns whose
 // products only reach outputs that are not stored. A K that is not a
-// multiple of 64 has its last step loaded through registers with the
+// multiple of BK has its last step loaded through registers with the
 // out-of-range elements set to zero.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -46,47 +52,74 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
-constexpr int kThreads = 256;
-constexpr int kBK = 64;
-constexpr int kRowA = kBK * 2;  // bytes per LDS row of A
-constexpr int kGroupM = 4;
+constexpr int kGroupM = 8;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
 // Tile geometry. Copies move 1 KB of LDS per wave instruction.
-template <int BM, int BN>
-struct Tile {
-  static constexpr int kBM = BM, kBN = BN;
-  static constexpr int kRowB = BN * 2;               // bytes per LDS row of B
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int kStages = STAGES_;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int kRowA = BK * 2;                // bytes per LDS row of A
+  static constexpr int kChunksA = BK / 8;             // 16-byte chunks per row of A
+  static constexpr int kRowB = BN * 2;                // bytes per LDS row of B
+  static constexpr int kChunksB = BN / 8;
   static constexpr int kStageA = BM * kRowA;
-  static constexpr int kStageB = kBK * kRowB;
+  static constexpr int kStageB = BK * kRowB;
   static constexpr int kStage = kStageA + kStageB;
-  static constexpr int kLdsBytes = 2 * kStage;       // double-buffered
-  static constexpr int kWaveM = BM / 2, kWaveN = BN / 2;
+  static constexpr int kLdsBytes = kStages * kStage;
+  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
-  static constexpr int kCopyA = kStageA / 1024 / 4;  // copies per wave
-  static constexpr int kCopyB = kStageB / 1024 / 4;
+  static constexpr int kCopyA = kStageA / 1024 / kWaves;  // copies per wave and step
+  static constexpr int kCopyB = kStageB / 1024 / kWaves;
+  static constexpr int kCopies = kCopyA + kCopyB;
+  static constexpr int kRowsPerCopyA = 1024 / kRowA;
   static constexpr int kRowsPerCopyB = 1024 / kRowB;
-  static constexpr int kLanesPerRowB = kRowB / 16;
-  static constexpr int kReads = kFragM + 2 * kFragN;  // LDS reads per k16 sub-step
-  static constexpr int kMfmas = kFragM * kFragN;      // MFMAs per k16 sub-step
+  static constexpr int kSub = BK / 16;                // MFMA k-steps per K step
+  static constexpr int kReads = kFragM + 2 * kFragN;  // LDS reads per sub-step
+  static constexpr int kMfmas = kFragM * kFragN;      // MFMAs per sub-step
+  static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
+                "each wave copies whole 1 KB blocks");
+  static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
+                "masked copy: whole 16-byte chunks per lane");
+  static_assert(kChunksA == 4 || kChunksA == 8, "swizzle of A rows");
+  static_assert(kSub % 2 == 0, "fragment double buffer alternates per sub-step");
+  static_assert(kStages >= 2 && (kStages - 2) * kCopies <= 63, "vmcnt range");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-__device__ __forceinline__ int swz_a(int m) { return (m ^ (m >> 3)) & 7; }
+// Row m of A, chunk c (8 k values) is stored at chunk c ^ swz_a(m): the rows
+// one 16-byte read instruction touches then cover every bank once.
+template <int kChunks>
+__device__ __forceinline__ int swz_a(int m) {
+  if constexpr (kChunks == 8)
+    return (m ^ (m >> 3)) & 7;
+  else
+    return ((m >> 1) ^ (m >> 3)) & 3;
+}
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
 
 // One 16-byte-per-lane global -> LDS copy from sbase + voff: lane l's 16
 // bytes land at lds_addr + 16*l. Issued as inline assembly so that the
 // compiler does not treat it as an LDS write of unknown address and stall
-// every later LDS read on it; completion is awaited explicitly
-// (wait_copies) before the barrier that publishes the buffer. M0 carries the
-// LDS address; nothing else in these kernels uses M0.
+// every later LDS read on it; completion is awaited explicitly (wait_vm)
+// before the barrier that publishes the buffer. M0 carries the LDS address;
+// nothing else in these kernels uses M0.
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
   asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                :
                : "v"(voff), "s"(sbase), "s"(lds_addr)
                : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight
+// (they complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
@@ -106,16 +139,16 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
                                                  int lane) {
   CopyPlan<T> p;
 #pragma unroll
-  for (int j = 0; j < T::kCopyA; ++j) {  // A: blocks of 8 rows
-    const int row = (wave * T::kCopyA + j) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ swz_a(row);
+  for (int j = 0; j < T::kCopyA; ++j) {  // A: blocks of kRowsPerCopyA rows
+    const int row = (wave * T::kCopyA + j) * T::kRowsPerCopyA + lane / T::kChunksA;
+    const int c = (lane % T::kChunksA) ^ swz_a<T::kChunksA>(row);
     const int gm = min(m0 + row, M - 1);
     p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(gm) * K + c * 8) * 2);
   }
 #pragma unroll
   for (int j = 0; j < T::kCopyB; ++j) {  // B: blocks of kRowsPerCopyB rows
-    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kLanesPerRowB;
-    const int c = (lane % T::kLanesPerRowB) ^ swz_b(row);
+    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kChunksB;
+    const int c = (lane % T::kChunksB) ^ swz_b(row);
     const int gn = min(n0 + c * 8, N - 8);
     p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + gn) * 2);
   }
@@ -145,20 +178,20 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
                                                  LDS_PTR(uint8_t) stage) {
   const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < T::kStageA / 16 / kThreads; ++i) {  // A chunks
-    const int id = tid + kThreads * i;
-    const int row = id >> 3, c = id & 7;
+  for (int i = 0; i < T::kStageA / 16 / T::kThreads; ++i) {  // A chunks
+    const int id = tid + T::kThreads * i;
+    const int row = id / T::kChunksA, c = id % T::kChunksA;
     const int gk = k0 + c * 8;
     const int gm = min(m0 + row, M - 1);
     u32x4 v = zero;
     if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-    *(LDS_PTR(u32x4))(stage + row * kRowA + ((c ^ swz_a(row)) << 4)) = v;
+    *(LDS_PTR(u32x4))(stage + row * T::kRowA + ((c ^ swz_a<T::kChunksA>(row)) << 4)) = v;
   }
   LDS_PTR(uint8_t) sb = stage + T::kStageA;
 #pragma unroll
-  for (int i = 0; i < T::kStageB / 16 / kThreads; ++i) {  // B chunks
-    const int id = tid + kThreads * i;
-    const int row = id / T::kLanesPerRowB, c = id % T::kLanesPerRowB;
+  for (int i = 0; i < T::kStageB / 16 / T::kThreads; ++i) {  // B chunks
+    const int id = tid + T::kThreads * i;
+    const int row = id / T::kChunksB, c = id % T::kChunksB;
     const int gk = k0 + row;
     const int gn = min(n0 + c * 8, N - 8);
     u32x4 v = zero;
@@ -167,12 +200,12 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
   }
 }
 
-__device__ __forceinline__ void wait_copies() {
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-__device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int chunk) {
-  const u32x4 v = *(LDS_PTR(const u32x4))(sa + row * kRowA + ((chunk ^ swz_a(row)) << 4));
+// Eight consecutive k (16s + 8*(lane/32) + 0..7) of row `row` of A.
+template <class T>
+__device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int s, int lg) {
+  const int chunk = 2 * s + lg;
+  const u32x4 v = *(LDS_PTR(const u32x4))(sa + row * T::kRowA +
+                                           ((chunk ^ swz_a<T::kChunksA>(row)) << 4));
   return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -194,23 +227,39 @@ __device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, 
   return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
+// Instruction order for the scheduler within one sub-step: one read of the
+// next fragments after each MFMA, leftovers after.
+template <class T>
+__device__ __forceinline__ void interleave_hint() {
+  constexpr int kPairs = T::kReads < T::kMfmas ? T::kReads : T::kMfmas;
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  if (T::kMfmas > kPairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas - kPairs, 0);
+  if (T::kReads > kPairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads - kPairs, 0);
+}
+
+template <class T>
+__global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
     float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
-  using T = Tile<BM, BN>;
+  constexpr int S = T::kStages;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
 
   int tm, tn;
   xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::WN, wn = wave % T::WN;
   const int lr = lane & 31, lg = lane >> 5;
+  const int row_a = wm * T::kWaveM + lr;  // + 32 i: this lane's rows of A
+  const int col_b = wn * T::kWaveN;       // + 32 j: this wave's columns of B
 
   f32x16 acc[T::kFragM][T::kFragN];
 #pragma unroll
@@ -220,79 +269,81 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int steps = (K + kBK - 1) / kBK;
-  const int full_steps = K / kBK;  // steps whose 64 k are all in range
+  const int steps = (K + T::BK - 1) / T::BK;
+  const int full_steps = K / T::BK;  // steps whose BK k are all in range
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
 
-  if (full_steps > 0)
-    copy_step_dma<T>(A, B, N, 0, wave, plan, lds0);
-  else
-    copy_step_masked<T>(A, B, M, N, K, m0, n0, 0, tid, lds);
-  wait_copies();
+  // Copy K step `st` into ring slot `slot`: asynchronously when all its k are
+  // in range, else through registers.
+  auto issue = [&](int st, int slot) {
+    if (st < full_steps)
+      copy_step_dma<T>(A, B, N, st * T::BK, wave, plan, lds0 + slot * T::kStage);
+    else if (st < steps)
+      copy_step_masked<T>(A, B, M, N, K, m0, n0, st * T::BK, tid, lds + slot * T::kStage);
+  };
+  // Before reading step `next`: its copies, and all earlier ones, have landed.
+  // The S-2 later steps may still be in flight when all of them are
+  // asynchronous copies.
+  auto wait_step = [&](int next) {
+    if (S > 2 && next + S - 2 < full_steps)
+      wait_vm<(S > 2 ? (S - 2) * T::kCopies : 0)>();
+    else
+      wait_vm<0>();
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st);
+  wait_step(0);
   __syncthreads();
 
+  bf16x8 a[2][T::kFragM], b[2][T::kFragN];
+#pragma unroll
+  for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lg);
+#pragma unroll
+  for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(lds + T::kStageA, col_b + 32 * j, 0, lane);
+
+  int cur = 0;  // ring slot of step t
   for (int t = 0; t < steps; ++t) {
-    const int cur = t & 1;
+    const int nxt = cur + 1 == S ? 0 : cur + 1;
+    issue(t + S - 1, cur == 0 ? S - 1 : cur - 1);  // the slot step t-1 used
     LDS_PTR(const uint8_t) sa = lds + cur * T::kStage;
     LDS_PTR(const uint8_t) sb = sa + T::kStageA;
-    LDS_PTR(uint8_t) nxt = lds + (cur ^ 1) * T::kStage;
-
-    if (t + 1 < full_steps)
-      copy_step_dma<T>(A, B, N, (t + 1) * kBK, wave, plan, lds0 + (cur ^ 1) * T::kStage);
-
-    bf16x8 a[2][T::kFragM], b[2][T::kFragN];
 #pragma unroll
-    for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a(sa, wm * T::kWaveM + i * 32 + lr, lg);
-#pragma unroll
-    for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(sb, wn * T::kWaveN + j * 32, 0, lane);
-#pragma unroll
-    for (int s = 0; s < kBK / 16; ++s) {
+    for (int s = 0; s < T::kSub; ++s) {
       const int c = s & 1, n = c ^ 1;
-      if (s + 1 < kBK / 16) {
+      if (s + 1 < T::kSub) {
 #pragma unroll
-        for (int i = 0; i < T::kFragM; ++i)
-          a[n][i] = read_a(sa, wm * T::kWaveM + i * 32 + lr, 2 * (s + 1) + lg);
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, s + 1, lg);
+#pragma unroll
+        for (int j = 0; j < T::kFragN; ++j) b[n][j] = read_b<T>(sb, col_b + 32 * j, s + 1, lane);
+      } else {
+        // Step t+1's copies land and every wave is done with the slot the
+        // next issue overwrites; then its first fragments are read while the
+        // last MFMAs of step t run. After the last step these reads fetch
+        // stale values that are never used.
+        wait_step(t + 1);
+        __syncthreads();
+        LDS_PTR(const uint8_t) na = lds + nxt * T::kStage;
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lg);
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j)
-          b[n][j] = read_b<T>(sb, wn * T::kWaveN + j * 32, s + 1, lane);
+          b[n][j] = read_b<T>(na + T::kStageA, col_b + 32 * j, 0, lane);
       }
 #pragma unroll
       for (int i = 0; i < T::kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      interleave_hint<T>();
     }
-    // Instruction order for the scheduler: the reads of sub-step 0, then for
-    // each later sub-step one of its reads after each MFMA of the previous
-    // sub-step (leftover reads or MFMAs follow), then the last sub-step.
-    constexpr int kPairs = T::kReads < T::kMfmas ? T::kReads : T::kMfmas;
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads, 0);
-#pragma unroll
-    for (int s = 0; s + 1 < kBK / 16; ++s) {
-#pragma unroll
-      for (int r = 0; r < kPairs; ++r) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-      if (T::kMfmas > kPairs)
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas - kPairs, 0);
-      if (T::kReads > kPairs)
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads - kPairs, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas, 0);
-
-    // A partial last K step is copied through registers (zeros beyond K).
-    if (t + 1 >= full_steps && t + 1 < steps)
-      copy_step_masked<T>(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, nxt);
-
-    wait_copies();
-    __syncthreads();
+    cur = nxt;
   }
 
   // Epilogue: element v of a 32 x 32 accumulator sits at
   // row 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
-  const bool full = (m0 + BM <= M) && (n0 + BN <= N);
+  const bool full = (m0 + T::BM <= M) && (n0 + T::BN <= N);
 #pragma unroll
   for (int i = 0; i < T::kFragM; ++i) {
 #pragma unroll
@@ -308,18 +359,17 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_bf16_kernel(
   }
 }
 
-template <int BM, int BN>
+template <class T>
 hipError_t launch_tile(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K,
                        hipStream_t s) {
-  using T = Tile<BM, BN>;
   // Opt in to more than 64 KB of dynamic LDS (done once per process).
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(mfma_bf16_kernel<BM, BN>),
+      reinterpret_cast<const void*>(mfma_bf16_kernel<T>),
       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
   if (attr != hipSuccess) return attr;
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((mfma_bf16_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(kThreads),
+  const int tiles_m = (M + T::BM - 1) / T::BM;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  hipLaunchKernelGGL((mfma_bf16_kernel<T>), dim3(tiles_m * tiles_n), dim3(T::kThreads),
                      T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -335,11 +385,14 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
          mis_b == 0;
 }
 
+using LargeTile = Cfg<256, 256, 2, 4, 32, 5>;
+using SmallTile = Cfg<128, 128, 2, 4, 32, 4>;
+
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
   if (use_large_tiles(M, N, kLargeTileFillBf16))
-    return launch_tile<256, 256>(A, B, C, M, N, K, s);
-  return launch_tile<128, 128>(A, B, C, M, N, K, s);
+    return launch_tile<LargeTile>(A, B, C, M, N, K, s);
+  return launch_tile<SmallTile>(A, B, C, M, N, K, s);
 }
 
 }  // namespace tdm
