@@ -11,22 +11,27 @@
 // pieces) by a slice of K, sized so that about 512 workgroups run (two per
 // CU):
 //   * a workgroup of 4 waves owns one block. Per step of 32 rows each wave
-//     copies 8 rows straight into an LDS ring of kStages stages
-//     (global_load_lds, 1 KB per instruction, no registers), kStages-1 steps
-//     ahead of the arithmetic;
+//     copies 8 rows of B and 4 rows of the matching 32 columns of A straight
+//     into an LDS ring of kStages stages (global_load_lds, no registers),
+//     kStages-1 steps ahead of the arithmetic. Nothing else in the loop
+//     touches global memory, so the only waits are for copies that are
+//     kStages-2 steps old;
 //   * each wave then reads its 64 columns back with ds_read_b64_tr_b16,
 //     which hands every lane four consecutive k of one column (the operand
 //     layout of v_mfma_f32_16x16x32_bf16), and runs four MFMAs against the
-//     rows of A (zero beyond M; A is tiny and read from L2);
+//     staged rows of A;
 //   * the workgroups of one column block each produce a partial 16 x 256
 //     sum and write it to a workspace; a second, small kernel adds the
 //     partials of each output in slice order and writes C, so the result is
-//     bitwise reproducible. (Combining them inside the first kernel would
-//     need device-scope fences, which write back and invalidate whole L2
-//     caches on this chip and cost far more than a second launch.) With a
-//     single slice the partial goes straight to C.
+//     bitwise reproducible. (Combining them inside the first kernel needs
+//     device-coherent stores, an arrival counter and device-coherent loads
+//     by the last workgroup; those round trips sit on the critical path and
+//     measured several times slower than a second launch.) With a single
+//     slice the partial goes straight to C.
 // A K that is not a multiple of 32 has its last step loaded through
-// registers with the rows beyond K set to zero.
+// registers with every k beyond K set to zero. Rows of A at or beyond M
+// are copied from row M-1; their products reach only rows of C that are not
+// stored.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -47,26 +52,30 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kBlockN = 256;                     // columns per workgroup
-constexpr int kRowBytes = kBlockN * 2;           // 512
-constexpr int kStepK = 32;                       // K rows per step
-constexpr int kStageBytes = kStepK * kRowBytes;  // 16 KB
-constexpr int kStages = 4;                       // LDS ring: 64 KB, two workgroups per CU
-constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kBlockN = 256;                        // columns per workgroup
+constexpr int kRowBytes = kBlockN * 2;              // 512
+constexpr int kStepK = 32;                          // K rows per step
 constexpr int kMaxM = 16;
-constexpr int kTargetGroups = 512;               // two per CU
-constexpr int kCopiesPerWave = 16 / kWaves;      // 1-KB copies per wave per step
+constexpr int kStageB = kStepK * kRowBytes;         // 16 KB of B
+constexpr int kRowA = kStepK * 2;                   // 64 bytes of one row of A
+constexpr int kStageBytes = kStageB + kMaxM * kRowA;  // + 1 KB of A
+constexpr int kStages = 4;                          // LDS ring: 68 KB, two workgroups per CU
+constexpr int kLdsBytes = kStages * kStageBytes;
+constexpr int kTargetGroups = 512;                  // two per CU
+constexpr int kCopiesB = 16 / kWaves;               // 1-KB copies of B per wave per step
+constexpr int kCopies = kCopiesB + 1;               // + one 256-byte copy of A
+constexpr int kPer = kMaxM * kBlockN;               // floats per partial block
 
 // Chunk swizzle of the staged rows: the four rows and two chunks that one
 // 16-lane group of a transposed read touches land on distinct banks.
 __device__ __forceinline__ int swz(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
-  // global -> LDS, 16 bytes per lane, lane l at lds_addr + 16*l, marked
-  // non-temporal (B is read once and should not displace A in L2). Inline
-  // assembly keeps the compiler from stalling later LDS reads on it; the
-  // wait is explicit (wait_copies_upto) before the barrier that publishes
-  // the stage. M0 carries the LDS address; nothing else here uses M0.
+  // global -> LDS, 16 bytes per active lane, lane l at lds_addr + 16*l,
+  // marked non-temporal (streamed once). Inline assembly keeps the compiler
+  // from stalling later LDS reads on it; the wait is explicit
+  // (wait_copies_upto) before the barrier that publishes the stage. M0
+  // carries the LDS address; nothing else here uses M0.
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt"
                :
                : "v"(gptr), "s"(lds_addr)
@@ -82,34 +91,49 @@ __device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Copy step rows [k0, k0+32) x columns [n0, n0+256) into a stage. Wave w
-// copies rows 8w..8w+7, two rows per instruction; columns past N are
-// clamped (their sums are never stored).
-__device__ __forceinline__ void copy_step(const uint16_t* __restrict__ B, int N, int k0,
-                                          int n0, int wave, int lane, uint32_t stage) {
+// Copy step rows [k0, k0+32) x columns [n0, n0+256) of B and rows 0..15 x
+// columns [k0, k0+32) of A into a stage. Wave w copies rows 8w..8w+7 of B,
+// two rows per instruction, and rows 4w..4w+3 of A with its first 16 lanes.
+// Columns of B past N and rows of A past M are clamped.
+__device__ __forceinline__ void copy_step(const uint16_t* __restrict__ A,
+                                          const uint16_t* __restrict__ B, int M, int N, int K,
+                                          int k0, int n0, int wave, int lane, uint32_t stage) {
 #pragma unroll
-  for (int j = 0; j < kCopiesPerWave; ++j) {
-    const int row = (wave * kCopiesPerWave + j) * 2 + (lane >> 5);
+  for (int j = 0; j < kCopiesB; ++j) {
+    const int row = (wave * kCopiesB + j) * 2 + (lane >> 5);
     const int c = (lane & 31) ^ swz(row);
     const int gn = min(n0 + c * 8, N - 8);
     dma16(B + static_cast<int64_t>(k0 + row) * N + gn,
-          stage + (wave * kCopiesPerWave + j) * 1024);
+          stage + (wave * kCopiesB + j) * 1024);
+  }
+  if (lane < 16) {
+    const int m = min(wave * 4 + (lane >> 2), M - 1);
+    dma16(A + static_cast<int64_t>(m) * K + k0 + (lane & 3) * 8,
+          stage + kStageB + wave * 256);
   }
 }
 
-// The same, through registers, with rows at or beyond K set to zero.
-__device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ B, int N, int K,
-                                                 int k0, int n0, int tid,
+// The same, through registers, with every k at or beyond K set to zero.
+__device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
+                                                 const uint16_t* __restrict__ B, int M, int N,
+                                                 int K, int k0, int n0, int tid,
                                                  LDS_PTR(uint8_t) stage) {
+  const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < kStageBytes / 16 / kThreads; ++i) {
+  for (int i = 0; i < kStageB / 16 / kThreads; ++i) {
     const int id = tid + kThreads * i;
     const int row = id >> 5, c = id & 31;
     const int gk = k0 + row;
     const int gn = min(n0 + c * 8, N - 8);
-    u32x4 v = {0u, 0u, 0u, 0u};
+    u32x4 v = zero;
     if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
     *(LDS_PTR(u32x4))(stage + row * kRowBytes + ((c ^ swz(row)) << 4)) = v;
+  }
+  if (tid < kMaxM * 4) {  // A: 16 rows x 4 chunks of 8 k
+    const int m = min(tid >> 2, M - 1), gk = k0 + (tid & 3) * 8;
+    u32x4 v = zero;
+    if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m) * K + gk);
+    *(LDS_PTR(u32x4))(stage + kStageB + tid * 16) = v;
   }
 }
 
@@ -149,9 +173,9 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
     if (j >= nsteps) return;
     const int stage = j % kStages;
     if (st < full_steps)
-      copy_step(B, N, st * kStepK, n0, wave, lane, lds0 + stage * kStageBytes);
+      copy_step(A, B, M, N, K, st * kStepK, n0, wave, lane, lds0 + stage * kStageBytes);
     else
-      copy_step_masked(B, N, K, st * kStepK, n0, tid, lds + stage * kStageBytes);
+      copy_step_masked(A, B, M, N, K, st * kStepK, n0, tid, lds + stage * kStageBytes);
   };
 
 #pragma unroll
@@ -170,19 +194,16 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
     // (Only when all of those are copies; near a register-loaded tail step
     // wait for everything.)
     if (j + kStages - 2 < nsteps && s_begin + j + kStages - 2 < full_steps)
-      wait_copies_upto<kCopiesPerWave * (kStages - 2)>();
+      wait_copies_upto<kCopies * (kStages - 2)>();
     else
       wait_copies_upto<0>();
     __syncthreads();
     issue(j + kStages - 1);
 
-    const int k0 = (s_begin + j) * kStepK;
-    const int ka = k0 + 8 * g;
-    const bool a_ok = m < M && ka < K;
-    const u32x4 av = *reinterpret_cast<const u32x4*>(
-        A + static_cast<int64_t>(a_ok ? m : 0) * K + (a_ok ? ka : 0));
-    const bf16x8 a = __builtin_bit_cast(bf16x8, a_ok ? av : u32x4{0u, 0u, 0u, 0u});
     LDS_PTR(const uint8_t) stage = lds + (j % kStages) * kStageBytes;
+    // Lane (m, g) takes k = 8g..8g+7 of row m of A.
+    const bf16x8 a = __builtin_bit_cast(
+        bf16x8, *(LDS_PTR(const u32x4))(stage + kStageB + m * kRowA + g * 16));
 #pragma unroll
     for (int q = 0; q < 16 / kWaves; ++q) {
       const int nb = wave * (256 / kWaves) + q * 16;
@@ -220,7 +241,6 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partials,
                                                             float* __restrict__ C, int M, int N,
                                                             int slices) {
-  constexpr int kPer = kMaxM * kBlockN;  // floats per partial block
   constexpr int kGroups = kPer / 256;    // workgroups per column block
   const int block = blockIdx.x / kGroups;
   const int e = (blockIdx.x - block * kGroups) * 256 + threadIdx.x;
