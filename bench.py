@@ -3,10 +3,14 @@
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
 
-A step is one call of the library's C ABI (gemm_f32 / gemm_bf16_f32acc) on
-one set of synthetic inputs already resident in HBM: cost model and path
-choice on the host, then the tiled kernel (tile schedule, coalesced loads,
-LDS staging, pipelined K loop, MFMA/FMA accumulation, C write-back).
+A step is one call of the library's C ABI (tdm_gemm_f32_path /
+tdm_gemm_bf16_f32acc_path, which with the auto path are gemm_f32 /
+gemm_bf16_f32acc) on one set of synthetic inputs already resident in HBM:
+cost model and path choice on the host, then the tiled kernel (tile
+schedule, coalesced loads, LDS staging, pipelined K loop, MFMA/FMA
+accumulation, C write-back). The square fp32 4096 product runs on the
+vector-ALU kernel by default (--path mfma times the matrix-core kernel the
+auto path picks for it); every other workload runs on the auto path.
 Consecutive steps rotate over several copies of (A, B, C) whose total size
 exceeds the 256 MB last-level cache, so every step reads its operands from
 HBM.
@@ -53,6 +57,11 @@ KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launc
                ["skinny_bf16_kernel", "skinny_reduce_kernel"]),
 }
 DEFAULT_WORKLOAD = "f32_4096"
+# The path each workload is specified on when --path is not given: the square
+# fp32 4096 product is the register- and LDS-tiled vector-ALU kernel; the
+# others take the library's own choice (matrix cores, or the streaming path
+# for M = 16).
+DEFAULT_PATH = {"f32_4096": "valu"}
 ROTATE_BYTES = 640 << 20  # working set across rotated copies
 
 
@@ -62,7 +71,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--path", default="auto", help="force a path (edge/valu/mfma/skinny)")
+    ap.add_argument("--path", default=None,
+                    help="force a path (auto/edge/valu/mfma/skinny); default: the workload's "
+                         "specified path (valu for f32_4096), else auto")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -160,7 +171,8 @@ def main():
 
     w = inputs.WORKLOADS[args.workload]
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
-    path = tdm.Path[args.path.upper()]
+    pname_arg = args.path or DEFAULT_PATH.get(w.name, "auto")
+    path = tdm.Path[pname_arg.upper()]
     chosen = tdm.tdm_select_path(kind, w.M, w.N, w.K) if path == tdm.Path.AUTO else path
     pname = tdm.path_name(chosen)
     kernel, ksrc, kernels = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else pname]
@@ -234,7 +246,11 @@ def main():
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
                    "rotated_copies": rot,
                    "gbps_algorithmic": round(gbs, 1)},
+        # One launch of the dominant kernel is timed as one call; a path that
+        # launches a second kernel (the skinny path's reduction) is timed
+        # with it, and `scope` says so.
         "roofline": {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+                     "scope": "kernel" if len(kernels) == 1 else "call (" + " + ".join(kernels) + ")",
                      "frac": round(achieved / peak, 4),
                      "traffic": None if traffic is None else round(traffic),
                      "algorithmic_bytes": int(roof.bytes), "algorithmic_flops": int(roof.flops)},

@@ -92,13 +92,16 @@ struct Cfg {
 };
 
 // Row m of A, chunk c (8 k values) is stored at chunk c ^ swz_a(m): the rows
-// one 16-byte read instruction touches then cover every bank once.
+// one 16-byte read instruction touches then cover every bank once. With
+// 64-byte rows, four rows share a 256-byte bank window, so rows that differ
+// in bits 2-3 take different chunks (measured conflict-free with rocprof's
+// SQ_LDS_BANK_CONFLICT; a swizzle on bits 1 and 3 was not).
 template <int kChunks>
 __device__ __forceinline__ int swz_a(int m) {
   if constexpr (kChunks == 8)
     return (m ^ (m >> 3)) & 7;
   else
-    return ((m >> 1) ^ (m >> 3)) & 3;
+    return (m >> 2) & 3;
 }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
 

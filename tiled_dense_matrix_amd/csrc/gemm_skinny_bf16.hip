@@ -66,9 +66,15 @@ constexpr int kCopiesB = 16 / kWaves;               // 1-KB copies of B per wave
 constexpr int kCopies = kCopiesB + 1;               // + one 256-byte copy of A
 constexpr int kPer = kMaxM * kBlockN;               // floats per partial block
 
-// Chunk swizzle of the staged rows: the four rows and two chunks that one
-// 16-lane group of a transposed read touches land on distinct banks.
-__device__ __forceinline__ int swz(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
+// Chunk swizzle of the staged rows of B: the four rows and two chunks that
+// one 16-lane group of a transposed read touches land on distinct banks, and
+// the group reading rows k+8.. in the same cycle lands on the other half.
+__device__ __forceinline__ int swz(int k) {
+  return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1) ^ (((k >> 3) & 1) << 1);
+}
+// Chunk swizzle of the staged rows of A (64 bytes each, four per bank
+// window): the 16 rows one read touches spread over every bank.
+__device__ __forceinline__ int swz_a(int m) { return (m >> 2) & 3; }
 
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_addr) {
   // global -> LDS, 16 bytes per active lane, lane l at lds_addr + 16*l,
@@ -107,8 +113,9 @@ __device__ __forceinline__ void copy_step(const uint16_t* __restrict__ A,
           stage + (wave * kCopiesB + j) * 1024);
   }
   if (lane < 16) {
-    const int m = min(wave * 4 + (lane >> 2), M - 1);
-    dma16(A + static_cast<int64_t>(m) * K + k0 + (lane & 3) * 8,
+    const int r = wave * 4 + (lane >> 2);
+    const int m = min(r, M - 1);
+    dma16(A + static_cast<int64_t>(m) * K + k0 + ((lane & 3) ^ swz_a(r)) * 8,
           stage + kStageB + wave * 256);
   }
 }
@@ -130,7 +137,7 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
     *(LDS_PTR(u32x4))(stage + row * kRowBytes + ((c ^ swz(row)) << 4)) = v;
   }
   if (tid < kMaxM * 4) {  // A: 16 rows x 4 chunks of 8 k
-    const int m = min(tid >> 2, M - 1), gk = k0 + (tid & 3) * 8;
+    const int m = min(tid >> 2, M - 1), gk = k0 + ((tid & 3) ^ swz_a(tid >> 2)) * 8;
     u32x4 v = zero;
     if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(m) * K + gk);
     *(LDS_PTR(u32x4))(stage + kStageB + tid * 16) = v;
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
     LDS_PTR(const uint8_t) stage = lds + (j % kStages) * kStageBytes;
     // Lane (m, g) takes k = 8g..8g+7 of row m of A.
     const bf16x8 a = __builtin_bit_cast(
-        bf16x8, *(LDS_PTR(const u32x4))(stage + kStageB + m * kRowA + g * 16));
+        bf16x8, *(LDS_PTR(const u32x4))(stage + kStageB + m * kRowA + ((g ^ swz_a(m)) << 4)));
 #pragma unroll
     for (int q = 0; q < 16 / kWaves; ++q) {
       const int nb = wave * (256 / kWaves) + q * 16;
