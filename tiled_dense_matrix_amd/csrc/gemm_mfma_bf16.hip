@@ -388,7 +388,7 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
          mis_b == 0;
 }
 
-using LargeTile = Cfg<256, 256, 2, 4, 32, 5>;
+using LargeTile = Cfg<256, 256, 2, 4, 32, 4>;
 using SmallTile = Cfg<128, 128, 2, 4, 32, 4>;
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,

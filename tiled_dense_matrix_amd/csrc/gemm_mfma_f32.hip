@@ -4,10 +4,11 @@
 // tiles in shared memory, register blocking, double buffering), with fp32
 // operands: each 32 x 32 x 2 MFMA takes one A value and one B value per lane
 // and accumulates in fp32.
-//   * one workgroup of 4 waves (2 x 2) owns a BM x BN tile of C (256 x 256,
+//   * one workgroup of 8 waves (2 x 4) owns a BM x BN tile of C (256 x 256,
 //     or 128 x 128 when a product has too few large tiles to occupy the CUs)
-//     and walks K in steps of 32; each wave keeps a (BM/2) x (BN/2) block of C
-//     in registers;
+//     and walks K in steps of 32; each wave keeps a (BM/2) x (BN/4) block of C
+//     in registers, and two waves per SIMD let one issue matrix instructions
+//     while the other waits on LDS or the barrier;
 //   * each step's BM x 32 slice of A and 32 x BN slice of B are loaded with
 //     16-byte row-contiguous loads into registers one step ahead, then
 //     written to the other half of a double-buffered LDS tile;
@@ -32,18 +33,17 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 #define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kBK = 32;
-constexpr int kThreads = 256;
 constexpr int kGroupM = 4;
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 struct Tile {
-  static constexpr int kBM = BM, kBN = BN;
+  static constexpr int kBM = BM, kBN = BN, kWN = WN, kThreads = 64 * WM * WN;
   static constexpr int kPitchA = BM + 32;          // floats per LDS row: rows k and
   static constexpr int kPitchB = BN + 32;          // k+1 fall in different bank halves
   static constexpr int kArrayA = kBK * kPitchA;
   static constexpr int kStage = kArrayA + kBK * kPitchB;  // As then Bs
   static constexpr int kLdsBytes = 2 * kStage * 4;        // double-buffered
-  static constexpr int kWaveM = BM / 2, kWaveN = BN / 2;
+  static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
   static constexpr int kLoadsA = BM * kBK / 4 / kThreads;  // 16-byte loads per lane
   static constexpr int kLoadsB = BN * kBK / 4 / kThreads;
@@ -56,7 +56,7 @@ __device__ __forceinline__ void load_step(const float* __restrict__ A, const flo
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < T::kLoadsA; ++i) {
-    const int id = tid + kThreads * i;
+    const int id = tid + T::kThreads * i;
     int gm = m0 + (id >> 3);
     int gk = k0 + (id & 7) * 4;
     if (!kGuard) {
@@ -71,7 +71,7 @@ __device__ __forceinline__ void load_step(const float* __restrict__ A, const flo
   }
 #pragma unroll
   for (int i = 0; i < T::kLoadsB; ++i) {
-    const int id = tid + kThreads * i;
+    const int id = tid + T::kThreads * i;
     int gk = k0 + id / (T::kBN / 4);
     int gn = n0 + (id % (T::kBN / 4)) * 4;
     if (!kGuard) {
@@ -94,7 +94,7 @@ __device__ __forceinline__ void store_step(LDS_PTR(float) stage, int tid,
   LDS_PTR(float) bs = stage + T::kArrayA;
 #pragma unroll
   for (int i = 0; i < T::kLoadsA; ++i) {
-    const int id = tid + kThreads * i;
+    const int id = tid + T::kThreads * i;
     const int m = id >> 3, k = (id & 7) * 4;
     as[(k + 0) * T::kPitchA + m] = ra[i].x;
     as[(k + 1) * T::kPitchA + m] = ra[i].y;
@@ -103,7 +103,7 @@ __device__ __forceinline__ void store_step(LDS_PTR(float) stage, int tid,
   }
 #pragma unroll
   for (int i = 0; i < T::kLoadsB; ++i) {
-    const int id = tid + kThreads * i;
+    const int id = tid + T::kThreads * i;
     *(LDS_PTR(f32x4))(bs + (id / (T::kBN / 4)) * T::kPitchB + (id % (T::kBN / 4)) * 4) = rb[i];
   }
 }
@@ -115,7 +115,7 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
                                              LDS_PTR(float) lds) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / T::kWN, wn = wave % T::kWN;
   const int lr = lane & 31, lg = lane >> 5;
 
   f32x16 acc[T::kFragM][T::kFragN];
@@ -170,11 +170,11 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
     }
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads, 1) void mfma_f32_kernel(
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void mfma_f32_kernel(
     const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M,
     int N, int K, int tiles_m, int tiles_n) {
-  using T = Tile<BM, BN>;
+  using T = Tile<BM, BN, WM, WN>;
   extern __shared__ __attribute__((aligned(16))) float lds_raw[];
   LDS_PTR(float) lds = (LDS_PTR(float))lds_raw;
   int tm, tn;
@@ -187,17 +187,17 @@ __global__ __launch_bounds__(kThreads, 1) void mfma_f32_kernel(
     tile_product<T, true>(A, B, C, M, N, K, m0, n0, lds);
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const float* A, const float* B, float* C, int M, int N, int K,
                        hipStream_t s) {
-  using T = Tile<BM, BN>;
+  using T = Tile<BM, BN, WM, WN>;
   static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(mfma_f32_kernel<BM, BN>),
+      reinterpret_cast<const void*>(mfma_f32_kernel<BM, BN, WM, WN>),
       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
   if (attr != hipSuccess) return attr;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((mfma_f32_kernel<BM, BN>), dim3(tiles_m * tiles_n), dim3(kThreads),
+  hipLaunchKernelGGL((mfma_f32_kernel<BM, BN, WM, WN>), dim3(tiles_m * tiles_n), dim3(T::kThreads),
                      T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
   return hipGetLastError();
 }
@@ -213,8 +213,8 @@ bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b, in
 hipError_t launch_mfma_f32(const float* A, const float* B, float* C, int M, int N, int K,
                            hipStream_t s) {
   if (use_large_tiles(M, N, kLargeTileFillF32))
-    return launch_tile<256, 256>(A, B, C, M, N, K, s);
-  return launch_tile<128, 128>(A, B, C, M, N, K, s);
+    return launch_tile<256, 256, 2, 4>(A, B, C, M, N, K, s);
+  return launch_tile<128, 128, 2, 4>(A, B, C, M, N, K, s);
 }
 
 }  // namespace tdm
