@@ -9,8 +9,10 @@ gemm_bf16_f32acc) on one set of synthetic inputs already resident in HBM:
 cost model and path choice on the host, then the tiled kernel (tile
 schedule, coalesced loads, LDS staging, pipelined K loop, MFMA/FMA
 accumulation, C write-back). The square fp32 4096 product runs on the
-vector-ALU kernel by default (--path mfma times the matrix-core kernel the
-auto path picks for it); every other workload runs on the auto path.
+vector-ALU kernel by default; the matrix-core kernel that the auto path
+picks for it is then timed as well and reported under config.auto_path
+(--path mfma makes it the main measurement). Every other workload runs on
+the auto path.
 Consecutive steps rotate over several copies of (A, B, C) whose total size
 exceeds the 256 MB last-level cache, so every step reads its operands from
 HBM.
@@ -194,21 +196,25 @@ def main():
     fn = tdm.tdm_gemm_f32_path if w.kind == "f32" else tdm.tdm_gemm_bf16_f32acc_path
     stream = torch.cuda.current_stream()
 
-    def step(i):
-        a, b, c = sets[i % rot]
-        fn(a, b, c, path=path, stream=stream)
+    def timed(p) -> float:
+        """Average ms per call of path p over args.steps calls after args.warmup."""
+        def step(i):
+            a, b, c = sets[i % rot]
+            fn(a, b, c, path=p, stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(args.steps):
-        step(args.warmup + i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for i in range(args.steps):
+            step(args.warmup + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / args.steps
+
+    ms = timed(path)
 
     roof = tdm.gemm_roofline(kind, w.M, w.N, w.K)
     tflops = roof.flops / (ms * 1e-3) / 1e12
@@ -228,6 +234,18 @@ def main():
         for a, b, c in sets[1:]:
             assert torch.equal(c[:4], sets[0][2][:4]), "rotated copies disagree"
 
+    # When the workload is specified on another path than the one gemm_* would
+    # pick, time the library's own choice too (after the main measurement).
+    auto_choice = tdm.path_name(tdm.tdm_select_path(kind, w.M, w.N, w.K))
+    auto_info = None
+    if path != tdm.Path.AUTO and auto_choice != pname:
+        ms_auto = timed(tdm.Path.AUTO)
+        tf_auto = roof.flops / (ms_auto * 1e-3) / 1e12
+        peak_auto = PEAK["mfma_f32" if w.kind == "f32" else "mfma_bf16"] \
+            if auto_choice == "mfma" else PEAK["alu_f32"]
+        auto_info = {"path": auto_choice, "ms_per_call": round(ms_auto, 6),
+                     "tflops": round(tf_auto, 3), "roofline_frac": round(tf_auto / peak_auto, 4)}
+
     line = {
         "metric": "GEMM TFLOP/s and % of MFMA/VALU/HBM roofline per shape, 1x MI355X",
         "value": round(tflops, 3),
@@ -245,6 +263,7 @@ def main():
                    "inputs": f"seed {w.seed}, {w.dist}",
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
                    "rotated_copies": rot,
+                   "auto_path": auto_info,
                    "gbps_algorithmic": round(gbs, 1)},
         # One launch of the dominant kernel is timed as one call; a path that
         # launches a second kernel (the skinny path's reduction) is timed
