@@ -8,8 +8,9 @@
 //
 // HBM streams well only when neighbouring lanes, waves and workgroups read
 // long contiguous runs, so B is cut into blocks of 256 columns (512-byte row
-// pieces) by a slice of K, sized so that about 512 workgroups run (two per
-// CU):
+// pieces) by a slice of K, sized so that at most 256 workgroups run (one per
+// CU; fewer, longer slices measured faster than two per CU, and they halve
+// the partial sums):
 //   * a workgroup of 4 waves owns one block. Per step of 32 rows each wave
 //     copies 8 rows of B and 4 rows of the matching 32 columns of A straight
 //     into an LDS ring of kStages stages (global_load_lds, no registers),
@@ -59,11 +60,11 @@ constexpr int kMaxM = 16;
 constexpr int kStageB = kStepK * kRowBytes;         // 16 KB of B
 constexpr int kRowA = kStepK * 2;                   // 64 bytes of one row of A
 constexpr int kStageBytes = kStageB + kMaxM * kRowA;  // + 1 KB of A
-constexpr int kStages = 4;                          // LDS ring: 68 KB, two workgroups per CU
+constexpr int kStages = 4;                          // LDS ring: 68 KB
 constexpr int kLdsBytes = kStages * kStageBytes;
-constexpr int kTargetGroups = 512;                  // two per CU
+constexpr int kTargetGroups = 256;                  // one per CU
 constexpr int kCopiesB = 16 / kWaves;               // 1-KB copies of B per wave per step
-constexpr int kCopies = kCopiesB + 1;               // + one 256-byte copy of A
+constexpr int kCopies = kCopiesB + 1;               // + one partial-wave copy of A
 constexpr int kPer = kMaxM * kBlockN;               // floats per partial block
 
 // Chunk swizzle of the staged rows of B: the four rows and two chunks that
@@ -99,7 +100,7 @@ __device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
 
 // Copy step rows [k0, k0+32) x columns [n0, n0+256) of B and rows 0..15 x
 // columns [k0, k0+32) of A into a stage. Wave w copies rows 8w..8w+7 of B,
-// two rows per instruction, and rows 4w..4w+3 of A with its first 16 lanes.
+// two rows per instruction, and 16/kWaves rows of A with its first lanes.
 // Columns of B past N and rows of A past M are clamped.
 __device__ __forceinline__ void copy_step(const uint16_t* __restrict__ A,
                                           const uint16_t* __restrict__ B, int M, int N, int K,
@@ -112,11 +113,12 @@ __device__ __forceinline__ void copy_step(const uint16_t* __restrict__ A,
     dma16(B + static_cast<int64_t>(k0 + row) * N + gn,
           stage + (wave * kCopiesB + j) * 1024);
   }
-  if (lane < 16) {
-    const int r = wave * 4 + (lane >> 2);
+  constexpr int kRowsA = kMaxM / kWaves;  // rows of A per wave
+  if (lane < 4 * kRowsA) {
+    const int r = wave * kRowsA + (lane >> 2);
     const int m = min(r, M - 1);
     dma16(A + static_cast<int64_t>(m) * K + k0 + ((lane & 3) ^ swz_a(r)) * 8,
-          stage + kStageB + wave * 256);
+          stage + kStageB + wave * kRowsA * kRowA);
   }
 }
 
@@ -311,7 +313,7 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
   if (attr != hipSuccess) return attr;
   const int blocks = (N + kBlockN - 1) / kBlockN;
   const int steps = (K + kStepK - 1) / kStepK;
-  int slices = (kTargetGroups + blocks - 1) / blocks;
+  int slices = kTargetGroups / blocks;  // rounded down: no second round of workgroups
   if (slices > steps) slices = steps;
   if (slices < 1) slices = 1;
   const int slice_steps = (steps + slices - 1) / slices;
