@@ -60,7 +60,7 @@ constexpr int kMaxM = 16;
 constexpr int kStageB = kStepK * kRowBytes;         // 16 KB of B
 constexpr int kRowA = kStepK * 2;                   // 64 bytes of one row of A
 constexpr int kStageBytes = kStageB + kMaxM * kRowA;  // + 1 KB of A
-constexpr int kStages = 4;                          // LDS ring: 68 KB
+constexpr int kStages = 3;                          // LDS ring: 51 KB
 constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kTargetGroups = 256;                  // one per CU
 constexpr int kCopiesB = 16 / kWaves;               // 1-KB copies of B per wave per step
