@@ -63,7 +63,10 @@ constexpr int kStageBytes = kStageB + kMaxM * kRowA;  // + 1 KB of A
 constexpr int kStages = 3;                          // LDS ring: 51 KB
 constexpr int kLdsBytes = kStages * kStageBytes;
 constexpr int kTargetGroups = 256;                  // one per CU
-constexpr int kCopiesB = 16 / kWaves;               // 1-KB copies of B per wave per step
+constexpr int kCopiesB = kStepK * kRowBytes / 1024 / kWaves;  // 1-KB copies of B per wave per step
+constexpr int kLanesPerRow = kRowBytes / 16;        // lanes of one copy that cover a row
+constexpr int kColsPerWave = kBlockN / kWaves;
+constexpr int kAcc = kColsPerWave / 16;             // 16 x 16 accumulators per wave
 constexpr int kCopies = kCopiesB + 1;               // + one partial-wave copy of A
 constexpr int kPer = kMaxM * kBlockN;               // floats per partial block
 
@@ -98,7 +101,7 @@ __device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
 }
 
-// Copy step rows [k0, k0+32) x columns [n0, n0+256) of B and rows 0..15 x
+// Copy step rows [k0, k0+32) x columns [n0, n0+kBlockN) of B and rows 0..15 x
 // columns [k0, k0+32) of A into a stage. Wave w copies rows 8w..8w+7 of B,
 // two rows per instruction, and 16/kWaves rows of A with its first lanes.
 // Columns of B past N and rows of A past M are clamped.
@@ -107,8 +110,8 @@ __device__ __forceinline__ void copy_step(const uint16_t* __restrict__ A,
                                           int k0, int n0, int wave, int lane, uint32_t stage) {
 #pragma unroll
   for (int j = 0; j < kCopiesB; ++j) {
-    const int row = (wave * kCopiesB + j) * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ swz(row);
+    const int row = (wave * kCopiesB + j) * (64 / kLanesPerRow) + lane / kLanesPerRow;
+    const int c = (lane % kLanesPerRow) ^ swz(row);
     const int gn = min(n0 + c * 8, N - 8);
     dma16(B + static_cast<int64_t>(k0 + row) * N + gn,
           stage + (wave * kCopiesB + j) * 1024);
@@ -131,7 +134,7 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < kStageB / 16 / kThreads; ++i) {
     const int id = tid + kThreads * i;
-    const int row = id >> 5, c = id & 31;
+    const int row = id / kLanesPerRow, c = id % kLanesPerRow;
     const int gk = k0 + row;
     const int gn = min(n0 + c * 8, N - 8);
     u32x4 v = zero;
@@ -190,9 +193,9 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
 #pragma unroll
   for (int j = 0; j < kStages - 1; ++j) issue(j);
 
-  f32x4 acc[16 / kWaves];
+  f32x4 acc[kAcc];
 #pragma unroll
-  for (int q = 0; q < 16 / kWaves; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < kAcc; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int g = lane >> 4;
   const int m = lane & 15;
 
@@ -214,8 +217,8 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
     const bf16x8 a = __builtin_bit_cast(
         bf16x8, *(LDS_PTR(const u32x4))(stage + kStageB + m * kRowA + ((g ^ swz_a(m)) << 4)));
 #pragma unroll
-    for (int q = 0; q < 16 / kWaves; ++q) {
-      const int nb = wave * (256 / kWaves) + q * 16;
+    for (int q = 0; q < kAcc; ++q) {
+      const int nb = wave * kColsPerWave + q * 16;
       const s16x4 lo = read_tr(stage, 8 * g, nb, lane);
       const s16x4 hi = read_tr(stage, 8 * g + 4, nb, lane);
       const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
@@ -225,25 +228,26 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
     }
   }
 
-  // Element v of accumulator q: row 4*(lane/16) + v, column 64*wave + 16q + lane%16.
+  // Element v of accumulator q: row 4*(lane/16) + v, column
+  // kColsPerWave*wave + 16q + lane%16.
   if (slices == 1) {
 #pragma unroll
-    for (int q = 0; q < 16 / kWaves; ++q)
+    for (int q = 0; q < kAcc; ++q)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int row = 4 * g + v, col = n0 + wave * (256 / kWaves) + q * 16 + m;
+        const int row = 4 * g + v, col = n0 + wave * kColsPerWave + q * 16 + m;
         if (row < M && col < N) C[static_cast<int64_t>(row) * N + col] = acc[q][v];
       }
     return;
   }
 
-  // Partial sums: workspace[block][slice][16][256].
+  // Partial sums: workspace[block][slice][16][kBlockN].
   float* mine = partials + (static_cast<int64_t>(block) * slices + slice) * (kMaxM * kBlockN);
 #pragma unroll
-  for (int q = 0; q < 16 / kWaves; ++q)
+  for (int q = 0; q < kAcc; ++q)
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      mine[(4 * g + v) * kBlockN + wave * (256 / kWaves) + q * 16 + m] = acc[q][v];
+      mine[(4 * g + v) * kBlockN + wave * kColsPerWave + q * 16 + m] = acc[q][v];
 }
 
 // C[row][col] = sum over slices (in slice order) of the partials.
