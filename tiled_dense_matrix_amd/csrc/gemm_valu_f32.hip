@@ -3,16 +3,16 @@
 // Method (CS336 Lecture 5 GPU notes, §4.2: tiling, register blocking and a
 // double-buffered pipeline; §4.1: coalesced loads, then any access pattern
 // from shared memory):
-//   * one workgroup of 256 lanes owns a 128 x 256 tile of C and walks K in
-//     steps of 16;
-//   * each step the lanes copy a 128 x 16 slice of A and a 16 x 256 slice of
+//   * one workgroup of 512 lanes (8 waves, two per SIMD) owns a 256 x 256
+//     tile of C and walks K in steps of 32;
+//   * each step the lanes copy a 256 x 32 slice of A and a 32 x 256 slice of
 //     B from HBM with 16-byte row-contiguous loads; A is written to LDS
 //     transposed (As[k][m]) so that the inner loop reads both operands as
 //     16-byte vectors;
-//   * every lane keeps an 8 x 16 block of C in registers (rows 4*ty + 64*g,
+//   * every lane keeps an 8 x 16 block of C in registers (rows 4*ty + 128*g,
 //     columns 4*tx + 64*h, in groups of 4) and per k does 128 fused
 //     multiply-adds from six 16-byte LDS reads;
-//   * LDS is double-buffered with one barrier per step.
+//   * LDS is double-buffered (133 KB) with one barrier per step.
 // Each output is accumulated in fp32 with k ascending.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -25,13 +25,15 @@ namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-// Each lane owns 4*kTMG rows (groups of 4, 64 rows apart) by 4*kTNG columns
-// (groups of 4, 64 columns apart) of the tile: 8 x 16 = 128 accumulators.
+// Each lane owns 4*kTMG rows (groups of 4, kRowGroup = 128 rows apart) by
+// 4*kTNG columns (groups of 4, 64 columns apart) of the tile: 8 x 16 = 128
+// accumulators.
 constexpr int kTMG = 2, kTNG = 4;
-constexpr int kBM = 64 * kTMG;
+constexpr int kThreads = 512;
+constexpr int kRowGroup = 4 * (kThreads / 16);  // rows between a lane's row groups
+constexpr int kBM = kRowGroup * kTMG;
 constexpr int kBN = 64 * kTNG;
-constexpr int kBK = 16;
-constexpr int kThreads = 256;
+constexpr int kBK = 32;
 constexpr int kPitchA = kBM + 4;  // floats per LDS row (keeps 16-byte alignment)
 constexpr int kPitchB = kBN + 4;
 constexpr int kStage = kBK * (kPitchA + kPitchB);  // As then Bs, floats
@@ -136,7 +138,7 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
       float a[RM], b[RN];
 #pragma unroll
       for (int g = 0; g < kTMG; ++g) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(as + k * kPitchA + 64 * g + ty * 4);
+        const f32x4 v = *reinterpret_cast<const f32x4*>(as + k * kPitchA + kRowGroup * g + ty * 4);
         a[4 * g] = v.x; a[4 * g + 1] = v.y; a[4 * g + 2] = v.z; a[4 * g + 3] = v.w;
       }
 #pragma unroll
@@ -155,7 +157,7 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
 
 #pragma unroll
   for (int i = 0; i < RM; ++i) {
-    const int row = m0 + 64 * (i / 4) + ty * 4 + (i % 4);
+    const int row = m0 + kRowGroup * (i / 4) + ty * 4 + (i % 4);
 #pragma unroll
     for (int h = 0; h < kTNG; ++h) {
       const int col = n0 + h * 64 + tx * 4;
