@@ -27,7 +27,7 @@ def test_world_size_above_one_is_refused():
 
 
 def test_committed_default_bench_line_keeps_the_contract():
-    with open(os.path.join(ROOT, "profiles", "bench_default.f32_4096.json")) as fh:
+    with open(os.path.join(ROOT, "profiles", "bench.f32_4096.json")) as fh:
         line = json.loads(fh.read())
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
