@@ -92,9 +92,8 @@ hipError_t launch_edge(const T* A, const T* B, float* C, int M, int N, int K,
   const int tiles_n = (N + kT - 1) / kT;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(edge_kernel<T>, dim3(static_cast<unsigned>(tiles)),
-                     dim3(kThreads), 0, s, A, B, C, M, N, K, tiles_n);
-  return hipGetLastError();
+  return launch(edge_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, A, B,
+                C, M, N, K, tiles_n);
 }
 
 }  // namespace
@@ -103,9 +102,7 @@ hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s) {
   if (count <= 0) return hipSuccess;
   int64_t blocks = (count + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)),
-                     dim3(256), 0, s, C, count);
-  return hipGetLastError();
+  return launch(fill_zero_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, C, count);
 }
 
 hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,

@@ -365,16 +365,14 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
 template <class T>
 hipError_t launch_tile(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K,
                        hipStream_t s) {
-  // Opt in to more than 64 KB of dynamic LDS (done once per process).
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(mfma_bf16_kernel<T>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
-  if (attr != hipSuccess) return attr;
+  static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
+  hipError_t e =
+      allow_lds(lds_ok, reinterpret_cast<const void*>(mfma_bf16_kernel<T>), T::kLdsBytes);
+  if (e != hipSuccess) return e;
   const int tiles_m = (M + T::BM - 1) / T::BM;
   const int tiles_n = (N + T::BN - 1) / T::BN;
-  hipLaunchKernelGGL((mfma_bf16_kernel<T>), dim3(tiles_m * tiles_n), dim3(T::kThreads),
-                     T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch(mfma_bf16_kernel<T>, dim3(tiles_m * tiles_n), dim3(T::kThreads), T::kLdsBytes, s,
+                A, B, C, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace

@@ -191,15 +191,14 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const float* A, const float* B, float* C, int M, int N, int K,
                        hipStream_t s) {
   using T = Tile<BM, BN, WM, WN>;
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(mfma_f32_kernel<BM, BN, WM, WN>),
-      hipFuncAttributeMaxDynamicSharedMemorySize, T::kLdsBytes);
-  if (attr != hipSuccess) return attr;
+  static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
+  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(mfma_f32_kernel<BM, BN, WM, WN>),
+                           T::kLdsBytes);
+  if (e != hipSuccess) return e;
   const int tiles_m = (M + BM - 1) / BM;
   const int tiles_n = (N + BN - 1) / BN;
-  hipLaunchKernelGGL((mfma_f32_kernel<BM, BN, WM, WN>), dim3(tiles_m * tiles_n), dim3(T::kThreads),
-                     T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch(mfma_f32_kernel<BM, BN, WM, WN>, dim3(tiles_m * tiles_n), dim3(T::kThreads),
+                T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
 }
 
 }  // namespace

@@ -311,10 +311,9 @@ bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s) {
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(skinny_bf16_kernel),
-      hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (attr != hipSuccess) return attr;
+  static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
+  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(skinny_bf16_kernel), kLdsBytes);
+  if (e != hipSuccess) return e;
   const int blocks = (N + kBlockN - 1) / kBlockN;
   const int steps = (K + kStepK - 1) / kStepK;
   int slices = kTargetGroups / blocks;  // rounded down: no second round of workgroups
@@ -327,19 +326,14 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
     const size_t part_bytes =
         static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
     void* ws = nullptr;
-    hipError_t e = workspace(part_bytes, &ws);
-    if (e != hipSuccess) return e;
+    if ((e = workspace(part_bytes, &ws)) != hipSuccess) return e;
     partials = static_cast<float*>(ws);
   }
-  hipLaunchKernelGGL(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s,
-                     A, B, C, M, N, K, slices, slice_steps, partials);
-  if (slices > 1) {
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3(blocks * (kMaxM * kBlockN / 256)), dim3(256),
-                       0, s, partials, C, M, N, slices);
-  }
-  return hipGetLastError();
+  e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B, C, M,
+             N, K, slices, slice_steps, partials);
+  if (e != hipSuccess || slices == 1) return e;
+  return launch(skinny_reduce_kernel, dim3(blocks * (kPer / 256)), dim3(256), 0, s, partials,
+                C, M, N, slices);
 }
 
 }  // namespace tdm

@@ -195,9 +195,8 @@ hipError_t launch_valu_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s) {
   const int tiles_m = (M + kBM - 1) / kBM;
   const int tiles_n = (N + kBN - 1) / kBN;
-  hipLaunchKernelGGL(valu_f32_kernel, dim3(tiles_m * tiles_n), dim3(kThreads),
-                     0, s, A, B, C, M, N, K, tiles_m, tiles_n);
-  return hipGetLastError();
+  return launch(valu_f32_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), 0, s, A, B, C, M, N, K,
+                tiles_m, tiles_n);
 }
 
 }  // namespace tdm

@@ -1,12 +1,48 @@
 // Internal interface between the C ABI (tdm_api.hip) and the kernel files.
-// Every launcher enqueues on `stream` and returns hipGetLastError() after
-// the launch. Callers have validated sizes and pointers beforehand.
+// Every launcher enqueues on `stream` and returns the status of its own
+// launches (hipLaunchKernel's return value, not a sticky error left by some
+// earlier call). Callers have validated sizes and pointers beforehand.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <tuple>
+#include <utility>
+
 namespace tdm {
+
+// Launch `kernel` and return the launch's status. The arguments are
+// converted to the kernel's parameter types and passed by address.
+template <typename... P, typename Tuple, size_t... I>
+hipError_t launch_with(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                       Tuple& args, std::index_sequence<I...>) {
+  void* ptrs[] = {static_cast<void*>(&std::get<I>(args))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, lds, s);
+}
+
+template <typename... P, typename... A>
+hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, size_t lds, hipStream_t s,
+                  A... args) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> values(static_cast<P>(args)...);
+  return launch_with(kernel, grid, block, lds, s, values, std::index_sequence_for<P...>{});
+}
+
+// Allow `kernel` more than the default 64 KB of dynamic LDS on the current
+// device; done once per kernel and device (devices 0..63 are remembered;
+// beyond that the attribute is set on every call).
+inline hipError_t allow_lds(std::atomic<uint64_t>& done, const void* kernel, int bytes) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
 
 // Tile-size choice of the matrix-core kernels. A 256 x 256 tile moves half
 // the bytes per FLOP of a 128 x 128 tile, but one workgroup per CU holds it,
