@@ -36,12 +36,15 @@
  *   - a matrix with 2^31 or more elements, or a forced path that cannot run
  *     the given shape/alignment                         -> TDM_ERROR_NOT_SUPPORTED
  *   - no HIP device is visible                          -> TDM_ERROR_NO_DEVICE
- *   - the kernel launch failed                          -> TDM_ERROR_LAUNCH
+ *   - a HIP call failed (kernel launch, the small-M path's workspace
+ *     allocation or the kernels' LDS attribute)         -> TDM_ERROR_LAUNCH
  *   - M == 0 or N == 0: nothing to do, TDM_SUCCESS without any HIP call.
  *   - K == 0: C is filled with zeros (the empty sum), TDM_SUCCESS.
  *
- * Threading: the calls keep no mutable global state and may be made from
- * several host threads; work on one stream is ordered as usual.
+ * Threading: the calls may be made from several host threads; work on one
+ * stream is ordered as usual. The only mutable global state is the small-M
+ * workspace (guarded by a mutex; see above for calls in flight at the same
+ * time) and a per-device record of the kernels' LDS attribute.
  */
 #ifndef TDM_H
 #define TDM_H
