@@ -165,3 +165,18 @@ def test_path_supports():
     assert not tdm.tdm_path_supports(K.BF16_F32ACC, P.SKINNY, 17, 8192, 8192)
     assert tdm.tdm_path_supports(K.F32, P.EDGE, 3, 5, 7, 1, 3, 5)
     assert not tdm.tdm_path_supports(K.F32, 9, 3, 5, 7)
+
+
+def test_f32_mfma_copy_offset_limits():
+    """The fp32 matrix-core kernel's per-lane copy offsets are 32-bit: K below
+    2^22 (256 rows of A) and N below 2^25 (32 rows of B); beyond that the
+    dispatcher takes the vector-ALU kernel."""
+    K, P = tdm.Kind, tdm.Path
+    assert tdm.tdm_path_supports(K.F32, P.MFMA, 256, 256, (1 << 22) - 4)
+    assert not tdm.tdm_path_supports(K.F32, P.MFMA, 256, 256, 1 << 22)
+    assert tdm.tdm_path_supports(K.F32, P.MFMA, 32, (1 << 25) - 4, 32)
+    assert not tdm.tdm_path_supports(K.F32, P.MFMA, 32, 1 << 25, 32)
+    # Valid matrices (under 2^31 elements) with K >= 2^22 have fewer than 16
+    # tiles and go to the edge kernel anyway; a wide B can reach the limit.
+    assert tdm.tdm_select_path(K.F32, 32, 1 << 25, 32) == P.VALU
+    assert tdm.tdm_select_path(K.F32, 32, (1 << 25) - 4, 32) == P.MFMA

@@ -38,6 +38,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_copy.h"
 #include "tdm_internal.h"
 #include "tile_map.h"
 
@@ -49,8 +50,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
-
-#define LDS_PTR(T) __attribute__((address_space(3))) T*
 
 constexpr int kGroupM = 8;
 // Instruction classes of __builtin_amdgcn_sched_group_barrier.
@@ -104,30 +103,6 @@ __device__ __forceinline__ int swz_a(int m) {
     return (m >> 2) & 3;
 }
 __device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1); }
-
-// One 16-byte-per-lane global -> LDS copy from sbase + voff: lane l's 16
-// bytes land at lds_addr + 16*l. Issued as inline assembly so that the
-// compiler does not treat it as an LDS write of unknown address and stall
-// every later LDS read on it; completion is awaited explicitly (wait_vm)
-// before the barrier that publishes the buffer. M0 carries the LDS address;
-// nothing else in these kernels uses M0.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(sbase), "s"(lds_addr)
-               : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are in flight
-// (they complete in issue order).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_offset(LDS_PTR(const uint8_t) p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p));
-}
 
 // Per-lane byte offsets of this wave's copy instructions; the K step only
 // moves the scalar base pointers.

@@ -1,26 +1,40 @@
 // fp32 product on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
 //
-// The same tiling as the bf16 kernel (CS336 Lecture 5 GPU notes, §4.2:
-// tiles in shared memory, register blocking, double buffering), with fp32
-// operands: each 32 x 32 x 2 MFMA takes one A value and one B value per lane
-// and accumulates in fp32.
+// The tiling of the bf16 kernel (CS336 Lecture 5 GPU notes, §4.2: tiles in
+// shared memory, register blocking, a pipelined K loop), with fp32 operands:
 //   * one workgroup of 8 waves (2 x 4) owns a BM x BN tile of C (256 x 256,
 //     or 128 x 128 when a product has too few large tiles to occupy the CUs)
 //     and walks K in steps of 32; each wave keeps a (BM/2) x (BN/4) block of C
-//     in registers, and two waves per SIMD let one issue matrix instructions
-//     while the other waits on LDS or the barrier;
-//   * each step's BM x 32 slice of A and 32 x BN slice of B are loaded with
-//     16-byte row-contiguous loads into registers one step ahead, then
-//     written to the other half of a double-buffered LDS tile;
-//   * LDS holds A k-major (As[k][m]) and B as is (Bs[k][n]), so the MFMA
-//     operands -- lane l takes row/column l%32 at k = l/32 -- are two rows of
-//     32 consecutive floats, read without bank conflicts (the row pitch puts
-//     rows k and k+1 in different bank halves).
-// fp32 matrix throughput is an eighth of bf16, so per FLOP the tile needs
-// little bandwidth; the kernel is bound by MFMA issue.
+//     in registers as 32 x 32 accumulators, two waves per SIMD;
+//   * each step's BM x 32 slice of A and 32 x BN slice of B are copied from
+//     HBM straight into LDS (global_load_lds, 16 bytes per lane), with no
+//     registers and no LDS store instructions on the way; LDS holds a ring of
+//     STAGES steps and the copy of step t+STAGES-1 is issued while step t is
+//     multiplied; one barrier per step.
+//
+// Operand layouts. A 32 x 32 x 2 MFMA takes one A value (row l%32) and one B
+// value (column l%32) per lane l, at the MFMA's k index l/32. Which two
+// K values an MFMA covers is free, so each group of 8 consecutive k feeds
+// four MFMAs r = 0..3 that cover k = 8q + r (lanes 0-31) and 8q + 4 + r
+// (lanes 32-63). A lane then needs four consecutive k of its row of A: one
+// 16-byte LDS read.
+//   A stays row-major in LDS, As[m][k] (128 bytes per row). Chunk c (4 k) of
+//   row m sits at chunk c ^ swz_a(m), so the 16 rows a 16-lane read phase
+//   touches fill all 64 banks once.
+//   B stays row-major too, Bs[k][n]; a lane reads four single floats of its
+//   column. Chunk c of row k sits at chunk c ^ swz_b(k): the rows k and k+4
+//   that the two halves of a wave read at once land in opposite bank halves.
+// Each output is a sum over k in fp32; the order of the terms differs from a
+// plain k-ascending loop only by rounding.
+//
+// Partial tiles in M or N load clamped (in-bounds) rows/columns whose
+// products only reach outputs that are not stored. A K that is not a
+// multiple of 32 has its last step loaded through registers with the
+// out-of-range elements set to zero.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_copy.h"
 #include "tdm_internal.h"
 #include "tile_map.h"
 
@@ -30,93 +44,171 @@ namespace {
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-#define LDS_PTR(T) __attribute__((address_space(3))) T*
-
-constexpr int kBK = 32;
 constexpr int kGroupM = 4;
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
-template <int BM, int BN, int WM, int WN>
-struct Tile {
-  static constexpr int kBM = BM, kBN = BN, kWN = WN, kThreads = 64 * WM * WN;
-  static constexpr int kPitchA = BM + 32;          // floats per LDS row: rows k and
-  static constexpr int kPitchB = BN + 32;          // k+1 fall in different bank halves
-  static constexpr int kArrayA = kBK * kPitchA;
-  static constexpr int kStage = kArrayA + kBK * kPitchB;  // As then Bs
-  static constexpr int kLdsBytes = 2 * kStage * 4;        // double-buffered
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32;
+  static constexpr int kStages = STAGES_;
+  static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
+  static constexpr int kRowA = BK * 4;   // bytes per LDS row of A
+  static constexpr int kChunksA = BK / 4;
+  static constexpr int kRowB = BN * 4;   // bytes per LDS row of B
+  static constexpr int kChunksB = BN / 4;
+  static constexpr int kStageA = BM * kRowA;
+  static constexpr int kStageB = BK * kRowB;
+  static constexpr int kStage = kStageA + kStageB;
+  static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
-  static constexpr int kLoadsA = BM * kBK / 4 / kThreads;  // 16-byte loads per lane
-  static constexpr int kLoadsB = BN * kBK / 4 / kThreads;
+  static constexpr int kCopyA = kStageA / 1024 / kWaves;  // copies per wave and step
+  static constexpr int kCopyB = kStageB / 1024 / kWaves;
+  static constexpr int kCopies = kCopyA + kCopyB;
+  static constexpr int kRowsPerCopyA = 1024 / kRowA;
+  static constexpr int kRowsPerCopyB = 1024 / kRowB;
+  static constexpr int kGroups = BK / 8;                 // 8-k groups per step
+  static constexpr int kMfmas = 4 * kFragM * kFragN;     // MFMAs per group
+  static constexpr int kReads = kFragM + 4 * kFragN;     // LDS reads per group
+  static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
+                "each wave copies whole 1 KB blocks");
+  static_assert(kRowsPerCopyB >= 1 && BN % 64 == 0, "B rows of 256 or 512 bytes and more");
+  static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
+                "masked copy: whole 16-byte chunks per lane");
+  static_assert(kGroups % 2 == 0, "fragment double buffer alternates per group");
+  static_assert(kStages >= 2 && (kStages - 2) * kCopies <= 63, "vmcnt range");
+  static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-template <class T, bool kGuard>
-__device__ __forceinline__ void load_step(const float* __restrict__ A, const float* __restrict__ B,
-                                          int M, int N, int K, int m0, int n0, int k0, int tid,
-                                          f32x4 (&ra)[T::kLoadsA], f32x4 (&rb)[T::kLoadsB]) {
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+__device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
+__device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
+
+// Per-lane byte offsets of this wave's copies, relative to the tile's first
+// row of A (A + m0*K + k0) and to B + k0*N + n0.
+template <class T>
+struct CopyPlan {
+  uint32_t a[T::kCopyA];
+  uint32_t b[T::kCopyB];
+};
+
+template <class T>
+__device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, int n0, int wave,
+                                                 int lane) {
+  CopyPlan<T> p;
 #pragma unroll
-  for (int i = 0; i < T::kLoadsA; ++i) {
-    const int id = tid + T::kThreads * i;
-    int gm = m0 + (id >> 3);
-    int gk = k0 + (id & 7) * 4;
-    if (!kGuard) {
-      ra[i] = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-    } else {
-      const bool ok = gm < M && gk < K;
-      gm = gm < M ? gm : M - 1;
-      gk = gk < K ? gk : K - 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-      ra[i] = ok ? v : zero;
-    }
+  for (int j = 0; j < T::kCopyA; ++j) {
+    const int row = (wave * T::kCopyA + j) * T::kRowsPerCopyA + lane / T::kChunksA;
+    const int c = (lane % T::kChunksA) ^ swz_a(row);
+    const int dm = min(m0 + row, M - 1) - m0;
+    p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(dm) * K + c * 4) * 4);
   }
 #pragma unroll
-  for (int i = 0; i < T::kLoadsB; ++i) {
-    const int id = tid + T::kThreads * i;
-    int gk = k0 + id / (T::kBN / 4);
-    int gn = n0 + (id % (T::kBN / 4)) * 4;
-    if (!kGuard) {
-      rb[i] = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    } else {
-      const bool ok = gk < K && gn < N;
-      gk = gk < K ? gk : K - 1;
-      gn = gn < N ? gn : N - 4;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-      rb[i] = ok ? v : zero;
-    }
+  for (int j = 0; j < T::kCopyB; ++j) {
+    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kChunksB;
+    const int c = (lane % T::kChunksB) ^ swz_b(row);
+    const int dn = min(n0 + c * 4, N - 4) - n0;
+    p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + dn) * 4);
   }
+  return p;
 }
 
 template <class T>
-__device__ __forceinline__ void store_step(LDS_PTR(float) stage, int tid,
-                                           const f32x4 (&ra)[T::kLoadsA],
-                                           const f32x4 (&rb)[T::kLoadsB]) {
-  LDS_PTR(float) as = stage;
-  LDS_PTR(float) bs = stage + T::kArrayA;
+__device__ __forceinline__ void copy_step_dma(const float* a_tile, const float* b_tile, int N,
+                                              int k0, int wave, const CopyPlan<T>& p,
+                                              uint32_t stage) {
+  const float* a_base = a_tile + k0;
+  const float* b_base = b_tile + static_cast<int64_t>(k0) * N;
 #pragma unroll
-  for (int i = 0; i < T::kLoadsA; ++i) {
+  for (int j = 0; j < T::kCopyA; ++j)
+    dma16(a_base, p.a[j], stage + (wave * T::kCopyA + j) * 1024);
+#pragma unroll
+  for (int j = 0; j < T::kCopyB; ++j)
+    dma16(b_base, p.b[j], stage + T::kStageA + (wave * T::kCopyB + j) * 1024);
+}
+
+// Same layout, through registers, with zeros beyond K (the partial last step).
+template <class T>
+__device__ __forceinline__ void copy_step_masked(const float* __restrict__ A,
+                                                 const float* __restrict__ B, int M, int N, int K,
+                                                 int m0, int n0, int k0, int tid,
+                                                 LDS_PTR(uint8_t) stage) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < T::kStageA / 16 / T::kThreads; ++i) {
     const int id = tid + T::kThreads * i;
-    const int m = id >> 3, k = (id & 7) * 4;
-    as[(k + 0) * T::kPitchA + m] = ra[i].x;
-    as[(k + 1) * T::kPitchA + m] = ra[i].y;
-    as[(k + 2) * T::kPitchA + m] = ra[i].z;
-    as[(k + 3) * T::kPitchA + m] = ra[i].w;
+    const int row = id / T::kChunksA, c = id % T::kChunksA;
+    const int gk = k0 + c * 4;
+    const int gm = min(m0 + row, M - 1);
+    f32x4 v = zero;
+    if (gk < K) v = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
+    *(LDS_PTR(f32x4))(stage + row * T::kRowA + ((c ^ swz_a(row)) << 4)) = v;
   }
+  LDS_PTR(uint8_t) sb = stage + T::kStageA;
 #pragma unroll
-  for (int i = 0; i < T::kLoadsB; ++i) {
+  for (int i = 0; i < T::kStageB / 16 / T::kThreads; ++i) {
     const int id = tid + T::kThreads * i;
-    *(LDS_PTR(f32x4))(bs + (id / (T::kBN / 4)) * T::kPitchB + (id % (T::kBN / 4)) * 4) = rb[i];
+    const int row = id / T::kChunksB, c = id % T::kChunksB;
+    const int gk = k0 + row;
+    const int gn = min(n0 + c * 4, N - 4);
+    f32x4 v = zero;
+    if (gk < K) v = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+    *(LDS_PTR(f32x4))(sb + row * T::kRowB + ((c ^ swz_b(row)) << 4)) = v;
   }
 }
 
-template <class T, bool kGuard>
-__device__ __forceinline__ void tile_product(const float* __restrict__ A,
-                                             const float* __restrict__ B, float* __restrict__ C,
-                                             int M, int N, int K, int m0, int n0,
-                                             LDS_PTR(float) lds) {
+// k = 8q + 4*(lane/32) + 0..3 of row `row` of A.
+template <class T>
+__device__ __forceinline__ f32x4 read_a(LDS_PTR(const uint8_t) sa, int row, int q, int lg) {
+  const int chunk = 2 * q + lg;
+  return *(LDS_PTR(const f32x4))(sa + row * T::kRowA + ((chunk ^ swz_a(row)) << 4));
+}
+
+// Rows k = 8q + 4*(lane/32) + 0..3 of column `col` of B.
+template <class T>
+__device__ __forceinline__ f32x4 read_b(LDS_PTR(const uint8_t) sb, int col, int q, int lg) {
+  const int k = 8 * q + 4 * lg;
+  LDS_PTR(const uint8_t) p = sb + (((col >> 2) ^ swz_b(k)) << 4) + ((col & 3) << 2);
+  f32x4 v;
+  v.x = *(LDS_PTR(const float))(p + (k + 0) * T::kRowB);
+  v.y = *(LDS_PTR(const float))(p + (k + 1) * T::kRowB);
+  v.z = *(LDS_PTR(const float))(p + (k + 2) * T::kRowB);
+  v.w = *(LDS_PTR(const float))(p + (k + 3) * T::kRowB);
+  return v;
+}
+
+// One read of the next group's operands after each MFMA, leftovers after.
+template <class T>
+__device__ __forceinline__ void interleave_hint() {
+  constexpr int kPairs = T::kReads < T::kMfmas ? T::kReads : T::kMfmas;
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+  }
+  if (T::kMfmas > kPairs) __builtin_amdgcn_sched_group_barrier(kSchedMfma, T::kMfmas - kPairs, 0);
+  if (T::kReads > kPairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads - kPairs, 0);
+}
+
+template <class T>
+__global__ __launch_bounds__(T::kThreads, 1) void mfma_f32_kernel(
+    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N,
+    int K, int tiles_m, int tiles_n) {
+  constexpr int S = T::kStages;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
+
+  int tm, tn;
+  xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
+  const int m0 = tm * T::BM, n0 = tn * T::BN;
+
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int wm = wave / T::kWN, wn = wave % T::kWN;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int wm = wave / T::WN, wn = wave % T::WN;
   const int lr = lane & 31, lg = lane >> 5;
+  const int row_a = wm * T::kWaveM + lr;  // + 32 i: this lane's rows of A
+  const int col_b = wn * T::kWaveN + lr;  // + 32 j: this lane's columns of B
 
   f32x16 acc[T::kFragM][T::kFragN];
 #pragma unroll
@@ -126,94 +218,125 @@ __device__ __forceinline__ void tile_product(const float* __restrict__ A,
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int steps = (K + kBK - 1) / kBK;
-  f32x4 ra[T::kLoadsA], rb[T::kLoadsB];
-  load_step<T, kGuard>(A, B, M, N, K, m0, n0, 0, tid, ra, rb);
-  store_step<T>(lds, tid, ra, rb);
+  const int steps = (K + T::BK - 1) / T::BK;
+  const int full_steps = K / T::BK;
+  const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
+  const float* a_tile = A + static_cast<int64_t>(m0) * K;
+  const float* b_tile = B + n0;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+
+  auto issue = [&](int st, int slot) {
+    if (st < full_steps)
+      copy_step_dma<T>(a_tile, b_tile, N, st * T::BK, wave, plan, lds0 + slot * T::kStage);
+    else if (st < steps)
+      copy_step_masked<T>(A, B, M, N, K, m0, n0, st * T::BK, tid, lds + slot * T::kStage);
+  };
+  auto wait_step = [&](int next) {
+    if (S > 2 && next + S - 2 < full_steps)
+      wait_vm<(S > 2 ? (S - 2) * T::kCopies : 0)>();
+    else
+      wait_vm<0>();
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st);
+  wait_step(0);
   __syncthreads();
 
+  f32x4 a[2][T::kFragM], b[2][T::kFragN];
+#pragma unroll
+  for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lg);
+#pragma unroll
+  for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(lds + T::kStageA, col_b + 32 * j, 0, lg);
+
+  int cur = 0;
   for (int t = 0; t < steps; ++t) {
-    LDS_PTR(const float) as = lds + (t & 1) * T::kStage;
-    LDS_PTR(const float) bs = as + T::kArrayA;
-    const bool more = t + 1 < steps;
-    if (more) load_step<T, kGuard>(A, B, M, N, K, m0, n0, (t + 1) * kBK, tid, ra, rb);
-#pragma unroll 4
-    for (int kp = 0; kp < kBK / 2; ++kp) {
-      const int k = 2 * kp + lg;
-      float a[T::kFragM], b[T::kFragN];
+    const int nxt = cur + 1 == S ? 0 : cur + 1;
+    issue(t + S - 1, cur == 0 ? S - 1 : cur - 1);
+    LDS_PTR(const uint8_t) sa = lds + cur * T::kStage;
+    LDS_PTR(const uint8_t) sb = sa + T::kStageA;
 #pragma unroll
-      for (int i = 0; i < T::kFragM; ++i) a[i] = as[k * T::kPitchA + wm * T::kWaveM + i * 32 + lr];
+    for (int q = 0; q < T::kGroups; ++q) {
+      const int c = q & 1, n = c ^ 1;
+      if (q + 1 < T::kGroups) {
 #pragma unroll
-      for (int j = 0; j < T::kFragN; ++j) b[j] = bs[k * T::kPitchB + wn * T::kWaveN + j * 32 + lr];
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, q + 1, lg);
 #pragma unroll
-      for (int i = 0; i < T::kFragM; ++i)
+        for (int j = 0; j < T::kFragN; ++j) b[n][j] = read_b<T>(sb, col_b + 32 * j, q + 1, lg);
+      } else {
+        // Step t+1's copies have landed and every wave is done with the slot
+        // the next issue overwrites; its first operands are read while the
+        // last MFMAs of step t run. After the last step these reads fetch
+        // stale values that are never used.
+        wait_step(t + 1);
+        __syncthreads();
+        LDS_PTR(const uint8_t) na = lds + nxt * T::kStage;
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lg);
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[j], acc[i][j], 0, 0, 0);
+          b[n][j] = read_b<T>(na + T::kStageA, col_b + 32 * j, 0, lg);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::kFragN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x2f32(a[c][i][r], b[c][j][r], acc[i][j], 0, 0, 0);
+      interleave_hint<T>();
     }
-    if (more) store_step<T>(lds + ((t + 1) & 1) * T::kStage, tid, ra, rb);
-    __syncthreads();
+    cur = nxt;
   }
 
   // Element v of a 32 x 32 accumulator: row 8*(v/4) + 4*(lane/32) + v%4,
   // column lane%32.
+  const bool full = (m0 + T::BM <= M) && (n0 + T::BN <= N);
 #pragma unroll
   for (int i = 0; i < T::kFragM; ++i)
 #pragma unroll
     for (int j = 0; j < T::kFragN; ++j) {
-      const int col = n0 + wn * T::kWaveN + j * 32 + lr;
+      const int col = n0 + col_b + 32 * j;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + wm * T::kWaveM + i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3);
-        if (!kGuard || (row < M && col < N)) C[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
+        if (full || (row < M && col < N)) C[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
       }
     }
 }
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void mfma_f32_kernel(
-    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M,
-    int N, int K, int tiles_m, int tiles_n) {
-  using T = Tile<BM, BN, WM, WN>;
-  extern __shared__ __attribute__((aligned(16))) float lds_raw[];
-  LDS_PTR(float) lds = (LDS_PTR(float))lds_raw;
-  int tm, tn;
-  xcd_tile(blockIdx.x, tiles_m, tiles_n, kGroupM, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const bool full = (m0 + BM <= M) && (n0 + BN <= N) && (K % kBK == 0);
-  if (full)
-    tile_product<T, false>(A, B, C, M, N, K, m0, n0, lds);
-  else
-    tile_product<T, true>(A, B, C, M, N, K, m0, n0, lds);
-}
-
-template <int BM, int BN, int WM, int WN>
+template <class T>
 hipError_t launch_tile(const float* A, const float* B, float* C, int M, int N, int K,
                        hipStream_t s) {
-  using T = Tile<BM, BN, WM, WN>;
   static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
-  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(mfma_f32_kernel<BM, BN, WM, WN>),
+  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(mfma_f32_kernel<T>),
                            T::kLdsBytes);
   if (e != hipSuccess) return e;
-  const int tiles_m = (M + BM - 1) / BM;
-  const int tiles_n = (N + BN - 1) / BN;
-  return launch(mfma_f32_kernel<BM, BN, WM, WN>, dim3(tiles_m * tiles_n), dim3(T::kThreads),
-                T::kLdsBytes, s, A, B, C, M, N, K, tiles_m, tiles_n);
+  const int tiles_m = (M + T::BM - 1) / T::BM;
+  const int tiles_n = (N + T::BN - 1) / T::BN;
+  return launch(mfma_f32_kernel<T>, dim3(tiles_m * tiles_n), dim3(T::kThreads), T::kLdsBytes, s,
+                A, B, C, M, N, K, tiles_m, tiles_n);
 }
+
+using LargeTile = Cfg<256, 256, 2, 4, 2>;
+using SmallTile = Cfg<128, 128, 2, 4, 4>;
 
 }  // namespace
 
 bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b, int mis_c) {
   (void)M;
   (void)mis_c;
-  return K % 4 == 0 && N % 4 == 0 && K >= 4 && mis_a == 0 && mis_b == 0;
+  // 32-bit per-lane copy offsets: 256 rows of A and 32 rows of B stay below
+  // 4 GiB from the tile's first element.
+  return K % 4 == 0 && N % 4 == 0 && K >= 4 && K < (1 << 22) && N < (1 << 25) && mis_a == 0 &&
+         mis_b == 0;
 }
 
 hipError_t launch_mfma_f32(const float* A, const float* B, float* C, int M, int N, int K,
                            hipStream_t s) {
-  if (use_large_tiles(M, N, kLargeTileFillF32))
-    return launch_tile<256, 256, 2, 4>(A, B, C, M, N, K, s);
-  return launch_tile<128, 128, 2, 4>(A, B, C, M, N, K, s);
+  if (use_large_tiles(M, N, kLargeTileFillF32)) return launch_tile<LargeTile>(A, B, C, M, N, K, s);
+  return launch_tile<SmallTile>(A, B, C, M, N, K, s);
 }
 
 }  // namespace tdm
