@@ -26,7 +26,9 @@ printed; besides the throughput it carries:
                 measured HBM bytes per launch from rocprofv3 counters when a
                 counter record for the current kernel source exists;
   cpu_baseline  the CPU oracle (plain fp64 triple loop) timed on a bounded
-                sample of the same workload on this host's cores.
+                sample of the same workload on this host's cores;
+  vendor_blas   (with --vendor) torch.mm on the same resident inputs, timed
+                the same way: context, not part of the measurement.
 """
 from __future__ import annotations
 
@@ -79,6 +81,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.mm (PyTorch's ROCm BLAS) on the same resident inputs "
+                         "and report it under vendor_blas, for context")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the product, run a plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -246,6 +251,32 @@ def main():
         auto_info = {"path": auto_choice, "ms_per_call": round(ms_auto, 6),
                      "tflops": round(tf_auto, 3), "roofline_frac": round(tf_auto / peak_auto, 4)}
 
+    # Context only: the vendor BLAS through torch.mm on the same inputs (bf16
+    # with fp32 output, like this library's product), timed the same way.
+    vendor = None
+    if args.vendor:
+        if w.kind == "f32":
+            vsets = [(a, b) for a, b, _ in sets]
+            vmm = torch.mm
+        else:
+            vsets = [(a.view(torch.bfloat16), b.view(torch.bfloat16)) for a, b, _ in sets]
+            vmm = lambda a, b: torch.mm(a, b, out_dtype=torch.float32)  # noqa: E731
+        for i in range(args.warmup):
+            vmm(*vsets[i % rot])
+        torch.cuda.synchronize()
+        v0 = torch.cuda.Event(enable_timing=True)
+        v1 = torch.cuda.Event(enable_timing=True)
+        v0.record(stream)
+        for i in range(args.steps):
+            vmm(*vsets[i % rot])
+        v1.record(stream)
+        torch.cuda.synchronize()
+        ms_v = v0.elapsed_time(v1) / args.steps
+        vendor = {"op": "torch.mm" + ("" if w.kind == "f32" else " (out_dtype=float32)"),
+                  "ms_per_call": round(ms_v, 6),
+                  "tflops": round(roof.flops / (ms_v * 1e-3) / 1e12, 3),
+                  "this_library_over_vendor": round(ms_v / ms, 4)}
+
     line = {
         "metric": "GEMM TFLOP/s and % of MFMA/VALU/HBM roofline per shape, 1x MI355X",
         "value": round(tflops, 3),
@@ -274,6 +305,8 @@ def main():
                      "traffic": None if traffic is None else round(traffic),
                      "algorithmic_bytes": int(roof.bytes), "algorithmic_flops": int(roof.flops)},
     }
+    if vendor is not None:
+        line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, A, B, C_gpu, args.cpu_seconds)
     print(json.dumps(line), flush=True)

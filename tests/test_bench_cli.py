@@ -40,3 +40,10 @@ def test_committed_default_bench_line_keeps_the_contract():
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
     cpu = line["cpu_baseline"]
     assert cpu["kind"] == "oracle" and cpu["cores"] >= 1 and cpu["value"] > 0
+
+
+def test_vendor_comparison_is_opt_in():
+    r = run_bench("--help")
+    assert r.returncode == 0 and "--vendor" in r.stdout
+    with open(os.path.join(ROOT, "profiles", "bench.f32_4096.json")) as fh:
+        assert "vendor_blas" not in json.loads(fh.read())
