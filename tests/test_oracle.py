@@ -374,3 +374,21 @@ def test_block_offset_mistake_is_caught():
     full = oracle.gemm(A, B)
     shifted = oracle.gemm_block(A, B, (1, 33), (0, 32))  # a block taken one row off
     assert not np.array_equal(shifted, full[0:32, 0:32])
+
+
+def test_special_values_follow_ieee_products_and_sums():
+    """Closed forms from IEEE arithmetic: Inf * finite is a signed Inf,
+    Inf * 0 and Inf + (-Inf) are NaN, and NaN is sticky. Checked on fp32
+    inputs and on the same values as bf16 bits."""
+    inf, nan = math.inf, math.nan
+    A = np.array([[inf, 1.0], [nan, 0.0], [1.0, -inf]], np.float32)
+    B = np.array([[1.0, 0.0, inf], [-1.0, 2.0, 1.0]], np.float32)
+    for a, b in ((A, B), (inputs.fp32_to_bf16_bits(A), inputs.fp32_to_bf16_bits(B))):
+        R = oracle.gemm(a, b)
+        assert R[0, 0] == inf                  # inf*1 + 1*(-1)
+        assert math.isnan(R[0, 1])             # inf*0 + 1*2
+        assert R[0, 2] == inf                  # inf*inf + 1*1
+        assert np.isnan(R[1]).all()            # NaN row
+        assert R[2, 0] == inf                  # 1*1 + (-inf)*(-1)
+        assert R[2, 1] == -inf                 # 1*0 + (-inf)*2
+        assert math.isnan(R[2, 2])             # 1*inf + (-inf)*1

@@ -74,7 +74,9 @@ WORKLOADS = {
 def fp32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round fp32 values to bf16 (nearest, ties to even); returns uint16 bits.
 
-    Inputs are finite; NaN payloads are not preserved.
+    Meant for finite values; +-Inf map to the bf16 infinities and the default
+    quiet NaN (0x7FC00000) to a bf16 NaN. A NaN whose payload sits only in the
+    low 16 bits would round to Inf: not used here.
     """
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
     rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
