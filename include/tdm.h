@@ -31,8 +31,9 @@
  * Faults during execution surface at the caller's next synchronization.
  *
  * Errors: arguments are validated on the host before any HIP call.
- *   - NULL pointer (with M*N > 0 and, for A/B, K > 0), negative size, or a
- *     misaligned pointer                                -> TDM_ERROR_INVALID_VALUE
+ *   - NULL pointer (with M*N > 0 and, for A/B, K > 0), negative size, a
+ *     misaligned pointer, or C's bytes overlapping A's or B's (with
+ *     M*N*K > 0)                                        -> TDM_ERROR_INVALID_VALUE
  *   - a matrix with 2^31 or more elements, or a forced path that cannot run
  *     the given shape/alignment                         -> TDM_ERROR_NOT_SUPPORTED
  *   - no HIP device is visible                          -> TDM_ERROR_NO_DEVICE

@@ -57,7 +57,22 @@ def test_version_and_strings():
 # Validation happens before any HIP call: these run identically without a GPU.
 # ---------------------------------------------------------------------------
 
-FAKE = 0x10000  # a 64 KiB-aligned address that is never dereferenced
+def skip_if_gpu():
+    """Calls that pass validation launch kernels: with fake addresses they may
+    only run where no GPU is visible (they then stop at the device check)."""
+    try:
+        import torch
+    except ImportError:
+        return
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present: the call would launch on fake addresses")
+
+
+# 64 KiB-aligned addresses that are never dereferenced, far enough apart that
+# the fake A, B and C of these tests do not overlap (C may not overlap A or B).
+FAKE = 0x10000
+FAKE_B = 1 << 40
+FAKE_C = 1 << 44
 
 
 @pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16_f32acc"])
@@ -65,52 +80,78 @@ def test_validation(fn):
     lib = tdm.load()
     f = getattr(lib, fn)
     S = tdm.Status
-    assert f(FAKE, FAKE, FAKE, -1, 4, 4, None) == S.ERROR_INVALID_VALUE
-    assert f(FAKE, FAKE, FAKE, 4, -1, 4, None) == S.ERROR_INVALID_VALUE
-    assert f(FAKE, FAKE, FAKE, 4, 4, -1, None) == S.ERROR_INVALID_VALUE
-    assert f(None, FAKE, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
-    assert f(FAKE, None, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
-    assert f(FAKE, FAKE, None, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
-    assert f(FAKE, FAKE, FAKE + 1, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # C misaligned
-    assert f(FAKE + 1, FAKE, FAKE, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # A misaligned
+    assert f(FAKE, FAKE_B, FAKE_C, -1, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, 4, -1, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, 4, 4, -1, None) == S.ERROR_INVALID_VALUE
+    assert f(None, FAKE_B, FAKE_C, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, None, FAKE_C, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, None, 4, 4, 4, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C + 1, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # C misaligned
+    assert f(FAKE + 1, FAKE_B, FAKE_C, 4, 4, 4, None) == S.ERROR_INVALID_VALUE  # A misaligned
     # Empty outputs are a no-op, with or without pointers and device.
     assert f(None, None, None, 0, 4, 4, None) == S.SUCCESS
     assert f(None, None, None, 4, 0, 4, None) == S.SUCCESS
     # 2^31 elements in one matrix is beyond 32-bit indexing.
-    assert f(FAKE, FAKE, FAKE, 1 << 16, 1 << 15, 1, None) == S.ERROR_NOT_SUPPORTED
-    assert f(FAKE, FAKE, FAKE, 1, 1 << 20, 1 << 11, None) == S.ERROR_NOT_SUPPORTED
+    assert f(FAKE, FAKE_B, FAKE_C, 1 << 16, 1 << 15, 1, None) == S.ERROR_NOT_SUPPORTED
+    assert f(FAKE, FAKE_B, FAKE_C, 1, 1 << 20, 1 << 11, None) == S.ERROR_NOT_SUPPORTED
+
+
+@pytest.mark.parametrize("fn,esize", [("gemm_f32", 4), ("gemm_bf16_f32acc", 2)])
+def test_output_overlapping_an_input_is_rejected(fn, esize):
+    f = getattr(tdm.load(), fn)
+    S = tdm.Status
+    M = N = K = 64
+    a_bytes, c_bytes = M * K * esize, M * N * 4
+    # C starting inside A, A starting inside C, C == B, C ending on B's first byte
+    assert f(FAKE, FAKE_B, FAKE + a_bytes - 16, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE_C + 64, FAKE_B, FAKE_C, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_B, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_B - c_bytes + 4, M, N, K, None) == S.ERROR_INVALID_VALUE
+
+
+@pytest.mark.parametrize("fn,esize", [("gemm_f32", 4), ("gemm_bf16_f32acc", 2)])
+def test_adjacent_or_input_only_overlap_passes_validation(fn, esize):
+    skip_if_gpu()
+    f = getattr(tdm.load(), fn)
+    S = tdm.Status
+    M = N = K = 64
+    a_bytes, c_bytes = M * K * esize, M * N * 4
+    # Adjacent but disjoint is fine (without a GPU the call then stops at the
+    # device check); A and B may overlap each other, both are only read; with
+    # K == 0 nothing is read and only C matters.
+    assert f(FAKE, FAKE_B, FAKE + a_bytes, M, N, K, None) == S.ERROR_NO_DEVICE
+    assert f(FAKE, FAKE_B, FAKE_B - c_bytes, M, N, K, None) == S.ERROR_NO_DEVICE
+    assert f(FAKE_B, FAKE_B, FAKE_C, M, N, K, None) == S.ERROR_NO_DEVICE
+    assert f(FAKE_C, FAKE_C, FAKE_C, M, N, 0, None) == S.ERROR_NO_DEVICE
 
 
 def test_validation_with_k_zero_needs_only_c():
+    skip_if_gpu()
     lib = tdm.load()
     # K == 0: A and B may be NULL; without a GPU the call stops at the device check.
-    st = lib.gemm_f32(None, None, FAKE, 3, 3, 0, None)
-    assert st in (tdm.Status.ERROR_NO_DEVICE, tdm.Status.SUCCESS)
+    assert lib.gemm_f32(None, None, FAKE, 3, 3, 0, None) == tdm.Status.ERROR_NO_DEVICE
 
 
 def test_bad_path_and_unsupported_paths():
     lib = tdm.load()
     S, P = tdm.Status, tdm.Path
-    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 4, 4, 4, 77, None) == S.ERROR_INVALID_VALUE
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE_B, FAKE_C, 4, 4, 4, 77, None) == S.ERROR_INVALID_VALUE
     # dtype/path mismatches are rejected before any device work
-    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 64, 62, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
-    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 16, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
-    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 64, 64, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE_B, FAKE_C, 64, 64, 62, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE_B, FAKE_C, 16, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE_B, FAKE_C, 64, 64, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
     # shape/alignment limits of the fast paths
-    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 64, 64, 60, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
-    assert lib.tdm_gemm_bf16_f32acc_path(FAKE + 2, FAKE, FAKE, 64, 64, 64, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
-    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE, FAKE, 17, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
-    assert lib.tdm_gemm_f32_path(FAKE, FAKE, FAKE, 64, 66, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE_B, FAKE_C, 64, 64, 60, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE + 2, FAKE_B, FAKE_C, 64, 64, 64, P.MFMA, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_bf16_f32acc_path(FAKE, FAKE_B, FAKE_C, 17, 64, 64, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
+    assert lib.tdm_gemm_f32_path(FAKE, FAKE_B, FAKE_C, 64, 66, 64, P.VALU, None) == S.ERROR_NOT_SUPPORTED
 
 
 def test_no_device_is_reported_not_crashed():
-    pytest.importorskip("torch")
-    import torch
-    if torch.cuda.is_available():
-        pytest.skip("a GPU is present")
+    skip_if_gpu()
     lib = tdm.load()
-    assert lib.gemm_f32(FAKE, FAKE, FAKE, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
-    assert lib.gemm_bf16_f32acc(FAKE, FAKE, FAKE, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
+    assert lib.gemm_f32(FAKE, FAKE_B, FAKE_C, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
+    assert lib.gemm_bf16_f32acc(FAKE, FAKE_B, FAKE_C, 4, 4, 4, None) == tdm.Status.ERROR_NO_DEVICE
 
 
 # ---------------------------------------------------------------------------

@@ -28,6 +28,12 @@ bool too_big(int64_t M, int64_t N, int64_t K) {
   return over(M, K) || over(K, N) || over(M, N);
 }
 
+// True when byte ranges [p, p+pb) and [q, q+qb) share an address.
+bool overlaps(const void* p, uint64_t pb, const void* q, uint64_t qb) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return pb > 0 && qb > 0 && a < b + qb && b < a + pb;
+}
+
 tdm_status check_device() {
   int n = 0;
   if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) return TDM_ERROR_NO_DEVICE;
@@ -98,6 +104,12 @@ tdm_status validate(const T* A, const T* B, const float* C, int64_t M, int64_t N
                 (reinterpret_cast<uintptr_t>(B) % alignof(T)) != 0))
     return TDM_ERROR_INVALID_VALUE;
   if (too_big(M, N, K)) return TDM_ERROR_NOT_SUPPORTED;
+  if (K > 0) {  // C is written while A and B are read: it may share no byte with them
+    const uint64_t c_bytes = uint64_t(M) * uint64_t(N) * sizeof(float);
+    if (overlaps(C, c_bytes, A, uint64_t(M) * uint64_t(K) * sizeof(T)) ||
+        overlaps(C, c_bytes, B, uint64_t(K) * uint64_t(N) * sizeof(T)))
+      return TDM_ERROR_INVALID_VALUE;
+  }
   return TDM_SUCCESS;
 }
 
