@@ -16,10 +16,12 @@
  *     a strided or transposed view must be made contiguous by the caller.
  *   - A, B and C are DEVICE pointers on the current HIP device, owned by the
  *     caller. The only memory the library allocates is the small-M path's
- *     per-device workspace for partial sums (about 8 MB for M <= 16,
- *     N = 8192), allocated on that path's first use and kept until the
- *     process ends. Two small-M calls running at the same time on one device
- *     (on different streams) share it and race.
+ *     workspace for partial sums, one per device and stream (about 8 MB for
+ *     M <= 16, N = 8192), allocated on the first small-M call on that stream
+ *     and kept until the process ends. Calls on different streams therefore
+ *     do not share it. Up to 32 streams per device keep their own; a call
+ *     from a 33rd stream reuses the least recently used one after waiting
+ *     for the device to go idle (hipDeviceSynchronize).
  *   - A and B are read only. C is overwritten (there is no alpha/beta). C
  *     must not overlap A or B.
  *   - Element sizes: fp32 = 4 bytes; bf16 = 2 bytes passed as raw uint16_t
@@ -44,8 +46,10 @@
  *
  * Threading: the calls may be made from several host threads; work on one
  * stream is ordered as usual. The only mutable global state is the small-M
- * workspace (guarded by a mutex; see above for calls in flight at the same
- * time) and a per-device record of the kernels' LDS attribute.
+ * workspace table (guarded by a mutex) and a per-device record of the
+ * kernels' LDS attribute. A graph captured from a stream keeps using that
+ * stream's workspace when replayed: do not replay it concurrently with other
+ * small-M work on the stream it was captured from.
  */
 #ifndef TDM_H
 #define TDM_H

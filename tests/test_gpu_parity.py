@@ -209,6 +209,55 @@ def test_nondefault_stream():
     check_full("bf16", A, B, C.cpu().numpy(), "stream")
 
 
+def test_small_m_calls_on_two_streams_at_once():
+    """The split-K partial sums live in a per-stream workspace: calls queued on
+    two streams at the same time must not disturb each other."""
+    log("case small-M two streams")
+    rng = np.random.default_rng(79)
+    ins = [(inputs.normal_bf16(rng, (16, 4096), 1.0), inputs.normal_bf16(rng, (4096, 2048), 0.02))
+           for _ in range(2)]
+    dev = [(to_device(A), to_device(B), torch.empty((16, 2048), device="cuda")) for A, B in ins]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(20):
+        for (Ad, Bd, Cd), s in zip(dev, streams):
+            run("bf16", Ad, Bd, P.SKINNY, Cd, stream=s)
+    torch.cuda.synchronize()
+    for (A, B), (_, _, Cd) in zip(ins, dev):
+        C = Cd.cpu().numpy()
+        check_full("bf16", A, B, C, "two streams")
+        assert np.array_equal(C, gpu_product("bf16", A, B, P.SKINNY))
+
+
+def test_small_m_calls_on_more_streams_than_workspace_slots():
+    """34 streams: the 33rd and 34th take over the least recently used slots."""
+    import ctypes
+    log("case small-M 34 streams")
+    hip = ctypes.CDLL("libamdhip64.so")
+    A, B = random_inputs("bf16", 16, 1024, 2048, 80)
+    Ad, Bd = to_device(A), to_device(B)
+    ref = gpu_product("bf16", A, B, P.SKINNY)
+    outs = [torch.empty((16, 1024), device="cuda") for _ in range(34)]
+    handles = []
+    try:
+        for _ in range(34):
+            h = ctypes.c_void_p()
+            assert hip.hipStreamCreate(ctypes.byref(h)) == 0
+            handles.append(h)
+        torch.cuda.synchronize()
+        for h, Cd in zip(handles, outs):
+            run("bf16", Ad, Bd, P.SKINNY, Cd, stream=h.value)
+        for h, Cd in zip(handles, outs):  # again, now with every slot taken
+            run("bf16", Ad, Bd, P.SKINNY, Cd, stream=h.value)
+        torch.cuda.synchronize()
+    finally:
+        torch.cuda.synchronize()
+        for h in handles:
+            hip.hipStreamDestroy(h)
+    for Cd in outs:
+        assert np.array_equal(Cd.cpu().numpy(), ref)
+
+
 def test_misaligned_pointers():
     log("case misaligned")
     A, B = random_inputs("bf16", 64, 64, 64, 78)

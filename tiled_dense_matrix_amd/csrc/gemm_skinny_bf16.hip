@@ -273,30 +273,55 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
   C[static_cast<int64_t>(row) * N + col] = sum;
 }
 
-// Per-device workspace for the partial sums. It grows on
-// demand and is kept until the process ends (a kernel may still use the old
-// one when it grows, so that one is never freed).
+// Workspace for the partial sums: one buffer per (device, stream), so calls
+// on different streams never share one and calls on one stream are ordered
+// by the stream. A buffer grows on demand and is kept until the process ends
+// (a kernel may still use the old one when it grows, so that one is never
+// freed). Up to kStreamSlots streams per device keep their own buffer; a call
+// from a further stream takes over the least recently used slot after waiting
+// for the device to go idle (hipDeviceSynchronize), since that slot's stream
+// may still have work in flight.
+constexpr int kStreamSlots = 32;
+struct StreamSlot {
+  hipStream_t stream = nullptr;  // compared only, never used
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  uint64_t last_use = 0;  // 0: free
+};
 struct Workspace {
   std::mutex mu;
-  void* ptr[64] = {};
-  size_t bytes[64] = {};
+  uint64_t clock = 0;
+  StreamSlot slot[64][kStreamSlots];
 };
 Workspace g_ws;
 
-hipError_t workspace(size_t need, void** out) {
+hipError_t workspace(hipStream_t s, size_t need, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_ws.mu);
-  if (g_ws.bytes[dev] < need) {
+  StreamSlot* slots = g_ws.slot[dev];
+  StreamSlot* w = nullptr;
+  StreamSlot* lru = &slots[0];
+  for (int i = 0; i < kStreamSlots && w == nullptr; ++i) {
+    if (slots[i].last_use != 0 && slots[i].stream == s) w = &slots[i];
+    else if (slots[i].last_use < lru->last_use) lru = &slots[i];
+  }
+  if (w == nullptr) {
+    if (lru->last_use != 0 && (e = hipDeviceSynchronize()) != hipSuccess) return e;
+    w = lru;
+    w->stream = s;
+  }
+  if (w->bytes < need) {
     void* p = nullptr;
     const size_t bytes = need < (size_t{8} << 20) ? (size_t{8} << 20) : need;
     if ((e = hipMalloc(&p, bytes)) != hipSuccess) return e;
-    g_ws.ptr[dev] = p;
-    g_ws.bytes[dev] = bytes;
+    w->ptr = p;
+    w->bytes = bytes;
   }
-  *out = g_ws.ptr[dev];
+  w->last_use = ++g_ws.clock;
+  *out = w->ptr;
   return hipSuccess;
 }
 
@@ -326,7 +351,7 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
     const size_t part_bytes =
         static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
     void* ws = nullptr;
-    if ((e = workspace(part_bytes, &ws)) != hipSuccess) return e;
+    if ((e = workspace(s, part_bytes, &ws)) != hipSuccess) return e;
     partials = static_cast<float*>(ws);
   }
   e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B, C, M,
