@@ -1,8 +1,8 @@
 """Near the size limit: matrices just below 2^31 elements (needs an MI355X).
 
-The library indexes each matrix with 32-bit element counts (and the bf16
-matrix-core kernel with 32-bit byte offsets per lane), so the largest legal
-operands are where an overflow would show. Inputs are small integers, so
+The library indexes each matrix with 32-bit element counts (and the
+matrix-core kernels' copies with 32-bit byte offsets per lane), so the largest
+legal operands are where an overflow would show. Inputs are small integers, so
 every partial sum is exact in fp32 and sampled tiles must match the oracle
 bit for bit; the tiles include the last rows and columns, which sit at the
 largest offsets.
@@ -47,6 +47,12 @@ def corner_tiles(M, N, tile=32):
     ("f32", (65536, 128, 32764), P.VALU),
     ("f32", (65536, 128, 32764), P.EDGE),
     ("bf16", (65536, 256, 32760), P.EDGE),
+    # The fp32 matrix-core kernel copies with 32-bit byte offsets from the
+    # tile's first row: 32 rows of B reach 31*N*4 bytes, just below 2^32 here,
+    # and K just below 2^22 is the longest it takes.
+    ("f32", (32, (1 << 25) - 4, 32), P.MFMA),
+    ("f32", (32, (1 << 25) - 4, 32), P.VALU),
+    ("f32", (256, 128, (1 << 22) - 4), P.MFMA),
 ])
 def test_operands_just_below_two_to_the_31(kind, shape, path):
     M, N, K = shape
