@@ -12,7 +12,9 @@ accumulation, C write-back). The square fp32 4096 product runs on the
 vector-ALU kernel by default; the matrix-core kernel that the auto path
 picks for it is then timed as well and reported under config.auto_path
 (--path mfma makes it the main measurement). Every other workload runs on
-the auto path.
+the auto path; bf16_mlp_gelu is the MLP product finished in the kernel (+
+bias, GELU, bf16 output, through gemm_bf16_epilogue), and its line also
+times the same steps unfused (config.unfused).
 Consecutive steps rotate over several copies of (A, B, C) whose total size
 exceeds the 256 MB last-level cache, so every step reads its operands from
 HBM.
@@ -127,8 +129,9 @@ def copy_probe(mib: int):
                       "launches": 5}), flush=True)
 
 
-def cpu_baseline(w, A, B, C_gpu, target_s: float):
-    """Time the oracle on the first rows of C; also check those rows."""
+def cpu_baseline(w, A, B, C_gpu, target_s: float, bias=None):
+    """Time the oracle on the first rows of C (with the workload's epilogue,
+    if any); also check those rows."""
     import oracle
     threads = oracle.default_threads()
     # Calibrate on one row per thread, then size the sample to ~target_s.
@@ -141,11 +144,14 @@ def cpu_baseline(w, A, B, C_gpu, target_s: float):
         rows -= rows % threads  # whole rows per thread
     t0 = time.perf_counter()
     R = oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
+    if w.has_epilogue:
+        R = oracle.epilogue(R, bias, None, w.gelu)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
     ma = float(np.abs(oracle.widen(A)).max())
     mb = float(np.abs(oracle.widen(B)).max())
-    p = oracle.parity(C_gpu[:rows], R, ma, mb, w.K)
+    got = oracle.widen(C_gpu[:rows]) if C_gpu.dtype == np.uint16 else C_gpu[:rows]
+    p = oracle.parity(got, R, ma, mb, w.K)
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -191,22 +197,36 @@ def main():
             X = X.view(np.int16)
         return torch.from_numpy(X).cuda()
 
+    # A workload with a fused epilogue (bias, GELU, bf16 output) runs the
+    # product through gemm_bf16_epilogue; its output has the epilogue's type.
+    epi = w.has_epilogue
+    out_bf16 = epi and w.out == "bf16"
+    out_size = 2 if out_bf16 else 4
+    bias_np = inputs.make_bias(w) if epi and w.bias_sigma > 0 else None
+
     A0, B0 = dev(A), dev(B)
-    set_bytes = A0.numel() * A0.element_size() + B0.numel() * B0.element_size() + w.M * w.N * 4
+    bias_d = None if bias_np is None else dev(bias_np)
+    set_bytes = A0.numel() * A0.element_size() + B0.numel() * B0.element_size() + \
+        w.M * w.N * out_size
     rot = max(2, math.ceil(ROTATE_BYTES / set_bytes))
-    sets = [(A0, B0, torch.empty((w.M, w.N), dtype=torch.float32, device="cuda"))]
+    out_t = torch.bfloat16 if out_bf16 else torch.float32
+    sets = [(A0, B0, torch.empty((w.M, w.N), dtype=out_t, device="cuda"))]
     for _ in range(rot - 1):
         sets.append((A0.clone(), B0.clone(), torch.empty_like(sets[0][2])))
 
     fn = tdm.tdm_gemm_f32_path if w.kind == "f32" else tdm.tdm_gemm_bf16_f32acc_path
     stream = torch.cuda.current_stream()
 
-    def timed(p) -> float:
-        """Average ms per call of path p over args.steps calls after args.warmup."""
-        def step(i):
-            a, b, c = sets[i % rot]
+    def call(i, p):
+        a, b, c = sets[i % rot]
+        if epi:
+            tdm.tdm_gemm_bf16_epilogue_path(a, b, c, bias=bias_d, gelu=w.gelu, path=p,
+                                            stream=stream)
+        else:
             fn(a, b, c, path=p, stream=stream)
 
+    def time_steps(step) -> float:
+        """Average ms per step(i) over args.steps steps after args.warmup."""
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
@@ -219,11 +239,19 @@ def main():
         torch.cuda.synchronize()
         return start.elapsed_time(end) / args.steps
 
+    def timed(p) -> float:
+        return time_steps(lambda i: call(i, p))
+
     ms = timed(path)
 
     roof = tdm.gemm_roofline(kind, w.M, w.N, w.K)
+    # Bytes with every array crossing HBM once: A and B read, the bias read,
+    # the output written in its own element type.
+    alg_bytes = roof.bytes if not epi else \
+        2 * (w.M * w.K + w.K * w.N) + out_size * w.M * w.N + \
+        (out_size * w.N if bias_np is not None else 0)
     tflops = roof.flops / (ms * 1e-3) / 1e12
-    gbs = roof.bytes / (ms * 1e-3) / 1e9
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
     if pname == "skinny":
         bound, unit, achieved, peak = "hbm", "GB/s", gbs, PEAK["hbm"]
     elif pname == "mfma":
@@ -234,7 +262,9 @@ def main():
     traffic = traffic_record(kernels, ksrc, w.name)
 
     # Every rotated copy must hold the same product (spot check: first rows).
-    C_gpu = sets[(args.warmup + args.steps - 1) % rot][2].cpu().numpy()
+    C_last = sets[(args.warmup + args.steps - 1) % rot][2]
+    C_gpu = C_last.view(torch.int16).cpu().numpy().view(np.uint16) if out_bf16 else \
+        C_last.cpu().numpy()
     if args.warmup + args.steps >= rot:
         for a, b, c in sets[1:]:
             assert torch.equal(c[:4], sets[0][2][:4]), "rotated copies disagree"
@@ -251,29 +281,52 @@ def main():
         auto_info = {"path": auto_choice, "ms_per_call": round(ms_auto, 6),
                      "tflops": round(tf_auto, 3), "roofline_frac": round(tf_auto / peak_auto, 4)}
 
-    # Context only: the vendor BLAS through torch.mm on the same inputs (bf16
-    # with fp32 output, like this library's product), timed the same way.
+    # The same epilogue unfused: this library's product with fp32 output, then
+    # the bias add, GELU and bf16 conversion as separate torch operations.
+    unfused = None
+    if epi:
+        cf = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
+        bias_f = None if bias_d is None else \
+            (bias_d.view(torch.bfloat16).float() if out_bf16 else bias_d)
+
+        def unfused_step(i):
+            a, b, c = sets[i % rot]
+            fn(a, b, cf, path=path, stream=stream)
+            t = cf if bias_f is None else cf + bias_f
+            if w.gelu:
+                t = torch.nn.functional.gelu(t)
+            c.copy_(t)
+
+        ms_u = time_steps(unfused_step)
+        unfused = {"what": "gemm_bf16_f32acc, then bias add, GELU and conversion in torch",
+                   "ms_per_call": round(ms_u, 6), "fused_speedup": round(ms_u / ms, 4)}
+        del cf
+
+    # Context only: the vendor BLAS through torch on the same inputs (bf16
+    # with fp32 output, like this library's product; for an epilogue
+    # workload torch.addmm with the bias and bf16 output, then GELU), timed
+    # the same way.
     vendor = None
     if args.vendor:
         if w.kind == "f32":
             vsets = [(a, b) for a, b, _ in sets]
-            vmm = torch.mm
+            vmm, vop = torch.mm, "torch.mm"
         else:
             vsets = [(a.view(torch.bfloat16), b.view(torch.bfloat16)) for a, b, _ in sets]
-            vmm = lambda a, b: torch.mm(a, b, out_dtype=torch.float32)  # noqa: E731
-        for i in range(args.warmup):
-            vmm(*vsets[i % rot])
-        torch.cuda.synchronize()
-        v0 = torch.cuda.Event(enable_timing=True)
-        v1 = torch.cuda.Event(enable_timing=True)
-        v0.record(stream)
-        for i in range(args.steps):
-            vmm(*vsets[i % rot])
-        v1.record(stream)
-        torch.cuda.synchronize()
-        ms_v = v0.elapsed_time(v1) / args.steps
-        vendor = {"op": "torch.mm" + ("" if w.kind == "f32" else " (out_dtype=float32)"),
-                  "ms_per_call": round(ms_v, 6),
+            if not epi:
+                vmm = lambda a, b: torch.mm(a, b, out_dtype=torch.float32)  # noqa: E731
+                vop = "torch.mm (out_dtype=float32)"
+            else:
+                if not out_bf16:
+                    raise SystemExit("--vendor covers epilogue workloads with bf16 output")
+                bias_v = None if bias_d is None else bias_d.view(torch.bfloat16)
+
+                def vmm(a, b):
+                    t = torch.mm(a, b) if bias_v is None else torch.addmm(bias_v, a, b)
+                    return torch.nn.functional.gelu(t) if w.gelu else t
+                vop = "torch.addmm (bf16 out), then GELU"
+        ms_v = time_steps(lambda i: vmm(*vsets[i % rot]))
+        vendor = {"op": vop, "ms_per_call": round(ms_v, 6),
                   "tflops": round(roof.flops / (ms_v * 1e-3) / 1e12, 3),
                   "this_library_over_vendor": round(ms_v / ms, 4)}
 
@@ -295,6 +348,9 @@ def main():
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
                    "rotated_copies": rot,
                    "auto_path": auto_info,
+                   "epilogue": None if not epi else {"bias": bias_np is not None,
+                                                     "gelu": w.gelu, "out": w.out},
+                   "unfused": unfused,
                    "gbps_algorithmic": round(gbs, 1)},
         # One launch of the dominant kernel is timed as one call; a path that
         # launches a second kernel (the skinny path's reduction) is timed
@@ -303,12 +359,12 @@ def main():
                      "scope": "kernel" if len(kernels) == 1 else "call (" + " + ".join(kernels) + ")",
                      "frac": round(achieved / peak, 4),
                      "traffic": None if traffic is None else round(traffic),
-                     "algorithmic_bytes": int(roof.bytes), "algorithmic_flops": int(roof.flops)},
+                     "algorithmic_bytes": int(alg_bytes), "algorithmic_flops": int(roof.flops)},
     }
     if vendor is not None:
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, A, B, C_gpu, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(w, A, B, C_gpu, args.cpu_seconds, bias_np)
     print(json.dumps(line), flush=True)
 
 

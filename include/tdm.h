@@ -111,6 +111,41 @@ TDM_API tdm_status gemm_f32(const float* A, const float* B, float* C, int64_t M,
 TDM_API tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C,
                             int64_t M, int64_t N, int64_t K, void* stream);
 
+/* Element type of an epilogue's output D, bias and residual. */
+typedef enum tdm_dtype {
+  TDM_DTYPE_F32 = 0,  /* 4-byte IEEE float                                   */
+  TDM_DTYPE_BF16 = 1  /* bf16 as raw uint16_t bits                            */
+} tdm_dtype;
+
+/* D = epilogue(A * B): the bf16 product of gemm_bf16_f32acc, finished in
+ * the kernel that computes it (fused: the fp32 sums never reach memory), as
+ * in the operator-fusion section of the CS336 Lecture 5 GPU notes (§4.3) and
+ * the GELU + residual example of LLM course ch. 15. Per output element, in
+ * fp32:
+ *   t = sum_k A[i,k] * B[k,j]                (as gemm_bf16_f32acc; 0 if K == 0)
+ *   t = t + bias[j]                          if bias != NULL
+ *   t = GELU(t) = t/2 * (1 + erf(t/sqrt(2))) if gelu != 0 (the exact form)
+ *   t = t + residual[i,j]                    if residual != NULL
+ *   D[i,j] = t, stored as d_type (bf16: rounded to nearest, ties to even)
+ * D, bias (N elements) and residual (M x N, row-major) are device pointers
+ * of element type d_type, aligned to it. residual may be D itself (an
+ * in-place residual add); otherwise D may not overlap A, B, bias or
+ * residual. Errors as for gemm_bf16_f32acc, plus TDM_ERROR_INVALID_VALUE for
+ * an unknown d_type or a misaligned bias/residual. K == 0 is not a no-op:
+ * D = epilogue(0). */
+TDM_API tdm_status gemm_bf16_epilogue(const uint16_t* A, const uint16_t* B, void* D,
+                                      tdm_dtype d_type, const void* bias, const void* residual,
+                                      int gelu, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Same, on a given path (TDM_PATH_EDGE, TDM_PATH_MFMA, TDM_PATH_SKINNY or
+ * TDM_PATH_AUTO); TDM_ERROR_NOT_SUPPORTED where gemm_bf16_f32acc's path
+ * would be. */
+TDM_API tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, void* D,
+                                               tdm_dtype d_type, const void* bias,
+                                               const void* residual, int gelu, int64_t M,
+                                               int64_t N, int64_t K, tdm_path path,
+                                               void* stream);
+
 /* Host-only cost query; touches no device. FLOPs = 2MNK (a multiply-add is
  * two operations) and bytes = reading A and B once and writing C once
  * (compute- vs memory-bound lesson, counting a matrix multiply; CS336

@@ -23,6 +23,14 @@ What it computes, and the passage each function follows:
 * ``freivalds`` -- a full-coverage probabilistic check of a product
   (C x against A (B x) for a random +-1 vector x), used where the full
   product is too large for the triple loop.
+* ``gelu``, ``epilogue`` -- the elementwise work a fused epilogue applies to
+  the product before it is written: + bias[j], GELU(t) = t * Phi(t), +
+  residual[i, j], in that order (CS336 Lecture 5 GPU notes, §4.3, operator
+  fusion; LLM course ch. 15, the GELU-then-residual-add example). The pages
+  name GELU without a formula; this is its exact (erf) form.
+* ``round_to_bf16`` -- bf16 bits of fp64 values that fp32 holds exactly,
+  rounded to nearest with ties to even (CS336 Lecture 5 GPU notes, §3.1 on
+  bf16 as the upper half of an fp32 word).
 
 Every function is pinned by tests in ``tests/test_oracle.py`` against values
 the pages print, closed forms (identity, permutation, all-ones, rank-1),
@@ -209,3 +217,45 @@ def freivalds(A: np.ndarray, B: np.ndarray, C: np.ndarray, x: np.ndarray) -> dic
         "max_row_abs_sum": float(np.abs(C64).sum(axis=1).max()) if C64.size else 0.0,
         "c_fro": float(np.linalg.norm(C64)),
     }
+
+
+# ---------------------------------------------------------------------------
+# Fused epilogue (elementwise work on the product before it is stored)
+# ---------------------------------------------------------------------------
+
+def gelu(x) -> np.ndarray:
+    """GELU(x) = x * Phi(x) = x/2 * (1 + erf(x / sqrt(2))) in fp64, Phi the
+    standard normal CDF (the exact form, not the tanh approximation)."""
+    from scipy.special import erf
+    x = np.asarray(x, dtype=np.float64)
+    return 0.5 * x * (1.0 + erf(x / np.sqrt(2.0)))
+
+
+def epilogue(R: np.ndarray, bias: np.ndarray | None = None,
+             residual: np.ndarray | None = None, use_gelu: bool = False) -> np.ndarray:
+    """fp64 epilogue of a product R[M, N]: R + bias[j] (bias broadcast along
+    the rows), then GELU, then + residual[i, j]. bias and residual are
+    float32 arrays or bf16 bits, widened exactly."""
+    T = np.array(R, dtype=np.float64)
+    if bias is not None:
+        T = T + widen(np.asarray(bias))[None, :]
+    if use_gelu:
+        T = gelu(T)
+    if residual is not None:
+        T = T + widen(np.asarray(residual))
+    return T
+
+
+def round_to_bf16(x) -> np.ndarray:
+    """bf16 bits nearest to each value (ties to even). The values must be
+    exactly representable in fp32 (checked), so this is the rounding of the
+    fp32 word's lower 16 bits."""
+    x = np.asarray(x, dtype=np.float64)
+    f = x.astype(np.float32)
+    if not np.array_equal(f.astype(np.float64), x, equal_nan=True):
+        raise ValueError("round_to_bf16 takes values that fp32 holds exactly")
+    u = f.view(np.uint32).astype(np.uint64)
+    upper, lower = u >> 16, u & 0xFFFF
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    return (upper + up.astype(np.uint64)).astype(np.uint16)
+

@@ -221,3 +221,41 @@ def test_f32_mfma_copy_offset_limits():
     # tiles and go to the edge kernel anyway; a wide B can reach the limit.
     assert tdm.tdm_select_path(K.F32, 32, 1 << 25, 32) == P.VALU
     assert tdm.tdm_select_path(K.F32, 32, (1 << 25) - 4, 32) == P.MFMA
+
+
+# ---------------------------------------------------------------------------
+# The fused-epilogue entry points: validation before any HIP call.
+# ---------------------------------------------------------------------------
+
+FAKE_BIAS = 1 << 42
+FAKE_RES = 1 << 43
+
+
+def test_epilogue_validation():
+    lib = tdm.load()
+    f, fp = lib.gemm_bf16_epilogue, lib.tdm_gemm_bf16_epilogue_path
+    S, P, D = tdm.Status, tdm.Path, tdm.DType
+    M = N = K = 64
+    assert f(FAKE, FAKE_B, FAKE_C, 7, None, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, None, D.BF16, None, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C + 2, D.F32, None, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, D.BF16, FAKE_BIAS + 1, None, 1, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, D.F32, None, FAKE_RES + 2, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(None, FAKE_B, FAKE_C, D.BF16, None, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    # D may not overlap A, B or bias; residual must be D itself or disjoint from it
+    assert f(FAKE, FAKE_B, FAKE + 64, D.BF16, None, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, D.BF16, FAKE_C + 16, None, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, FAKE_C, D.BF16, None, FAKE_C + 2, 0, M, N, K, None) == S.ERROR_INVALID_VALUE
+    # empty output: no-op; paths that cannot take bf16 or the shape
+    assert f(None, None, None, D.F32, None, None, 1, 0, N, K, None) == S.SUCCESS
+    assert fp(FAKE, FAKE_B, FAKE_C, D.BF16, None, None, 0, M, N, K, P.VALU, None) == S.ERROR_NOT_SUPPORTED
+    assert fp(FAKE, FAKE_B, FAKE_C, D.BF16, None, None, 0, 17, N, K, P.SKINNY, None) == S.ERROR_NOT_SUPPORTED
+    assert fp(FAKE, FAKE_B, FAKE_C, D.BF16, None, None, 0, M, N, K, 9, None) == S.ERROR_INVALID_VALUE
+
+
+def test_epilogue_in_place_residual_and_k_zero_pass_validation():
+    skip_if_gpu()
+    f = tdm.load().gemm_bf16_epilogue
+    S, D = tdm.Status, tdm.DType
+    assert f(FAKE, FAKE_B, FAKE_C, D.BF16, FAKE_BIAS, FAKE_C, 1, 64, 64, 64, None) == S.ERROR_NO_DEVICE
+    assert f(None, None, FAKE_C, D.F32, FAKE_BIAS, FAKE_RES, 1, 64, 64, 0, None) == S.ERROR_NO_DEVICE

@@ -89,3 +89,15 @@ def test_small_int_and_pm_one():
     assert set(np.unique(v).tolist()) <= set(range(-3, 4))
     x = inputs.pm_one_vector(rng, 1000)
     assert set(np.unique(x).tolist()) == {-1.0, 1.0}
+
+
+def test_epilogue_workload_shares_the_mlp_operands_and_draws_its_bias_apart():
+    w = inputs.WORKLOADS["bf16_mlp_gelu"]
+    m = inputs.WORKLOADS["bf16_mlp"]
+    assert (w.M, w.N, w.K, w.seed, w.sigma_a, w.sigma_b) == (m.M, m.N, m.K, m.seed, m.sigma_a, m.sigma_b)
+    assert w.has_epilogue and not m.has_epilogue and w.gelu and w.out == "bf16"
+    b = inputs.make_bias(w)
+    assert b.dtype == np.uint16 and b.shape == (w.N,)
+    assert np.array_equal(b, inputs.make_bias("bf16_mlp_gelu"))  # seeded
+    x = inputs.bf16_bits_to_fp32(b).astype(np.float64)
+    assert abs(x.std() - 0.02) < 0.002 and abs(x.mean()) < 0.002

@@ -392,3 +392,45 @@ def test_special_values_follow_ieee_products_and_sums():
         assert R[2, 0] == inf                  # 1*1 + (-inf)*(-1)
         assert R[2, 1] == -inf                 # 1*0 + (-inf)*2
         assert math.isnan(R[2, 2])             # 1*inf + (-inf)*1
+
+
+# ---------------------------------------------------------------------------
+# Fused epilogue: GELU, bias, residual, bf16 rounding.
+# ---------------------------------------------------------------------------
+
+def test_gelu_matches_the_normal_cdf_table():
+    """GELU(x) = x Phi(x): Phi(1) = 0.8413447460685429 and Phi(2) =
+    0.9772498680518208 (standard normal table). The tanh approximation
+    (0.84119 at 1), x*sigmoid(1.702x), a missing 1/2 or erf(x/2) all miss."""
+    assert oracle.gelu(0.0) == 0.0
+    assert abs(oracle.gelu(1.0) - 0.8413447460685429) < 1e-15
+    assert abs(oracle.gelu(-1.0) + (1.0 - 0.8413447460685429)) < 1e-15
+    assert abs(oracle.gelu(2.0) - 2 * 0.9772498680518208) < 1e-15
+    x = np.linspace(-8.0, 8.0, 161)
+    assert np.allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=0, atol=1e-14)  # Phi(x)+Phi(-x) = 1
+    assert abs(oracle.gelu(20.0) - 20.0) < 1e-12 and abs(oracle.gelu(-20.0)) < 1e-12
+
+
+def test_epilogue_order_and_broadcast():
+    """bias before GELU, residual after: 1 + 1 -> GELU(2) = 2 Phi(2), + 3.
+    Residual before GELU would give ~5, bias after GELU 4.84."""
+    R = np.array([[1.0]])
+    got = oracle.epilogue(R, np.array([1.0], np.float32), np.array([[3.0]], np.float32), True)
+    assert abs(got[0, 0] - (2 * 0.9772498680518208 + 3.0)) < 1e-14
+    # bias is per column, residual per element; bf16 bits are widened exactly
+    bias = inputs.fp32_to_bf16_bits(np.array([1.0, 2.0, 3.0], np.float32))
+    res = inputs.fp32_to_bf16_bits(np.array([[0.5, 0.0, 0.0], [0.0, 0.0, -0.25]], np.float32))
+    got = oracle.epilogue(np.zeros((2, 3)), bias, res)
+    assert np.array_equal(got, [[1.5, 2.0, 3.0], [1.0, 2.0, 2.75]])
+    assert np.array_equal(oracle.epilogue(np.ones((2, 2))), np.ones((2, 2)))
+
+
+def test_round_to_bf16_ties_to_even():
+    """bf16 keeps 8 significant bits: on [256, 512) neighbours are 2 apart,
+    on [1, 2) 2^-7 apart. Halfway cases go to the even neighbour."""
+    got = oracle.round_to_bf16([257.0, 259.0, 1 + 2 ** -8, 1 + 3 * 2 ** -9, 1 + 2 ** -7,
+                                -257.0, 0.0, 256.0])
+    assert [int(v) for v in got] == [0x4380, 0x4382, 0x3F80, 0x3F81, 0x3F81, 0xC380, 0x0000,
+                                     0x4380]
+    with pytest.raises(ValueError):
+        oracle.round_to_bf16([0.1])  # not an fp32 value

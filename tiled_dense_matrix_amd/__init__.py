@@ -6,17 +6,20 @@ binding over that ABI; the submodule ``inputs`` holds the seeded synthetic
 input generator used by tests and the benchmark.
 """
 from ._lib import (  # noqa: F401
+    DType,
     Kind,
     Path,
     Roofline,
     Status,
     TdmError,
+    gemm_bf16_epilogue,
     gemm_bf16_f32acc,
     gemm_f32,
     gemm_roofline,
     load,
     path_name,
     status_string,
+    tdm_gemm_bf16_epilogue_path,
     tdm_gemm_bf16_f32acc_path,
     tdm_gemm_f32_path,
     tdm_path_supports,

@@ -38,6 +38,11 @@ SIGNATURES = {
     "tdm_select_path": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64]),
     "tdm_path_name": (ctypes.c_char_p, [ctypes.c_int]),
     "tdm_version": (ctypes.c_int, []),
+    "gemm_bf16_epilogue": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p, ctypes.c_int,
+                                          _i64, _i64, _i64, _p]),
+    "tdm_gemm_bf16_epilogue_path": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p,
+                                                   ctypes.c_int, _i64, _i64, _i64,
+                                                   ctypes.c_int, _p]),
 }
 
 
@@ -60,6 +65,11 @@ class Path(enum.IntEnum):
     VALU = 2
     MFMA = 3
     SKINNY = 4
+
+
+class DType(enum.IntEnum):
+    F32 = 0
+    BF16 = 1
 
 
 class TdmError(RuntimeError):
@@ -211,6 +221,73 @@ def tdm_gemm_f32_path(A, B, C=None, path=Path.AUTO, stream=None):
 def tdm_gemm_bf16_f32acc_path(A, B, C=None, path=Path.AUTO, stream=None):
     M, N, K, C = _prep(A, B, C, _bf16_dtypes())
     return _call("tdm_gemm_bf16_f32acc_path", A, B, C, M, N, K, stream, path)
+
+
+def _epilogue_args(A, B, D, out_dtype, bias, residual):
+    """Check the epilogue operands; returns (M, N, K, D, DType)."""
+    torch = _torch()
+    bf16 = _bf16_dtypes()
+    _check_matrix("A", A, bf16)
+    M, K = A.shape
+    _check_matrix("B", B, bf16, rows=K)
+    N = B.shape[1]
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    if D is None:
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    dt = DType.F32 if D.dtype == torch.float32 else DType.BF16
+    same = (torch.float32,) if dt == DType.F32 else bf16
+    _check_matrix("D", D, same, rows=M, cols=N)
+    if D.device != A.device:
+        raise ValueError("D is on another device than A and B")
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.dim() != 1 or bias.shape[0] != N:
+            raise ValueError(f"bias must be a 1-D tensor of {N} elements")
+        if bias.dtype not in same or not bias.is_cuda or not bias.is_contiguous() \
+                or bias.device != A.device:
+            raise ValueError("bias must be a contiguous tensor of D's element type on A's device")
+    if residual is not None:
+        _check_matrix("residual", residual, same, rows=M, cols=N)
+        if residual.device != A.device:
+            raise ValueError("residual is on another device than A and B")
+    return M, N, K, D, dt
+
+
+def _call_epilogue(fname, A, B, D, dt, bias, residual, gelu, M, N, K, stream, path=None):
+    torch = _torch()
+    fn = getattr(load(), fname)
+    with torch.cuda.device(A.device):
+        args = [A.data_ptr() or None, B.data_ptr() or None, D.data_ptr() or None, int(dt),
+                None if bias is None else bias.data_ptr(),
+                None if residual is None else residual.data_ptr(),
+                1 if gelu else 0, M, N, K]
+        if path is not None:
+            args.append(int(path))
+        args.append(_stream_handle(stream))
+        st = fn(*args)
+    if st != Status.SUCCESS:
+        raise TdmError(st, fname)
+    return D
+
+
+def gemm_bf16_epilogue(A, B, D=None, out_dtype=None, bias=None, residual=None, gelu=False,
+                       stream=None):
+    """D = epilogue(A @ B) for bf16 A, B: + bias[j], then GELU (exact, erf), then
+    + residual[i, j], stored as D's dtype (torch.float32 or bf16). Without D, a
+    new tensor of out_dtype (default torch.bfloat16) is returned."""
+    torch = _torch()
+    M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual)
+    return _call_epilogue("gemm_bf16_epilogue", A, B, D, dt, bias, residual, gelu, M, N, K, stream)
+
+
+def tdm_gemm_bf16_epilogue_path(A, B, D=None, out_dtype=None, bias=None, residual=None,
+                                gelu=False, path=Path.AUTO, stream=None):
+    torch = _torch()
+    M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual)
+    return _call_epilogue("tdm_gemm_bf16_epilogue_path", A, B, D, dt, bias, residual, gelu,
+                          M, N, K, stream, path)
 
 
 def _bf16_dtypes():

@@ -26,10 +26,12 @@ __device__ __forceinline__ float to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-template <typename T>
+// kEpi: finish each output with the fused epilogue and write it to C as the
+// epilogue's type says (C is then the epilogue's D); else store the fp32 sum.
+template <typename T, bool kEpi>
 __global__ __launch_bounds__(kThreads) void edge_kernel(
-    const T* __restrict__ A, const T* __restrict__ B, float* __restrict__ C,
-    int M, int N, int K, int tiles_n) {
+    const T* __restrict__ A, const T* __restrict__ B, void* C,
+    int M, int N, int K, int tiles_n, Epilogue epi) {
   __shared__ float As[kT][kT + 1];
   __shared__ float Bs[kT][kT + 1];
 
@@ -72,10 +74,18 @@ __global__ __launch_bounds__(kThreads) void edge_kernel(
 
   const int r0 = m0 + ty, r1 = m0 + ty + 16;
   const int c0 = n0 + tx, c1 = n0 + tx + 16;
-  if (r0 < M && c0 < N) C[static_cast<int64_t>(r0) * N + c0] = acc00;
-  if (r0 < M && c1 < N) C[static_cast<int64_t>(r0) * N + c1] = acc01;
-  if (r1 < M && c0 < N) C[static_cast<int64_t>(r1) * N + c0] = acc10;
-  if (r1 < M && c1 < N) C[static_cast<int64_t>(r1) * N + c1] = acc11;
+  auto put = [&](int r, int c, float v) {
+    if (r >= M || c >= N) return;
+    const int64_t idx = static_cast<int64_t>(r) * N + c;
+    if constexpr (kEpi)
+      epi_store(C, idx, c, v, epi);
+    else
+      static_cast<float*>(C)[idx] = v;
+  };
+  put(r0, c0, acc00);
+  put(r0, c1, acc01);
+  put(r1, c0, acc10);
+  put(r1, c1, acc11);
 }
 
 __global__ void fill_zero_kernel(float* __restrict__ C, int64_t count) {
@@ -85,15 +95,15 @@ __global__ void fill_zero_kernel(float* __restrict__ C, int64_t count) {
     C[i] = 0.f;
 }
 
-template <typename T>
-hipError_t launch_edge(const T* A, const T* B, float* C, int M, int N, int K,
+template <typename T, bool kEpi>
+hipError_t launch_edge(const T* A, const T* B, void* C, int M, int N, int K, const Epilogue& e,
                        hipStream_t s) {
   const int tiles_m = (M + kT - 1) / kT;
   const int tiles_n = (N + kT - 1) / kT;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  return launch(edge_kernel<T>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s, A, B,
-                C, M, N, K, tiles_n);
+  return launch(edge_kernel<T, kEpi>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s,
+                A, B, C, M, N, K, tiles_n, e);
 }
 
 }  // namespace
@@ -107,12 +117,17 @@ hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s) {
 
 hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s) {
-  return launch_edge<float>(A, B, C, M, N, K, s);
+  return launch_edge<float, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
 hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
-  return launch_edge<uint16_t>(A, B, C, M, N, K, s);
+  return launch_edge<uint16_t, false>(A, B, C, M, N, K, Epilogue{}, s);
+}
+
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                int K, const Epilogue& e, hipStream_t s) {
+  return launch_edge<uint16_t, true>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

@@ -18,7 +18,10 @@
 //     whose latency one step does not cover); one barrier per step;
 //   * the fragments of the next sub-step are read while the current one is
 //     multiplied, across the step boundary too: the first reads of step t+1
-//     follow the barrier and overlap the last MFMAs of step t.
+//     follow the barrier and overlap the last MFMAs of step t;
+//   * C is written through LDS in row-contiguous groups of four, where the
+//     optional fused epilogue (bias, GELU, residual, bf16 output; §4.3
+//     operator fusion) finishes each output.
 //
 // Operand layouts. MFMA wants, in every lane, eight consecutive K values of
 // one row of A and of one column of B.
@@ -47,6 +50,7 @@ namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -219,10 +223,12 @@ __device__ __forceinline__ void interleave_hint() {
   if (T::kReads > kPairs) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, T::kReads - kPairs, 0);
 }
 
+// C receives the sums finished by `epi` (epilogue.h), in the epilogue's
+// element type; an empty epilogue stores the fp32 sums themselves.
 template <class T>
 __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
-    float* __restrict__ C, int M, int N, int K, int tiles_m, int tiles_n) {
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C, int M, int N,
+    int K, int tiles_m, int tiles_n, Epilogue epi) {
   constexpr int S = T::kStages;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
@@ -319,35 +325,60 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
     cur = nxt;
   }
 
-  // Epilogue: element v of a 32 x 32 accumulator sits at
-  // row 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
-  const bool full = (m0 + T::BM <= M) && (n0 + T::BN <= N);
+  // Writing C. Each wave stages its block through its share of the (now
+  // idle) LDS ring, kPassRows rows at a time, then finishes the outputs in
+  // row-contiguous groups of four: one compact loop for the epilogue instead
+  // of one inlined per accumulator, coalesced residual reads, and 8- or
+  // 16-byte stores (measured faster than storing from the accumulators'
+  // layout even with no epilogue). Element v of a 32 x 32 accumulator sits
+  // at row 8*(v/4) + 4*(lane/32) + v%4, column lane%32.
+  {
+    constexpr int kWaveLds = T::kLdsBytes / T::kWaves;
+    constexpr int kPassFrags = kWaveLds / (32 * T::kWaveN * 4) < T::kFragM
+                                   ? kWaveLds / (32 * T::kWaveN * 4) : T::kFragM;
+    static_assert(kPassFrags >= 1 && T::kFragM % kPassFrags == 0, "epilogue staging");
+    constexpr int kPassRows = 32 * kPassFrags;
+    constexpr int kLanesPerRow = T::kWaveN / 4;
+    constexpr int kRowsPerIter = 64 / kLanesPerRow;
+    LDS_PTR(float) stage = (LDS_PTR(float))(lds + wave * kWaveLds);
+    const int c4 = (lane % kLanesPerRow) * 4;
+    const int col = n0 + wn * T::kWaveN + c4;
+    const f32x4 bias4 = epi_bias4(col, N, epi);  // this lane's columns never change
+    __syncthreads();  // every wave is done with the ring
 #pragma unroll
-  for (int i = 0; i < T::kFragM; ++i) {
+    for (int i0 = 0; i0 < T::kFragM; i0 += kPassFrags) {
 #pragma unroll
-    for (int j = 0; j < T::kFragN; ++j) {
-      const int col = n0 + wn * T::kWaveN + j * 32 + lr;
+      for (int i = 0; i < kPassFrags; ++i)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * T::kWaveM + i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3);
-        if (full || (row < M && col < N))
-          C[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
+        for (int j = 0; j < T::kFragN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            stage[(i * 32 + (v >> 2) * 8 + lg * 4 + (v & 3)) * T::kWaveN + j * 32 + lr] =
+                acc[i0 + i][j][v];
+      __syncthreads();
+#pragma unroll 4
+      for (int r = lane / kLanesPerRow; r < kPassRows; r += kRowsPerIter) {
+        const f32x4 t = *(LDS_PTR(const f32x4))(stage + r * T::kWaveN + c4);
+        const int row = m0 + wm * T::kWaveM + i0 * 32 + r;
+        if (row < M && col < N)
+          epi_store4(C, static_cast<int64_t>(row) * N + col, col, N, t, bias4, epi);
       }
+      __syncthreads();
     }
   }
 }
 
 template <class T>
-hipError_t launch_tile(const uint16_t* A, const uint16_t* B, float* C, int M, int N, int K,
-                       hipStream_t s) {
+hipError_t launch_tile(const uint16_t* A, const uint16_t* B, void* C, int M, int N, int K,
+                       const Epilogue& epi, hipStream_t s) {
   static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
   hipError_t e =
       allow_lds(lds_ok, reinterpret_cast<const void*>(mfma_bf16_kernel<T>), T::kLdsBytes);
   if (e != hipSuccess) return e;
   const int tiles_m = (M + T::BM - 1) / T::BM;
   const int tiles_n = (N + T::BN - 1) / T::BN;
-  return launch(mfma_bf16_kernel<T>, dim3(tiles_m * tiles_n), dim3(T::kThreads), T::kLdsBytes, s,
-                A, B, C, M, N, K, tiles_m, tiles_n);
+  return launch(mfma_bf16_kernel<T>, dim3(tiles_m * tiles_n), dim3(T::kThreads), T::kLdsBytes,
+                s, A, B, C, M, N, K, tiles_m, tiles_n, epi);
 }
 
 }  // namespace
@@ -366,9 +397,17 @@ using SmallTile = Cfg<128, 128, 2, 4, 32, 4>;
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
+  // The plain product goes through the staged store too, with no epilogue
+  // terms: its row-contiguous 16-byte stores write C faster than the
+  // accumulators' own layout does.
+  return launch_mfma_bf16_epi(A, B, C, M, N, K, Epilogue{}, s);
+}
+
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                int K, const Epilogue& e, hipStream_t s) {
   if (use_large_tiles(M, N, kLargeTileFillBf16))
-    return launch_tile<LargeTile>(A, B, C, M, N, K, s);
-  return launch_tile<SmallTile>(A, B, C, M, N, K, s);
+    return launch_tile<LargeTile>(A, B, D, M, N, K, e, s);
+  return launch_tile<SmallTile>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

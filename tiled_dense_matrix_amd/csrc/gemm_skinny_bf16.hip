@@ -229,8 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
   }
 
   // Element v of accumulator q: row 4*(lane/16) + v, column
-  // kColsPerWave*wave + 16q + lane%16.
-  if (slices == 1) {
+  // kColsPerWave*wave + 16q + lane%16. Without a partial-sum buffer (one
+  // slice, no epilogue) the sums are the outputs.
+  if (partials == nullptr) {
 #pragma unroll
     for (int q = 0; q < kAcc; ++q)
 #pragma unroll
@@ -250,10 +251,12 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
       mine[(4 * g + v) * kBlockN + wave * kColsPerWave + q * 16 + m] = acc[q][v];
 }
 
-// C[row][col] = sum over slices (in slice order) of the partials.
+// C[row][col] = sum over slices (in slice order) of the partials; with kEpi
+// the sum is finished by the fused epilogue (C is then the epilogue's D).
+template <bool kEpi>
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partials,
-                                                            float* __restrict__ C, int M, int N,
-                                                            int slices) {
+                                                            void* C, int M, int N, int slices,
+                                                            Epilogue epi) {
   constexpr int kGroups = kPer / 256;    // workgroups per column block
   const int block = blockIdx.x / kGroups;
   const int e = (blockIdx.x - block * kGroups) * 256 + threadIdx.x;
@@ -270,7 +273,11 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     for (int u = 0; u < 8; ++u) sum += v[u];
   }
   for (; s < slices; ++s) sum += p[s * kPer];
-  C[static_cast<int64_t>(row) * N + col] = sum;
+  const int64_t idx = static_cast<int64_t>(row) * N + col;
+  if constexpr (kEpi)
+    epi_store(C, idx, col, sum, epi);
+  else
+    static_cast<float*>(C)[idx] = sum;
 }
 
 // Workspace for the partial sums: one buffer per (device, stream), so calls
@@ -334,8 +341,11 @@ bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
          mis_b == 0;
 }
 
-hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
-                              int M, int N, int K, hipStream_t s) {
+namespace {
+
+template <bool kEpi>
+hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, int N, int K,
+                         const Epilogue& epi, hipStream_t s) {
   static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
   hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(skinny_bf16_kernel), kLdsBytes);
   if (e != hipSuccess) return e;
@@ -346,19 +356,32 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
   if (slices < 1) slices = 1;
   const int slice_steps = (steps + slices - 1) / slices;
   slices = (steps + slice_steps - 1) / slice_steps;  // no empty slices
-  float* partials = nullptr;
-  if (slices > 1) {
-    const size_t part_bytes =
-        static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
-    void* ws = nullptr;
-    if ((e = workspace(s, part_bytes, &ws)) != hipSuccess) return e;
-    partials = static_cast<float*>(ws);
-  }
-  e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B, C, M,
-             N, K, slices, slice_steps, partials);
-  if (e != hipSuccess || slices == 1) return e;
-  return launch(skinny_reduce_kernel, dim3(blocks * (kPer / 256)), dim3(256), 0, s, partials,
-                C, M, N, slices);
+  if (slices == 1 && !kEpi)  // the sums are the outputs: no workspace
+    return launch(skinny_bf16_kernel, dim3(blocks), dim3(kThreads), kLdsBytes, s, A, B,
+                  static_cast<float*>(C), M, N, K, slices, slice_steps,
+                  static_cast<float*>(nullptr));
+  const size_t part_bytes =
+      static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
+  void* ws = nullptr;
+  if ((e = workspace(s, part_bytes, &ws)) != hipSuccess) return e;
+  float* partials = static_cast<float*>(ws);
+  e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B,
+             static_cast<float*>(nullptr), M, N, K, slices, slice_steps, partials);
+  if (e != hipSuccess) return e;
+  return launch(skinny_reduce_kernel<kEpi>, dim3(blocks * (kPer / 256)), dim3(256), 0, s,
+                partials, C, M, N, slices, epi);
+}
+
+}  // namespace
+
+hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
+                              int M, int N, int K, hipStream_t s) {
+  return launch_skinny<false>(A, B, C, M, N, K, Epilogue{}, s);
+}
+
+hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                  int K, const Epilogue& e, hipStream_t s) {
+  return launch_skinny<true>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

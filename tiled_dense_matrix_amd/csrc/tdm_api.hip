@@ -156,6 +156,50 @@ bool valid_path(tdm_path p) {
          p == TDM_PATH_MFMA || p == TDM_PATH_SKINNY;
 }
 
+// D = epilogue(A * B) for bf16 inputs (include/tdm.h).
+tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype d_type,
+                        const void* bias, const void* residual, int gelu, int64_t M, int64_t N,
+                        int64_t K, tdm_path path, void* stream) {
+  if (d_type != TDM_DTYPE_F32 && d_type != TDM_DTYPE_BF16) return TDM_ERROR_INVALID_VALUE;
+  const uint64_t dsize = d_type == TDM_DTYPE_BF16 ? 2 : 4;
+  if (M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return TDM_SUCCESS;
+  if (D == nullptr) return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && (A == nullptr || B == nullptr)) return TDM_ERROR_INVALID_VALUE;
+  auto aligned = [](const void* p, uint64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+  if (!aligned(D, dsize) || !aligned(bias, dsize) || !aligned(residual, dsize))
+    return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && (!aligned(A, 2) || !aligned(B, 2))) return TDM_ERROR_INVALID_VALUE;
+  if (too_big(M, N, K)) return TDM_ERROR_NOT_SUPPORTED;
+  const uint64_t d_bytes = uint64_t(M) * uint64_t(N) * dsize;
+  if (K > 0 && (overlaps(D, d_bytes, A, uint64_t(M) * uint64_t(K) * 2) ||
+                overlaps(D, d_bytes, B, uint64_t(K) * uint64_t(N) * 2)))
+    return TDM_ERROR_INVALID_VALUE;
+  if (bias != nullptr && overlaps(D, d_bytes, bias, uint64_t(N) * dsize))
+    return TDM_ERROR_INVALID_VALUE;
+  if (residual != nullptr && residual != D && overlaps(D, d_bytes, residual, d_bytes))
+    return TDM_ERROR_INVALID_VALUE;
+  const int ma = misalign(A), mb = misalign(B);
+  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, 0))
+    return TDM_ERROR_NOT_SUPPORTED;
+  tdm_status st = check_device();
+  if (st != TDM_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tdm::Epilogue e;
+  e.bias = bias;
+  e.residual = residual;
+  e.gelu = gelu != 0;
+  e.d_bf16 = d_type == TDM_DTYPE_BF16;
+  const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+  if (K == 0) return to_status(tdm::launch_edge_bf16_epi(A, B, D, m, n, 0, e, s));
+  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, 0);
+  switch (path) {
+    case TDM_PATH_MFMA: return to_status(tdm::launch_mfma_bf16_epi(A, B, D, m, n, k, e, s));
+    case TDM_PATH_SKINNY: return to_status(tdm::launch_skinny_bf16_epi(A, B, D, m, n, k, e, s));
+    default: return to_status(tdm::launch_edge_bf16_epi(A, B, D, m, n, k, e, s));
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -181,6 +225,20 @@ tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B, float
                                      void* stream) {
   if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
   return run_bf16(A, B, C, M, N, K, path, stream);
+}
+
+tdm_status gemm_bf16_epilogue(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype d_type,
+                              const void* bias, const void* residual, int gelu, int64_t M,
+                              int64_t N, int64_t K, void* stream) {
+  return run_bf16_epi(A, B, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO, stream);
+}
+
+tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, void* D,
+                                       tdm_dtype d_type, const void* bias, const void* residual,
+                                       int gelu, int64_t M, int64_t N, int64_t K, tdm_path path,
+                                       void* stream) {
+  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  return run_bf16_epi(A, B, D, d_type, bias, residual, gelu, M, N, K, path, stream);
 }
 
 tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roofline* out) {

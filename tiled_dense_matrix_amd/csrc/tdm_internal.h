@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "epilogue.h"
+
 #include <atomic>
 #include <tuple>
 #include <utility>
@@ -102,5 +104,14 @@ hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s);
+
+// The bf16 products with the fused epilogue of epilogue.h, written to D (fp32
+// or bf16 as e.d_bf16 says). K may be 0 on the edge kernel (D = epilogue(0)).
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                  int K, const Epilogue& e, hipStream_t s);
 
 }  // namespace tdm

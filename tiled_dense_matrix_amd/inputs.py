@@ -12,6 +12,8 @@ seed; A is drawn first, row-major, then B):
 * bf16 workloads: i.i.d. normal(0, sigma) drawn in float64 (sigma is a
   standard deviation), rounded to fp32 and then to bf16, both
   round-to-nearest-even.
+* a fused-epilogue workload's bias: normal(0, bias_sigma) from its own
+  generator, seeded with (seed, 1), in the output's element type.
 
 The bf16 format is the upper half of an IEEE fp32 word (1 sign, 8 exponent,
 7 mantissa bits), as the CS336 Lecture 5 GPU notes describe in §3.1 (table of
@@ -33,6 +35,7 @@ __all__ = [
     "fp32_to_bf16_bits",
     "bf16_bits_to_fp32",
     "make_inputs",
+    "make_bias",
     "uniform_fp32",
     "normal_bf16",
     "small_int_matrix",
@@ -55,6 +58,15 @@ class Workload:
     dist: str  # "uniform" (fp32 workloads) or "normal" (bf16 workloads)
     sigma_a: float = 1.0
     sigma_b: float = 1.0
+    # Fused epilogue (bf16 workloads): bias of this standard deviation (0: no
+    # bias), GELU, and the output's element type ("f32" or "bf16").
+    bias_sigma: float = 0.0
+    gelu: bool = False
+    out: str = "f32"
+
+    @property
+    def has_epilogue(self) -> bool:
+        return self.bias_sigma > 0 or self.gelu or self.out != "f32"
 
 
 # The workloads, with their sizes, seeds and value distributions.
@@ -66,6 +78,10 @@ WORKLOADS = {
         Workload("bf16_4096", "bf16", 4096, 4096, 4096, 2, "normal"),
         Workload("bf16_8192", "bf16", 8192, 8192, 8192, 2, "normal"),
         Workload("bf16_mlp", "bf16", 8192, 14336, 4096, 3, "normal", 1.0, 0.02),
+        # The same product as the MLP up-projection above, finished in the
+        # kernel: + bias, GELU, bf16 output.
+        Workload("bf16_mlp_gelu", "bf16", 8192, 14336, 4096, 3, "normal", 1.0, 0.02,
+                 bias_sigma=0.02, gelu=True, out="bf16"),
         Workload("bf16_skinny", "bf16", 16, 8192, 8192, 4, "normal", 1.0, 0.02),
     )
 }
@@ -121,6 +137,17 @@ def make_inputs(w: Workload | str):
     else:
         raise ValueError(w.kind)
     return A, B
+
+
+def make_bias(w: Workload | str) -> np.ndarray:
+    """The bias of an epilogue workload: N values normal(0, bias_sigma) from a
+    PCG64 generator seeded with (seed, 1) (independent of A and B), in the
+    output's element type (fp32, or bf16 bits rounded to nearest even)."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    rng = np.random.default_rng((w.seed, 1))
+    x = (rng.standard_normal(w.N) * w.bias_sigma).astype(np.float32)
+    return fp32_to_bf16_bits(x) if w.out == "bf16" else x
 
 
 def small_int_matrix(rng: np.random.Generator, shape, lo: int = -3, hi: int = 3,
