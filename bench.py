@@ -83,6 +83,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-unfused", action="store_true",
+                    help="epilogue workloads: skip timing the unfused steps (for profiler runs, "
+                         "whose kernel statistics would mix both)")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.mm (PyTorch's ROCm BLAS) on the same resident inputs "
                          "and report it under vendor_blas, for context")
@@ -284,7 +287,7 @@ def main():
     # The same epilogue unfused: this library's product with fp32 output, then
     # the bias add, GELU and bf16 conversion as separate torch operations.
     unfused = None
-    if epi:
+    if epi and not args.no_unfused:
         cf = torch.empty((w.M, w.N), dtype=torch.float32, device="cuda")
         bias_f = None if bias_d is None else \
             (bias_d.view(torch.bfloat16).float() if out_bf16 else bias_d)
