@@ -61,6 +61,7 @@ KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launc
     "mfma_f32": ("mfma_f32_kernel", "gemm_mfma_f32.hip", ["mfma_f32_kernel"]),
     "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip",
                ["skinny_bf16_kernel", "skinny_reduce_kernel"]),
+    "skinny_nk": ("skinny_nk_bf16_kernel", "gemm_skinny_nk_bf16.hip", ["skinny_nk_bf16_kernel"]),
 }
 DEFAULT_WORKLOAD = "f32_4096"
 # The path each workload is specified on when --path is not given: the square
@@ -189,9 +190,13 @@ def main():
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
     pname_arg = args.path or DEFAULT_PATH.get(w.name, "auto")
     path = tdm.Path[pname_arg.upper()]
-    chosen = tdm.tdm_select_path(kind, w.M, w.N, w.K) if path == tdm.Path.AUTO else path
+    nk = w.b_layout == "nk"  # B stored N x K: C = A @ B.T
+    layout = tdm.Layout.NK if nk else tdm.Layout.KN
+    chosen = tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K) if path == tdm.Path.AUTO \
+        else path
     pname = tdm.path_name(chosen)
-    kernel, ksrc, kernels = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else pname]
+    kernel, ksrc, kernels = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else
+                                   "skinny_nk" if (pname == "skinny" and nk) else pname]
 
     A, B = inputs.make_inputs(w)
 
@@ -222,9 +227,9 @@ def main():
 
     def call(i, p):
         a, b, c = sets[i % rot]
-        if epi:
-            tdm.tdm_gemm_bf16_epilogue_path(a, b, c, bias=bias_d, gelu=w.gelu, path=p,
-                                            stream=stream)
+        if epi or nk:
+            tdm.tdm_gemm_bf16_ex_path(a, b, layout, c, bias=bias_d, gelu=w.gelu, path=p,
+                                      stream=stream)
         else:
             fn(a, b, c, path=p, stream=stream)
 
@@ -274,7 +279,7 @@ def main():
 
     # When the workload is specified on another path than the one gemm_* would
     # pick, time the library's own choice too (after the main measurement).
-    auto_choice = tdm.path_name(tdm.tdm_select_path(kind, w.M, w.N, w.K))
+    auto_choice = tdm.path_name(tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K))
     auto_info = None
     if path != tdm.Path.AUTO and auto_choice != pname:
         ms_auto = timed(tdm.Path.AUTO)
@@ -294,7 +299,7 @@ def main():
 
         def unfused_step(i):
             a, b, c = sets[i % rot]
-            fn(a, b, cf, path=path, stream=stream)
+            tdm.tdm_gemm_bf16_ex_path(a, b, layout, cf, path=path, stream=stream)
             t = cf if bias_f is None else cf + bias_f
             if w.gelu:
                 t = torch.nn.functional.gelu(t)
@@ -317,17 +322,25 @@ def main():
         else:
             vsets = [(a.view(torch.bfloat16), b.view(torch.bfloat16)) for a, b, _ in sets]
             if not epi:
-                vmm = lambda a, b: torch.mm(a, b, out_dtype=torch.float32)  # noqa: E731
-                vop = "torch.mm (out_dtype=float32)"
+                if nk:  # a 2-D product with the weight's transposed view (not batched)
+                    vmm = lambda a, b: torch.mm(a, b.t(), out_dtype=torch.float32)  # noqa: E731
+                    vop = "torch.mm with B.t() (out_dtype=float32)"
+                else:
+                    vmm = lambda a, b: torch.mm(a, b, out_dtype=torch.float32)  # noqa: E731
+                    vop = "torch.mm (out_dtype=float32)"
             else:
                 if not out_bf16:
                     raise SystemExit("--vendor covers epilogue workloads with bf16 output")
                 bias_v = None if bias_d is None else bias_d.view(torch.bfloat16)
 
                 def vmm(a, b):
-                    t = torch.mm(a, b) if bias_v is None else torch.addmm(bias_v, a, b)
+                    if nk:
+                        t = torch.nn.functional.linear(a, b, bias_v)
+                    else:
+                        t = torch.mm(a, b) if bias_v is None else torch.addmm(bias_v, a, b)
                     return torch.nn.functional.gelu(t) if w.gelu else t
-                vop = "torch.addmm (bf16 out), then GELU"
+                vop = ("torch.nn.functional.linear" if nk else "torch.addmm") + \
+                    " (bf16 out), then GELU"
         ms_v = time_steps(lambda i: vmm(*vsets[i % rot]))
         vendor = {"op": vop, "ms_per_call": round(ms_v, 6),
                   "tflops": round(roof.flops / (ms_v * 1e-3) / 1e12, 3),
@@ -351,6 +364,7 @@ def main():
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
                    "rotated_copies": rot,
                    "auto_path": auto_info,
+                   "b_layout": w.b_layout,
                    "epilogue": None if not epi else {"bias": bias_np is not None,
                                                      "gelu": w.gelu, "out": w.out},
                    "unfused": unfused,
@@ -367,7 +381,8 @@ def main():
     if vendor is not None:
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, A, B, C_gpu, args.cpu_seconds, bias_np)
+        B_kn = np.ascontiguousarray(B.T) if nk else B  # the oracle takes B as K x N
+        line["cpu_baseline"] = cpu_baseline(w, A, B_kn, C_gpu, args.cpu_seconds, bias_np)
     print(json.dumps(line), flush=True)
 
 

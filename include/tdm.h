@@ -146,6 +146,39 @@ TDM_API tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t
                                                int64_t N, int64_t K, tdm_path path,
                                                void* stream);
 
+/* How B is stored (NEXT-2 of the scope: transposed operands). */
+typedef enum tdm_layout {
+  TDM_LAYOUT_KN = 0,  /* B is K x N, row-major: C = A * B (every gemm_* call)  */
+  TDM_LAYOUT_NK = 1   /* B is N x K, row-major -- a linear layer's weight, as a
+                         PyTorch Linear stores it: C = A * B^T, i.e.
+                         C[i,j] = sum_k A[i,k] * B[j,k]                        */
+} tdm_layout;
+
+/* gemm_bf16_epilogue with B in either layout: D = epilogue(A * op(B)), op(B)
+ * = B for TDM_LAYOUT_KN and B^T for TDM_LAYOUT_NK (CS336 Lecture 5 GPU notes,
+ * review question 5 and the §4.1 warning on transposed views: a transposed
+ * operand is a different memory layout, not a free view). Everything else
+ * -- the epilogue, D, bias, residual, errors -- as gemm_bf16_epilogue;
+ * TDM_ERROR_INVALID_VALUE for an unknown layout. With no bias, residual or
+ * GELU and d_type TDM_DTYPE_F32 this is the plain product. */
+TDM_API tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+                                void* D, tdm_dtype d_type, const void* bias,
+                                const void* residual, int gelu, int64_t M, int64_t N, int64_t K,
+                                void* stream);
+TDM_API tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B,
+                                         tdm_layout b_layout, void* D, tdm_dtype d_type,
+                                         const void* bias, const void* residual, int gelu,
+                                         int64_t M, int64_t N, int64_t K, tdm_path path,
+                                         void* stream);
+
+/* Host-only: tdm_path_supports / tdm_select_path for a given layout of B
+ * (TDM_LAYOUT_NK: bf16 only; 0 / TDM_PATH_EDGE for an unknown layout). */
+TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path path, int64_t M,
+                                 int64_t N, int64_t K, int misalign_a, int misalign_b,
+                                 int misalign_c);
+TDM_API tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout b_layout, int64_t M, int64_t N,
+                                    int64_t K);
+
 /* Host-only cost query; touches no device. FLOPs = 2MNK (a multiply-add is
  * two operations) and bytes = reading A and B once and writing C once
  * (compute- vs memory-bound lesson, counting a matrix multiply; CS336

@@ -28,6 +28,11 @@ What it computes, and the passage each function follows:
   residual[i, j], in that order (CS336 Lecture 5 GPU notes, §4.3, operator
   fusion; LLM course ch. 15, the GELU-then-residual-add example). The pages
   name GELU without a formula; this is its exact (erf) form.
+* ``gemm_nt`` / ``gemm_nt_tiles`` -- the product with B stored N x K (a
+  linear layer's weight): C[i,j] = sum_k A[i,k] B[j,k], i.e. A times the
+  transpose of the stored matrix (CS336 Lecture 5 GPU notes, review question
+  5: op(A) in BLAS terms; §4.1: a transposed view is another memory layout).
+  The stored matrix is transposed into K x N order and handed to ``gemm``.
 * ``round_to_bf16`` -- bf16 bits of fp64 values that fp32 holds exactly,
   rounded to nearest with ties to even (CS336 Lecture 5 GPU notes, §3.1 on
   bf16 as the upper half of an fp32 word).
@@ -135,6 +140,22 @@ def gemm_tiles(A: np.ndarray, B: np.ndarray, tiles, tile: int = 32,
     M, N = A.shape[0], B.shape[1]
     return [gemm_block(A, B, (r, min(r + tile, M)), (c, min(c + tile, N)), threads)
             for r, c in tiles]
+
+
+def gemm_nt(A: np.ndarray, Bt: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """fp64 A @ Bt.T for Bt[N, K] (C[i,j] = sum_k A[i,k] Bt[j,k])."""
+    return gemm(A, np.ascontiguousarray(np.asarray(Bt).T), threads)
+
+
+def gemm_nt_tiles(A: np.ndarray, Bt: np.ndarray, tiles, tile: int = 32,
+                  threads: int | None = None) -> list[np.ndarray]:
+    """fp64 tiles of A @ Bt.T at the given (row0, col0) corners."""
+    out = []
+    for r, c in tiles:
+        c1 = min(c + tile, Bt.shape[0])
+        B = np.ascontiguousarray(np.asarray(Bt)[c:c1].T)
+        out.append(gemm_block(A, B, (r, min(r + tile, A.shape[0])), (0, c1 - c), threads))
+    return out
 
 
 def widen(X: np.ndarray) -> np.ndarray:

@@ -434,3 +434,34 @@ def test_round_to_bf16_ties_to_even():
                                      0x4380]
     with pytest.raises(ValueError):
         oracle.round_to_bf16([0.1])  # not an fp32 value
+
+
+# ---------------------------------------------------------------------------
+# B stored N x K (a linear layer's weight): C = A B^T.
+# ---------------------------------------------------------------------------
+
+def test_gemm_nt_hand_values_and_shape():
+    """C[i,j] = sum_k A[i,k] Bt[j,k] worked by hand for a 2x3 A and 4x3 Bt;
+    reading Bt as K x N would not even have matching shapes."""
+    A = np.array([[1, 2, 3], [4, 5, 6]], np.float32)
+    Bt = np.array([[1, 0, -1], [2, 1, 0], [0, 0, 1], [1, 1, 1]], np.float32)
+    C = oracle.gemm_nt(A, Bt)
+    assert C.shape == (2, 4)
+    assert np.array_equal(C, [[-2, 4, 3, 6], [-2, 13, 6, 15]])
+    for a, b in ((A, Bt), (inputs.fp32_to_bf16_bits(A), inputs.fp32_to_bf16_bits(Bt))):
+        assert np.array_equal(oracle.gemm_nt(a, b), C)
+
+
+def test_gemm_nt_of_a_matrix_with_itself_is_its_gram_matrix():
+    """A A^T is symmetric with the squared row norms on the diagonal (exact
+    for small integers); the tile helper agrees with the full product."""
+    rng = np.random.default_rng(12)
+    A = rng.integers(-3, 4, size=(37, 53)).astype(np.float32)
+    G = oracle.gemm_nt(A, A)
+    assert np.array_equal(G, G.T)
+    assert np.array_equal(np.diag(G), (A.astype(np.float64) ** 2).sum(axis=1))
+    Bt = rng.integers(-3, 4, size=(70, 53)).astype(np.float32)
+    full = oracle.gemm_nt(A, Bt)
+    tiles = [(0, 0), (32, 32), (5, 64)]
+    for (r, c), T in zip(tiles, oracle.gemm_nt_tiles(A, Bt, tiles, 32)):
+        assert np.array_equal(T, full[r:r + 32, c:c + 32])

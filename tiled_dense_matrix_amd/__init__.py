@@ -8,11 +8,13 @@ input generator used by tests and the benchmark.
 from ._lib import (  # noqa: F401
     DType,
     Kind,
+    Layout,
     Path,
     Roofline,
     Status,
     TdmError,
     gemm_bf16_epilogue,
+    gemm_bf16_ex,
     gemm_bf16_f32acc,
     gemm_f32,
     gemm_roofline,
@@ -20,9 +22,12 @@ from ._lib import (  # noqa: F401
     path_name,
     status_string,
     tdm_gemm_bf16_epilogue_path,
+    tdm_gemm_bf16_ex_path,
     tdm_gemm_bf16_f32acc_path,
     tdm_gemm_f32_path,
     tdm_path_supports,
+    tdm_path_supports_ex,
     tdm_select_path,
+    tdm_select_path_ex,
     version,
 )

@@ -43,6 +43,14 @@ SIGNATURES = {
     "tdm_gemm_bf16_epilogue_path": (ctypes.c_int, [_p, _p, _p, ctypes.c_int, _p, _p,
                                                    ctypes.c_int, _i64, _i64, _i64,
                                                    ctypes.c_int, _p]),
+    "gemm_bf16_ex": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _p,
+                                    ctypes.c_int, _i64, _i64, _i64, _p]),
+    "tdm_gemm_bf16_ex_path": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _p,
+                                             ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p]),
+    "tdm_path_supports_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64,
+                                            _i64, _i64, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_int]),
+    "tdm_select_path_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64]),
 }
 
 
@@ -65,6 +73,13 @@ class Path(enum.IntEnum):
     VALU = 2
     MFMA = 3
     SKINNY = 4
+
+
+class Layout(enum.IntEnum):
+    """How B is stored: KN = K x N (C = A @ B); NK = N x K, a linear layer's
+    weight (C = A @ B.T)."""
+    KN = 0
+    NK = 1
 
 
 class DType(enum.IntEnum):
@@ -223,14 +238,18 @@ def tdm_gemm_bf16_f32acc_path(A, B, C=None, path=Path.AUTO, stream=None):
     return _call("tdm_gemm_bf16_f32acc_path", A, B, C, M, N, K, stream, path)
 
 
-def _epilogue_args(A, B, D, out_dtype, bias, residual):
+def _epilogue_args(A, B, D, out_dtype, bias, residual, layout=Layout.KN):
     """Check the epilogue operands; returns (M, N, K, D, DType)."""
     torch = _torch()
     bf16 = _bf16_dtypes()
     _check_matrix("A", A, bf16)
     M, K = A.shape
-    _check_matrix("B", B, bf16, rows=K)
-    N = B.shape[1]
+    if Layout(layout) == Layout.NK:
+        _check_matrix("B", B, bf16, cols=K)
+        N = B.shape[0]
+    else:
+        _check_matrix("B", B, bf16, rows=K)
+        N = B.shape[1]
     if A.device != B.device:
         raise ValueError("A and B are on different devices")
     if D is None:
@@ -288,6 +307,51 @@ def tdm_gemm_bf16_epilogue_path(A, B, D=None, out_dtype=None, bias=None, residua
     M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual)
     return _call_epilogue("tdm_gemm_bf16_epilogue_path", A, B, D, dt, bias, residual, gelu,
                           M, N, K, stream, path)
+
+
+def gemm_bf16_ex(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None, residual=None,
+                 gelu=False, stream=None):
+    """D = epilogue(A @ op(B)) for bf16 A, B: op(B) = B for Layout.KN (B is
+    K x N), B.T for Layout.NK (B is N x K, like a torch Linear weight). The
+    epilogue is gemm_bf16_epilogue's; without D a new tensor of out_dtype
+    (default torch.bfloat16) is returned."""
+    torch = _torch()
+    M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual, layout)
+    return _call_ex("gemm_bf16_ex", A, B, layout, D, dt, bias, residual, gelu, M, N, K, stream)
+
+
+def tdm_gemm_bf16_ex_path(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None,
+                          residual=None, gelu=False, path=Path.AUTO, stream=None):
+    torch = _torch()
+    M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual, layout)
+    return _call_ex("tdm_gemm_bf16_ex_path", A, B, layout, D, dt, bias, residual, gelu, M, N, K,
+                    stream, path)
+
+
+def _call_ex(fname, A, B, layout, D, dt, bias, residual, gelu, M, N, K, stream, path=None):
+    torch = _torch()
+    fn = getattr(load(), fname)
+    with torch.cuda.device(A.device):
+        args = [A.data_ptr() or None, B.data_ptr() or None, int(layout), D.data_ptr() or None,
+                int(dt), None if bias is None else bias.data_ptr(),
+                None if residual is None else residual.data_ptr(), 1 if gelu else 0, M, N, K]
+        if path is not None:
+            args.append(int(path))
+        args.append(_stream_handle(stream))
+        st = fn(*args)
+    if st != Status.SUCCESS:
+        raise TdmError(st, fname)
+    return D
+
+
+def tdm_path_supports_ex(kind: int, layout: int, path: int, M: int, N: int, K: int,
+                         misalign_a: int = 0, misalign_b: int = 0, misalign_c: int = 0) -> bool:
+    return bool(load().tdm_path_supports_ex(int(kind), int(layout), int(path), M, N, K,
+                                            misalign_a, misalign_b, misalign_c))
+
+
+def tdm_select_path_ex(kind: int, layout: int, M: int, N: int, K: int) -> Path:
+    return Path(load().tdm_select_path_ex(int(kind), int(layout), M, N, K))
 
 
 def _bf16_dtypes():

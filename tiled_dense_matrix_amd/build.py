@@ -28,6 +28,7 @@ SOURCES = [
     "gemm_mfma_bf16.hip",
     "gemm_mfma_f32.hip",
     "gemm_skinny_bf16.hip",
+    "gemm_skinny_nk_bf16.hip",
 ]
 
 # Packed fp32 instructions are switched off for all device code: the kernels

@@ -28,7 +28,8 @@ __device__ __forceinline__ float to_f32(uint16_t h) {
 
 // kEpi: finish each output with the fused epilogue and write it to C as the
 // epilogue's type says (C is then the epilogue's D); else store the fp32 sum.
-template <typename T, bool kEpi>
+// kBNK: B is stored N x K (C = A * B^T).
+template <typename T, bool kEpi, bool kBNK>
 __global__ __launch_bounds__(kThreads) void edge_kernel(
     const T* __restrict__ A, const T* __restrict__ B, void* C,
     int M, int N, int K, int tiles_n, Epilogue epi) {
@@ -55,9 +56,15 @@ __global__ __launch_bounds__(kThreads) void edge_kernel(
       const int am = m0 + r, ak = k0 + lc;
       As[r][lc] = (am < M && ak < K)
                       ? to_f32(A[static_cast<int64_t>(am) * K + ak]) : 0.f;
-      const int bk = k0 + r, bn = n0 + lc;
-      Bs[r][lc] = (bk < K && bn < N)
-                      ? to_f32(B[static_cast<int64_t>(bk) * N + bn]) : 0.f;
+      if constexpr (kBNK) {  // lanes along k (contiguous in B), stored transposed
+        const int bn = n0 + r, bk = k0 + lc;
+        Bs[lc][r] = (bk < K && bn < N)
+                        ? to_f32(B[static_cast<int64_t>(bn) * K + bk]) : 0.f;
+      } else {
+        const int bk = k0 + r, bn = n0 + lc;
+        Bs[r][lc] = (bk < K && bn < N)
+                        ? to_f32(B[static_cast<int64_t>(bk) * N + bn]) : 0.f;
+      }
     }
     __syncthreads();
 #pragma unroll 8
@@ -95,14 +102,14 @@ __global__ void fill_zero_kernel(float* __restrict__ C, int64_t count) {
     C[i] = 0.f;
 }
 
-template <typename T, bool kEpi>
+template <typename T, bool kEpi, bool kBNK>
 hipError_t launch_edge(const T* A, const T* B, void* C, int M, int N, int K, const Epilogue& e,
                        hipStream_t s) {
   const int tiles_m = (M + kT - 1) / kT;
   const int tiles_n = (N + kT - 1) / kT;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  return launch(edge_kernel<T, kEpi>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s,
+  return launch(edge_kernel<T, kEpi, kBNK>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s,
                 A, B, C, M, N, K, tiles_n, e);
 }
 
@@ -117,17 +124,18 @@ hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s) {
 
 hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s) {
-  return launch_edge<float, false>(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_edge<float, false, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
 hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
-  return launch_edge<uint16_t, false>(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_edge<uint16_t, false, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
-hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                int K, const Epilogue& e, hipStream_t s) {
-  return launch_edge<uint16_t, true>(A, B, D, M, N, K, e, s);
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                int M, int N, int K, const Epilogue& e, hipStream_t s) {
+  if (b_nk) return launch_edge<uint16_t, true, true>(A, B, D, M, N, K, e, s);
+  return launch_edge<uint16_t, true, false>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

@@ -60,18 +60,21 @@ constexpr int kGroupM = 8;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-// Tile geometry. Copies move 1 KB of LDS per wave instruction.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_>
+// Tile geometry. Copies move 1 KB of LDS per wave instruction. BNK_: B is
+// stored N x K (C = A * B^T, a linear layer's weight) and is then kept in LDS
+// like A, one K-contiguous row per column n; otherwise B is K x N.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool BNK_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
   static constexpr int kStages = STAGES_;
+  static constexpr bool kBNK = BNK_;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
   static constexpr int kRowA = BK * 2;                // bytes per LDS row of A
   static constexpr int kChunksA = BK / 8;             // 16-byte chunks per row of A
-  static constexpr int kRowB = BN * 2;                // bytes per LDS row of B
-  static constexpr int kChunksB = BN / 8;
+  static constexpr int kRowB = kBNK ? BK * 2 : BN * 2;  // bytes per LDS row of B
+  static constexpr int kChunksB = kRowB / 16;
   static constexpr int kStageA = BM * kRowA;
-  static constexpr int kStageB = BK * kRowB;
+  static constexpr int kStageB = BK * BN * 2;
   static constexpr int kStage = kStageA + kStageB;
   static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
@@ -82,13 +85,14 @@ struct Cfg {
   static constexpr int kRowsPerCopyA = 1024 / kRowA;
   static constexpr int kRowsPerCopyB = 1024 / kRowB;
   static constexpr int kSub = BK / 16;                // MFMA k-steps per K step
-  static constexpr int kReads = kFragM + 2 * kFragN;  // LDS reads per sub-step
+  static constexpr int kReads = kFragM + (kBNK ? 1 : 2) * kFragN;  // LDS reads per sub-step
   static constexpr int kMfmas = kFragM * kFragN;      // MFMAs per sub-step
   static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
                 "each wave copies whole 1 KB blocks");
   static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
                 "masked copy: whole 16-byte chunks per lane");
   static_assert(kChunksA == 4 || kChunksA == 8, "swizzle of A rows");
+  static_assert(!kBNK || kChunksB == kChunksA, "N x K rows of B like A's");
   static_assert(kSub % 2 == 0, "fragment double buffer alternates per sub-step");
   static_assert(kStages >= 2 && (kStages - 2) * kCopies <= 63, "vmcnt range");
   static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
@@ -130,9 +134,15 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
 #pragma unroll
   for (int j = 0; j < T::kCopyB; ++j) {  // B: blocks of kRowsPerCopyB rows
     const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kChunksB;
-    const int c = (lane % T::kChunksB) ^ swz_b(row);
-    const int gn = min(n0 + c * 8, N - 8);
-    p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + gn) * 2);
+    if constexpr (T::kBNK) {  // row = column n of the tile, chunk c = 8 k
+      const int c = (lane % T::kChunksB) ^ swz_a<T::kChunksB>(row);
+      const int gn = min(n0 + row, N - 1);
+      p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(gn) * K + c * 8) * 2);
+    } else {  // row = k of the step, chunk c = 8 columns
+      const int c = (lane % T::kChunksB) ^ swz_b(row);
+      const int gn = min(n0 + c * 8, N - 8);
+      p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + gn) * 2);
+    }
   }
   return p;
 }
@@ -143,7 +153,7 @@ __device__ __forceinline__ void copy_step_dma(const uint16_t* __restrict__ A,
                                               const uint16_t* __restrict__ B, int N, int k0,
                                               int wave, const CopyPlan<T>& p, uint32_t stage) {
   const uint16_t* a_base = A + k0;
-  const uint16_t* b_base = B + static_cast<int64_t>(k0) * N;
+  const uint16_t* b_base = T::kBNK ? B + k0 : B + static_cast<int64_t>(k0) * N;
 #pragma unroll
   for (int j = 0; j < T::kCopyA; ++j)
     dma16(a_base, p.a[j], stage + (wave * T::kCopyA + j) * 1024);
@@ -174,11 +184,18 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
   for (int i = 0; i < T::kStageB / 16 / T::kThreads; ++i) {  // B chunks
     const int id = tid + T::kThreads * i;
     const int row = id / T::kChunksB, c = id % T::kChunksB;
-    const int gk = k0 + row;
-    const int gn = min(n0 + c * 8, N - 8);
     u32x4 v = zero;
-    if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    *(LDS_PTR(u32x4))(sb + row * T::kRowB + ((c ^ swz_b(row)) << 4)) = v;
+    if constexpr (T::kBNK) {
+      const int gk = k0 + c * 8;
+      const int gn = min(n0 + row, N - 1);
+      if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gn) * K + gk);
+      *(LDS_PTR(u32x4))(sb + row * T::kRowB + ((c ^ swz_a<T::kChunksB>(row)) << 4)) = v;
+    } else {
+      const int gk = k0 + row;
+      const int gn = min(n0 + c * 8, N - 8);
+      if (gk < K) v = *reinterpret_cast<const u32x4*>(B + static_cast<int64_t>(gk) * N + gn);
+      *(LDS_PTR(u32x4))(sb + row * T::kRowB + ((c ^ swz_b(row)) << 4)) = v;
+    }
   }
 }
 
@@ -195,6 +212,12 @@ __device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int
 template <class T>
 __device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, int s,
                                          int lane) {
+  if constexpr (T::kBNK) {  // a K-contiguous row per column: read as A
+    const int row = n_base + (lane & 31), chunk = 2 * s + (lane >> 5);
+    const u32x4 v = *(LDS_PTR(const u32x4))(sb + row * T::kRowB +
+                                             ((chunk ^ swz_a<T::kChunksB>(row)) << 4));
+    return __builtin_bit_cast(bf16x8, v);
+  }
   const int g = lane >> 4, i = lane & 15;
   const int col = n_base + 16 * (g & 1) + 4 * (i & 3);
   const int c = col >> 3, half = (col & 7) << 1;
@@ -392,22 +415,36 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
          mis_b == 0;
 }
 
-using LargeTile = Cfg<256, 256, 2, 4, 32, 4>;
-using SmallTile = Cfg<128, 128, 2, 4, 32, 4>;
+bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
+                           int mis_c) {
+  (void)M;
+  (void)N;  // columns are rows of B: any count, clamped like the rows of A
+  (void)mis_c;
+  // Offsets gn*K*2 stay below 4 GiB because B has fewer than 2^31 elements.
+  return K % 8 == 0 && K >= 8 && mis_a == 0 && mis_b == 0;
+}
+
+template <bool BNK>
+using LargeTile = Cfg<256, 256, 2, 4, 32, 4, BNK>;
+template <bool BNK>
+using SmallTile = Cfg<128, 128, 2, 4, 32, 4, BNK>;
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
   // The plain product goes through the staged store too, with no epilogue
   // terms: its row-contiguous 16-byte stores write C faster than the
   // accumulators' own layout does.
-  return launch_mfma_bf16_epi(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_mfma_bf16_epi(A, B, false, C, M, N, K, Epilogue{}, s);
 }
 
-hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                int K, const Epilogue& e, hipStream_t s) {
-  if (use_large_tiles(M, N, kLargeTileFillBf16))
-    return launch_tile<LargeTile>(A, B, D, M, N, K, e, s);
-  return launch_tile<SmallTile>(A, B, D, M, N, K, e, s);
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                int M, int N, int K, const Epilogue& e, hipStream_t s) {
+  const bool large = use_large_tiles(M, N, kLargeTileFillBf16);
+  if (b_nk)
+    return large ? launch_tile<LargeTile<true>>(A, B, D, M, N, K, e, s)
+                 : launch_tile<SmallTile<true>>(A, B, D, M, N, K, e, s);
+  return large ? launch_tile<LargeTile<false>>(A, B, D, M, N, K, e, s)
+               : launch_tile<SmallTile<false>>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

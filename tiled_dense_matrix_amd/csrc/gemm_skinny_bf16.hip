@@ -379,8 +379,9 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
   return launch_skinny<false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
-hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                  int K, const Epilogue& e, hipStream_t s) {
+hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                  int M, int N, int K, const Epilogue& e, hipStream_t s) {
+  if (b_nk) return launch_skinny_nk_bf16(A, B, D, M, N, K, e, s);  // gemm_skinny_nk_bf16.hip
   return launch_skinny<true>(A, B, D, M, N, K, e, s);
 }
 

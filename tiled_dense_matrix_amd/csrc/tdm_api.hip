@@ -40,12 +40,14 @@ tdm_status check_device() {
   return TDM_SUCCESS;
 }
 
-// Shape/alignment admission of each path for one kind.
+// Shape/alignment admission of each path for one kind; b_nk: B is stored
+// N x K (bf16 only).
 bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
-              int ma, int mb, int mc) {
+              int ma, int mb, int mc, bool b_nk = false) {
   const bool kind_ok =
       (path != TDM_PATH_VALU || kind == TDM_KIND_F32) &&
-      (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC);
+      (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC) &&
+      (!b_nk || kind == TDM_KIND_BF16_F32ACC);
   if (!kind_ok) return false;
   if (M == 0 || N == 0 || K == 0) return true;  // nothing to run, or a zero fill
   switch (path) {
@@ -55,10 +57,13 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
     case TDM_PATH_VALU:
       return kind == TDM_KIND_F32 && tdm::valu_f32_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_MFMA:
-      return kind == TDM_KIND_BF16_F32ACC ? tdm::mfma_bf16_supports(M, N, K, ma, mb, mc)
-                                          : tdm::mfma_f32_supports(M, N, K, ma, mb, mc);
+      if (kind == TDM_KIND_F32) return tdm::mfma_f32_supports(M, N, K, ma, mb, mc);
+      return b_nk ? tdm::mfma_bf16_nk_supports(M, N, K, ma, mb, mc)
+                  : tdm::mfma_bf16_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_SKINNY:
-      return kind == TDM_KIND_BF16_F32ACC && tdm::skinny_bf16_supports(M, N, K, ma, mb, mc);
+      if (kind != TDM_KIND_BF16_F32ACC) return false;
+      return b_nk ? tdm::skinny_bf16_nk_supports(M, N, K, ma, mb, mc)
+                  : tdm::skinny_bf16_supports(M, N, K, ma, mb, mc);
   }
   return false;
 }
@@ -67,7 +72,8 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
 // unit that would run it (CS336 Lecture 5 GPU notes, §2.2). Below the ridge a
 // small-M bf16 product is memory-bound and goes to the streaming path; above
 // it the compute paths are used.
-tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc) {
+tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc,
+                bool b_nk = false) {
   if (M <= 0 || N <= 0 || K <= 0) return TDM_PATH_EDGE;
   const double flops = 2.0 * M * N * K;
   const double in = kind == TDM_KIND_F32 ? 4.0 : 2.0;
@@ -75,9 +81,9 @@ tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, 
   const double intensity = flops / bytes;
   if (kind == TDM_KIND_BF16_F32ACC) {
     const double ridge = kPeakMfmaBf16 / kHbmBandwidth;
-    if (intensity < ridge && supports(kind, TDM_PATH_SKINNY, M, N, K, ma, mb, mc))
+    if (intensity < ridge && supports(kind, TDM_PATH_SKINNY, M, N, K, ma, mb, mc, b_nk))
       return TDM_PATH_SKINNY;
-    if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc)) return TDM_PATH_MFMA;
+    if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc, b_nk)) return TDM_PATH_MFMA;
     return TDM_PATH_EDGE;
   }
   // fp32 has no streaming path; the choice is about filling the CUs. With
@@ -156,11 +162,13 @@ bool valid_path(tdm_path p) {
          p == TDM_PATH_MFMA || p == TDM_PATH_SKINNY;
 }
 
-// D = epilogue(A * B) for bf16 inputs (include/tdm.h).
-tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype d_type,
-                        const void* bias, const void* residual, int gelu, int64_t M, int64_t N,
-                        int64_t K, tdm_path path, void* stream) {
+// D = epilogue(A * op(B)) for bf16 inputs (include/tdm.h).
+tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layout, void* D,
+                        tdm_dtype d_type, const void* bias, const void* residual, int gelu,
+                        int64_t M, int64_t N, int64_t K, tdm_path path, void* stream) {
   if (d_type != TDM_DTYPE_F32 && d_type != TDM_DTYPE_BF16) return TDM_ERROR_INVALID_VALUE;
+  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return TDM_ERROR_INVALID_VALUE;
+  const bool b_nk = b_layout == TDM_LAYOUT_NK;
   const uint64_t dsize = d_type == TDM_DTYPE_BF16 ? 2 : 4;
   if (M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return TDM_SUCCESS;
@@ -180,7 +188,7 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype
   if (residual != nullptr && residual != D && overlaps(D, d_bytes, residual, d_bytes))
     return TDM_ERROR_INVALID_VALUE;
   const int ma = misalign(A), mb = misalign(B);
-  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, 0))
+  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, 0, b_nk))
     return TDM_ERROR_NOT_SUPPORTED;
   tdm_status st = check_device();
   if (st != TDM_SUCCESS) return st;
@@ -191,12 +199,14 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype
   e.gelu = gelu != 0;
   e.d_bf16 = d_type == TDM_DTYPE_BF16;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  if (K == 0) return to_status(tdm::launch_edge_bf16_epi(A, B, D, m, n, 0, e, s));
-  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, 0);
+  if (K == 0) return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, D, m, n, 0, e, s));
+  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, 0, b_nk);
   switch (path) {
-    case TDM_PATH_MFMA: return to_status(tdm::launch_mfma_bf16_epi(A, B, D, m, n, k, e, s));
-    case TDM_PATH_SKINNY: return to_status(tdm::launch_skinny_bf16_epi(A, B, D, m, n, k, e, s));
-    default: return to_status(tdm::launch_edge_bf16_epi(A, B, D, m, n, k, e, s));
+    case TDM_PATH_MFMA:
+      return to_status(tdm::launch_mfma_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
+    case TDM_PATH_SKINNY:
+      return to_status(tdm::launch_skinny_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
+    default: return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
   }
 }
 
@@ -230,7 +240,8 @@ tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B, float
 tdm_status gemm_bf16_epilogue(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype d_type,
                               const void* bias, const void* residual, int gelu, int64_t M,
                               int64_t N, int64_t K, void* stream) {
-  return run_bf16_epi(A, B, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO, stream);
+  return run_bf16_epi(A, B, TDM_LAYOUT_KN, D, d_type, bias, residual, gelu, M, N, K,
+                      TDM_PATH_AUTO, stream);
 }
 
 tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, void* D,
@@ -238,7 +249,23 @@ tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, voi
                                        int gelu, int64_t M, int64_t N, int64_t K, tdm_path path,
                                        void* stream) {
   if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
-  return run_bf16_epi(A, B, D, d_type, bias, residual, gelu, M, N, K, path, stream);
+  return run_bf16_epi(A, B, TDM_LAYOUT_KN, D, d_type, bias, residual, gelu, M, N, K, path,
+                      stream);
+}
+
+tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout b_layout, void* D,
+                        tdm_dtype d_type, const void* bias, const void* residual, int gelu,
+                        int64_t M, int64_t N, int64_t K, void* stream) {
+  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
+                      stream);
+}
+
+tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+                                 void* D, tdm_dtype d_type, const void* bias,
+                                 const void* residual, int gelu, int64_t M, int64_t N,
+                                 int64_t K, tdm_path path, void* stream) {
+  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, path, stream);
 }
 
 tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roofline* out) {
@@ -277,6 +304,23 @@ int tdm_path_supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_
 tdm_path tdm_select_path(tdm_kind kind, int64_t M, int64_t N, int64_t K) {
   if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
   return choose(kind, M, N, K, 0, 0, 0);
+}
+
+int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path path, int64_t M,
+                         int64_t N, int64_t K, int misalign_a, int misalign_b, int misalign_c) {
+  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return 0;
+  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return 0;
+  if (!valid_path(path) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
+  return supports(kind, path, M, N, K, misalign_a, misalign_b, misalign_c,
+                  b_layout == TDM_LAYOUT_NK) ? 1 : 0;
+}
+
+tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout b_layout, int64_t M, int64_t N,
+                            int64_t K) {
+  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
+  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return TDM_PATH_EDGE;
+  if (b_layout == TDM_LAYOUT_NK && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
+  return choose(kind, M, N, K, 0, 0, 0, b_layout == TDM_LAYOUT_NK);
 }
 
 const char* tdm_path_name(tdm_path p) {

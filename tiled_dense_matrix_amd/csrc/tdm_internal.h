@@ -80,10 +80,16 @@ bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
 // bf16 MFMA kernel: 16-byte chunks (8 elements) along K and N.
 bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                         int mis_c);
+// ... with B stored N x K (C = A * B^T): 16-byte chunks along K only.
+bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
+                           int mis_c);
 
 // bf16 small-M streaming kernel.
 bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
                           int mis_b, int mis_c);
+// ... with B stored N x K.
+bool skinny_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
+                             int mis_c);
 
 // --- launchers ----------------------------------------------------------
 hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s);
@@ -106,12 +112,15 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s);
 
 // The bf16 products with the fused epilogue of epilogue.h, written to D (fp32
-// or bf16 as e.d_bf16 says). K may be 0 on the edge kernel (D = epilogue(0)).
-hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                int K, const Epilogue& e, hipStream_t s);
-hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                int K, const Epilogue& e, hipStream_t s);
-hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
-                                  int K, const Epilogue& e, hipStream_t s);
+// or bf16 as e.d_bf16 says). b_nk: B is stored N x K (C = A * B^T). K may be
+// 0 on the edge kernel (D = epilogue(0)).
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                int M, int N, int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                int M, int N, int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
+                                  int M, int N, int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_skinny_nk_bf16(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
+                                 int K, const Epilogue& e, hipStream_t s);
 
 }  // namespace tdm

@@ -14,6 +14,7 @@ seed; A is drawn first, row-major, then B):
   round-to-nearest-even.
 * a fused-epilogue workload's bias: normal(0, bias_sigma) from its own
   generator, seeded with (seed, 1), in the output's element type.
+* a workload whose B is stored N x K draws B in that order (row n, then k).
 
 The bf16 format is the upper half of an IEEE fp32 word (1 sign, 8 exponent,
 7 mantissa bits), as the CS336 Lecture 5 GPU notes describe in §3.1 (table of
@@ -63,6 +64,9 @@ class Workload:
     bias_sigma: float = 0.0
     gelu: bool = False
     out: str = "f32"
+    # How B is stored: "kn" (K x N) or "nk" (N x K, a linear layer's weight;
+    # the product is then A @ B.T).
+    b_layout: str = "kn"
 
     @property
     def has_epilogue(self) -> bool:
@@ -82,6 +86,12 @@ WORKLOADS = {
         # kernel: + bias, GELU, bf16 output.
         Workload("bf16_mlp_gelu", "bf16", 8192, 14336, 4096, 3, "normal", 1.0, 0.02,
                  bias_sigma=0.02, gelu=True, out="bf16"),
+        # Weights stored N x K, as a linear layer keeps them: the MLP
+        # up-projection with bias, GELU and bf16 output, and the small-M shape.
+        Workload("bf16_linear_gelu", "bf16", 8192, 14336, 4096, 5, "normal", 1.0, 0.02,
+                 bias_sigma=0.02, gelu=True, out="bf16", b_layout="nk"),
+        Workload("bf16_skinny_nk", "bf16", 16, 8192, 8192, 6, "normal", 1.0, 0.02,
+                 b_layout="nk"),
         Workload("bf16_skinny", "bf16", 16, 8192, 8192, 4, "normal", 1.0, 0.02),
     )
 }
@@ -120,6 +130,8 @@ def make_inputs(w: Workload | str):
     """Return (A, B) for a workload.
 
     fp32 workloads give float32 arrays; bf16 workloads give uint16 bf16 bits.
+    B comes in its stored shape: K x N, or N x K for b_layout "nk" (drawn in
+    that order).
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -133,7 +145,7 @@ def make_inputs(w: Workload | str):
         if w.dist != "normal":
             raise ValueError(w.dist)
         A = normal_bf16(rng, (w.M, w.K), w.sigma_a)
-        B = normal_bf16(rng, (w.K, w.N), w.sigma_b)
+        B = normal_bf16(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N), w.sigma_b)
     else:
         raise ValueError(w.kind)
     return A, B
