@@ -5,7 +5,8 @@
 // LLM course ch. 15 "GPU", §15.6 table of GEMM techniques):
 //   * one workgroup owns a BM x BN tile of C (256 x 256, or 128 x 128 when a
 //     product has too few large tiles to occupy the CUs) and walks K in steps
-//     of BK;
+//     of BK, from a start staggered by up to seven steps between neighbouring
+//     workgroups (spreads the L2 channels a step's loads hit);
 //   * each step copies a BM x BK slice of A and a BK x BN slice of B from HBM
 //     into LDS with 16-byte row-contiguous loads that write LDS directly
 //     (global_load_lds), so the copy costs no registers and no LDS stores;
@@ -278,16 +279,32 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
 
   const int steps = (K + T::BK - 1) / T::BK;
   const int full_steps = K / T::BK;  // steps whose BK k are all in range
+  // Staggered start: the full steps run from step rot and wrap round (the
+  // partial step stays last). Workgroups are dealt round-robin to the eight
+  // XCDs, so blockIdx/8 numbers the workgroups of one XCD; eight neighbours
+  // there start up to seven steps apart. Rows of A (and of an N x K B) lie
+  // K*2 bytes apart, so with one common start every line a step fetches sits
+  // at the same offset of its row and the requests crowd into a few L2
+  // channels; a small stagger spreads them while workgroups that share
+  // operand rows stay within a few steps of each other, which keeps their
+  // reuse in L2 (a stagger over the whole K range loses it and is slower).
+  const int rot = full_steps > 0
+                      ? static_cast<int>(((blockIdx.x >> 3) & 7u) % static_cast<unsigned>(full_steps))
+                      : 0;
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
 
-  // Copy K step `st` into ring slot `slot`: asynchronously when all its k are
-  // in range, else through registers.
+  // Copy the K step taken at position `st` of the loop into ring slot
+  // `slot`: asynchronously when all its k are in range, else through
+  // registers.
   auto issue = [&](int st, int slot) {
-    if (st < full_steps)
-      copy_step_dma<T>(A, B, N, st * T::BK, wave, plan, lds0 + slot * T::kStage);
-    else if (st < steps)
+    if (st < full_steps) {
+      int ks = st + rot;
+      if (ks >= full_steps) ks -= full_steps;
+      copy_step_dma<T>(A, B, N, ks * T::BK, wave, plan, lds0 + slot * T::kStage);
+    } else if (st < steps) {
       copy_step_masked<T>(A, B, M, N, K, m0, n0, st * T::BK, tid, lds + slot * T::kStage);
+    }
   };
   // Before reading step `next`: its copies, and all earlier ones, have landed.
   // The S-2 later steps may still be in flight when all of them are
@@ -424,8 +441,11 @@ bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b
   return K % 8 == 0 && K >= 8 && mis_a == 0 && mis_b == 0;
 }
 
+// An N x K B takes 64 k per step, double-buffered: 128-byte row pieces of
+// both operands (one cache line each) instead of 64-byte halves measured 2-9%
+// faster there; a K x N B keeps 32 k per step and four stages.
 template <bool BNK>
-using LargeTile = Cfg<256, 256, 2, 4, 32, 4, BNK>;
+using LargeTile = Cfg<256, 256, 2, 4, BNK ? 64 : 32, BNK ? 2 : 4, BNK>;
 template <bool BNK>
 using SmallTile = Cfg<128, 128, 2, 4, 32, 4, BNK>;
 
