@@ -33,6 +33,23 @@ What it computes, and the passage each function follows:
   transpose of the stored matrix (CS336 Lecture 5 GPU notes, review question
   5: op(A) in BLAS terms; §4.1: a transposed view is another memory layout).
   The stored matrix is transposed into K x N order and handed to ``gemm``.
+* ``fp8_decode``, ``e8m0_decode``, ``gemm_fp8`` / ``gemm_fp8_tiles`` -- the
+  FP8 product. The two 8-bit formats are laid out as the table of
+  floating-point formats in CS336 Lecture 5 GPU notes, §3.1 gives them:
+  E4M3 = 1 sign, 4 exponent, 3 mantissa bits, range +-448; E5M2 = 1, 5, 2,
+  range +-57,344. The pages give no exponent bias or special codes; the
+  reading taken is the one those two ranges fix: an IEEE-style layout with
+  bias 2^(e-1) - 1 (7 and 15) and subnormals, where E5M2 keeps IEEE's
+  all-ones exponent for infinities and NaNs (largest finite 1.75 * 2^15 =
+  57344) and E4M3 gives it back to finite values except the one code
+  S.1111.111, its NaN (largest finite 1.75 * 2^8 = 448, no infinities).
+  The fine-grained per-tile scaling the same section says FP8 needs is
+  taken as block scaling along K: one power-of-two scale 2^(e-127), stored
+  as an 8-bit exponent e (e = 255: NaN), per 32 consecutive k of each row
+  of A and of each row of the N x K operand B; every element of a block is
+  multiplied by its block's scale. The product is then
+  C[i,j] = sum_k (sa[i,k/32] A[i,k]) (sb[j,k/32] B[j,k]), every term exact
+  in fp64 and summed in fp64 by the C loop.
 * ``round_to_bf16`` -- bf16 bits of fp64 values that fp32 holds exactly,
   rounded to nearest with ties to even (CS336 Lecture 5 GPU notes, §3.1 on
   bf16 as the upper half of an fp32 word).
@@ -78,7 +95,7 @@ def _load():
             build()
             lib = ctypes.CDLL(_LIB_PATH)
             i64 = ctypes.c_int64
-            for name in ("oracle_gemm_f32", "oracle_gemm_bf16"):
+            for name in ("oracle_gemm_f32", "oracle_gemm_bf16", "oracle_gemm_f64"):
                 fn = getattr(lib, name)
                 fn.restype = ctypes.c_int
                 fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
@@ -280,3 +297,96 @@ def round_to_bf16(x) -> np.ndarray:
     up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
     return (upper + up.astype(np.uint64)).astype(np.uint16)
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 operands with block scales
+# ---------------------------------------------------------------------------
+
+FP8_FORMATS = {"e4m3": (4, 3), "e5m2": (5, 2)}  # (exponent bits, mantissa bits)
+SCALE_BLOCK = 32  # k per block scale
+
+
+def fp8_decode(codes, fmt: str) -> np.ndarray:
+    """Exact fp64 value of each FP8 code (uint8) in format "e4m3" or "e5m2".
+
+    Fields sign | exponent | mantissa; exponent bias 2^(E-1) - 1. Exponent 0
+    holds the subnormals m/2^M * 2^(1-bias); otherwise (1 + m/2^M) *
+    2^(e-bias). E5M2's all-ones exponent is infinity (m = 0) or NaN; E4M3's
+    all-ones exponent is finite except S.1111.111 (NaN)."""
+    if fmt not in FP8_FORMATS:
+        raise ValueError(f"unknown FP8 format {fmt!r}")
+    E, Mb = FP8_FORMATS[fmt]
+    bias = (1 << (E - 1)) - 1
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> Mb) & ((1 << E) - 1)
+    m = (c & ((1 << Mb) - 1)).astype(np.float64)
+    frac = m / float(1 << Mb)
+    mag = np.where(e == 0, frac * 2.0 ** (1 - bias), (1.0 + frac) * np.exp2((e - bias).astype(np.float64)))
+    top = (1 << E) - 1
+    if fmt == "e5m2":
+        mag = np.where((e == top) & (m == 0), np.inf, mag)
+        mag = np.where((e == top) & (m != 0), np.nan, mag)
+    else:
+        mag = np.where((e == top) & (m == (1 << Mb) - 1), np.nan, mag)
+    return sign * mag
+
+
+def e8m0_decode(codes) -> np.ndarray:
+    """Exact fp64 value 2^(e-127) of each 8-bit scale exponent; 255 is NaN."""
+    e = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    return np.where(e == 255, np.nan, np.exp2((e - 127).astype(np.float64)))
+
+
+def fp8_scaled(codes, fmt: str, scales=None) -> np.ndarray:
+    """fp64 values of a row-major [R, K] FP8 operand, each element times the
+    scale of its 32-k block (scales: [R, K/32] exponents, or None for 1)."""
+    X = fp8_decode(codes, fmt)
+    if scales is None:
+        return X
+    R, K = X.shape
+    if K % SCALE_BLOCK:
+        raise ValueError("a block-scaled operand needs K a multiple of 32")
+    S = e8m0_decode(scales)
+    if S.shape != (R, K // SCALE_BLOCK):
+        raise ValueError(f"scales {S.shape} do not match operand {X.shape}")
+    return X * np.repeat(S, SCALE_BLOCK, axis=1)
+
+
+def gemm_f64_nt_block(a: np.ndarray, b: np.ndarray, rows, cols,
+                      threads: int | None = None) -> np.ndarray:
+    """fp64 block of a @ b.T for fp64 a[M, K], b[N, K] (the C loop)."""
+    a = np.ascontiguousarray(a, dtype=np.float64)
+    bt = np.ascontiguousarray(np.asarray(b, dtype=np.float64)[cols[0]:cols[1]].T)
+    M, K = a.shape
+    if bt.shape[0] != K:
+        raise ValueError(f"inner dimensions differ: {a.shape} vs {np.asarray(b).shape}")
+    i0, i1 = rows
+    R = np.empty((max(i1 - i0, 0), bt.shape[1]), dtype=np.float64)
+    rc = _load().oracle_gemm_f64(a.ctypes.data, bt.ctypes.data, R.ctypes.data, M, bt.shape[1], K,
+                                 i0, i1, 0, bt.shape[1], int(threads or default_threads()))
+    if rc != 0:
+        raise ValueError(f"oracle rejected block rows={rows} cols={cols}")
+    return R
+
+
+def gemm_fp8(A, a_fmt: str, B, b_fmt: str, a_scale=None, b_scale=None,
+             threads: int | None = None) -> np.ndarray:
+    """fp64 C[i,j] = sum_k (sa[i,k/32] A[i,k]) (sb[j,k/32] B[j,k]) for FP8 codes
+    A[M, K] and B[N, K] (B stored N x K), block scales optional."""
+    a = fp8_scaled(A, a_fmt, a_scale)
+    b = fp8_scaled(B, b_fmt, b_scale)
+    return gemm_f64_nt_block(a, b, (0, a.shape[0]), (0, b.shape[0]), threads)
+
+
+def gemm_fp8_tiles(A, a_fmt: str, B, b_fmt: str, tiles, a_scale=None, b_scale=None,
+                   tile: int = 32, threads: int | None = None) -> list[np.ndarray]:
+    """fp64 tiles of the FP8 product at the given (row0, col0) corners."""
+    out = []
+    for r, c in tiles:
+        r1, c1 = min(r + tile, A.shape[0]), min(c + tile, B.shape[0])
+        a = fp8_scaled(A[r:r1], a_fmt, None if a_scale is None else a_scale[r:r1])
+        b = fp8_scaled(B[c:c1], b_fmt, None if b_scale is None else b_scale[c:c1])
+        out.append(gemm_f64_nt_block(a, b, (0, r1 - r), (0, c1 - c), threads))
+    return out

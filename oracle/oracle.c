@@ -82,6 +82,17 @@ int oracle_gemm_bf16(const uint16_t *A, const uint16_t *B, double *R,
   ORACLE_BODY(widen_bf16, widen_bf16)
 }
 
+/* Same sum over operands already widened to double: the FP8 product, whose
+ * codes and block scales the Python side decodes to their exact values
+ * first. */
+static double widen_f64(double x) { return x; }
+
+int oracle_gemm_f64(const double *A, const double *B, double *R, int64_t M,
+                    int64_t N, int64_t K, int64_t i0, int64_t i1, int64_t j0,
+                    int64_t j1, int nthreads) {
+  ORACLE_BODY(widen_f64, widen_f64)
+}
+
 /* Threads OpenMP would use by default (for reporting). */
 int oracle_max_threads(void) {
 #ifdef _OPENMP

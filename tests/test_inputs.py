@@ -1,8 +1,10 @@
 """Checks of the seeded input generator (shared by the oracle's and the GPU's tests)."""
+import dataclasses
 import json
 import os
 
 import numpy as np
+import pytest
 import torch
 
 from tiled_dense_matrix_amd import inputs
@@ -101,3 +103,53 @@ def test_epilogue_workload_shares_the_mlp_operands_and_draws_its_bias_apart():
     assert np.array_equal(b, inputs.make_bias("bf16_mlp_gelu"))  # seeded
     x = inputs.bf16_bits_to_fp32(b).astype(np.float64)
     assert abs(x.std() - 0.02) < 0.002 and abs(x.mean()) < 0.002
+
+
+def test_fp8_encoding_matches_torch_round_to_nearest_even():
+    """encode_fp8 against PyTorch's float8 conversion on values spread over
+    both formats' ranges (subnormals, ties, saturation excluded by clipping)."""
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal(200_000) * np.array([1e-3, 0.05, 1.0, 30.0, 3e3])[rng.integers(0, 5, 200_000)]
+    for fmt, dt, top in (("e4m3", torch.float8_e4m3fn, 448.0), ("e5m2", torch.float8_e5m2, 57344.0)):
+        xc = np.clip(x, -top, top)
+        ref = torch.from_numpy(xc).to(dt).view(torch.uint8).numpy()
+        assert np.array_equal(inputs.encode_fp8(xc, fmt), ref), fmt
+        # beyond the range: saturates to the largest finite code
+        big = inputs.encode_fp8(np.array([1e6, -1e6]), fmt)
+        assert np.array_equal(big, torch.tensor([top, -top], dtype=torch.float64).to(dt).view(torch.uint8).numpy())
+
+
+def test_mx_block_scales_follow_the_recipe():
+    """Per 32-k block: scale exponent floor(log2 max|x|) - emax + 127; the
+    block's values divided by 2^(scale-127) round to the stored codes (the
+    block maximum can land above the largest finite value, 1.75 * 2^emax, and
+    saturates there)."""
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((6, 128)) * np.exp2(rng.integers(-6, 6, size=(6, 1)))
+    X[5, 32:64] = 0.0
+    for fmt, dt, emax, top in (("e4m3", torch.float8_e4m3fn, 8, 448.0),
+                               ("e5m2", torch.float8_e5m2, 15, 57344.0)):
+        codes, s = inputs.mx_quantize(X, fmt)
+        assert codes.shape == X.shape and s.shape == (6, 4) and s.dtype == np.uint8
+        blocks = np.abs(X).reshape(6, 4, 32).max(axis=2)
+        want = np.where(blocks > 0, np.floor(np.log2(np.where(blocks > 0, blocks, 1.0))) - emax, 0) + 127
+        assert np.array_equal(s, want.astype(np.uint8))
+        scale = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+        ref = torch.from_numpy(np.clip(X / scale, -top, top)).to(dt).view(torch.uint8).numpy()
+        assert np.array_equal(codes, ref), fmt
+
+
+def test_fp8_workload():
+    w = inputs.WORKLOADS["fp8_mlp"]
+    assert (w.kind, w.M, w.N, w.K, w.b_layout, w.scaled, w.out) == ("fp8", 8192, 14336, 4096, "nk", True, "bf16")
+    small = inputs.Workload("t", "fp8", 40, 24, 96, 11, "normal", b_layout="nk", scaled=True)
+    A, B, sa, sb = inputs.make_fp8_inputs(small)
+    assert A.shape == (40, 96) and B.shape == (24, 96) and sa.shape == (40, 3) and sb.shape == (24, 3)
+    assert A.dtype == B.dtype == sa.dtype == sb.dtype == np.uint8
+    A2, B2, sa2, sb2 = inputs.make_fp8_inputs(small)  # seeded: the same draws again
+    assert np.array_equal(A, A2) and np.array_equal(sb, sb2)
+    plain = dataclasses.replace(small, scaled=False)
+    A3, B3, sa3, sb3 = inputs.make_fp8_inputs(plain)
+    assert sa3 is None and sb3 is None and A3.shape == (40, 96)
+    with pytest.raises(ValueError):
+        inputs.make_inputs("fp8_mlp")

@@ -465,3 +465,228 @@ def test_gemm_nt_of_a_matrix_with_itself_is_its_gram_matrix():
     tiles = [(0, 0), (32, 32), (5, 64)]
     for (r, c), T in zip(tiles, oracle.gemm_nt_tiles(A, Bt, tiles, 32)):
         assert np.array_equal(T, full[r:r + 32, c:c + 32])
+
+
+# ---------------------------------------------------------------------------
+# FP8 operands with block scales
+# ---------------------------------------------------------------------------
+
+FP8_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_fp8_formats.json")
+ALL_CODES = np.arange(256, dtype=np.uint8)
+
+
+def _fp8_formats():
+    with open(FP8_GOLDEN) as fh:
+        return json.load(fh)["formats"]
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_largest_value_is_the_pages_range(fmt):
+    """The largest finite magnitude is the range the pages' format table
+    prints (448, 57344), reached by the positive and the negative code."""
+    g = {f["name"]: f for f in _fp8_formats()}[fmt]
+    assert g["sign_bits"] + g["exponent_bits"] + g["mantissa_bits"] == g["total_bits"] == 8
+    v = oracle.fp8_decode(ALL_CODES, fmt)
+    fin = v[np.isfinite(v)]
+    assert fin.max() == g["max_finite"] and fin.min() == -g["max_finite"]
+
+
+@pytest.mark.parametrize("fmt,torch_dtype", [("e4m3", "float8_e4m3fn"), ("e5m2", "float8_e5m2")])
+def test_fp8_decode_of_every_code_matches_torch(fmt, torch_dtype):
+    """All 256 codes against PyTorch's own float8 types (an independent
+    library decode): equal values, NaN and infinities at the same codes."""
+    torch = pytest.importorskip("torch")
+    ref = torch.from_numpy(ALL_CODES.copy()).view(getattr(torch, torch_dtype)).to(torch.float64).numpy()
+    got = oracle.fp8_decode(ALL_CODES, fmt)
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+    assert np.array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))  # -0.0 at 0x80
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_value_ladder(fmt):
+    """Structure the field widths fix: positive codes increase strictly; the
+    spacing is constant across the subnormals and the first binade (no gap
+    or overlap at the boundary) and doubles from binade to binade; the sign
+    bit only negates; E4M3 has exactly two NaN codes and no infinity, E5M2
+    two infinities and six NaNs."""
+    E, Mb = oracle.FP8_FORMATS[fmt]
+    v = oracle.fp8_decode(ALL_CODES, fmt)
+    pos = v[:128]
+    fin = pos[np.isfinite(pos)]
+    assert np.all(np.diff(fin) > 0)
+    step0 = fin[1] - fin[0]
+    per = 1 << Mb
+    assert np.all(np.diff(fin[:2 * per + 1]) == step0)  # subnormals + first binade
+    for b in range(1, (len(fin) - 1) // per - 1):
+        seg = np.diff(fin[per * b: per * (b + 1) + 1])
+        assert np.all(seg == step0 * 2.0 ** (b - 1)), b
+    neg = v[128:]
+    assert np.array_equal(np.isnan(neg), np.isnan(pos))
+    okv = ~np.isnan(pos)
+    assert np.array_equal(neg[okv], -pos[okv])
+    if fmt == "e4m3":
+        assert np.isnan(v).sum() == 2 and not np.isinf(v).any()
+        assert step0 == 2.0 ** -9
+    else:
+        assert np.isnan(v).sum() == 6 and np.isinf(v).sum() == 2
+        assert step0 == 2.0 ** -16
+    assert oracle.fp8_decode(np.array([(7 if fmt == "e4m3" else 15) << Mb], np.uint8), fmt)[0] == 1.0
+
+
+def test_e8m0_scale_exponents():
+    v = oracle.e8m0_decode(ALL_CODES)
+    assert v[127] == 1.0 and v[128] == 2.0 and v[0] == 2.0 ** -127 and v[254] == 2.0 ** 127
+    assert np.isnan(v[255]) and not np.isnan(v[:255]).any()
+    assert np.array_equal(v[1:255], 2.0 * v[:254])
+
+
+def test_gemm_fp8_hand_values():
+    """2 x 2 by hand: A = [[1, 2], [-0.5, 448]], B (N x K) = [[1, 1], [4, -2]]
+    in E4M3: C = [[3, 0], [447.5, -898]]."""
+    enc = {1.0: 0x38, 2.0: 0x40, -0.5: 0xB0, 448.0: 0x7E, 4.0: 0x48, -2.0: 0xC0}
+    A = np.array([[enc[1.0], enc[2.0]], [enc[-0.5], enc[448.0]]], np.uint8)
+    B = np.array([[enc[1.0], enc[1.0]], [enc[4.0], enc[-2.0]]], np.uint8)
+    assert np.array_equal(oracle.gemm_fp8(A, "e4m3", B, "e4m3"), [[3.0, 0.0], [447.5, -898.0]])
+
+
+def test_gemm_fp8_all_ones_with_block_scales_has_a_closed_form():
+    """A and B all 1.0: C[i,j] = 32 * sum_b 2^(sa[i,b]-127) 2^(sb[j,b]-127).
+    Scales differ per row and per block, and M != N, so swapped scale axes or
+    rows would not pass."""
+    rng = np.random.default_rng(21)
+    M, N, K = 3, 5, 96
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x3C, np.uint8)  # 1.0 in E5M2
+    sa = rng.integers(120, 135, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(120, 135, size=(N, K // 32)).astype(np.uint8)
+    C = oracle.gemm_fp8(A, "e4m3", B, "e5m2", sa, sb)
+    want = 32.0 * (2.0 ** (sa.astype(np.int64) - 127)) @ (2.0 ** (sb.astype(np.int64) - 127)).T
+    assert np.array_equal(C, want)
+
+
+def test_gemm_fp8_equals_the_fp32_product_of_independently_decoded_operands():
+    """Random codes and scales: the operands rebuilt through PyTorch's float8
+    decode and np.ldexp, as fp32 (exact for these scales), through the fp32
+    oracle path with B transposed to K x N. Rows, columns, blocks and the
+    transpose all differ in size."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(22)
+    M, N, K = 7, 9, 128
+    A = rng.integers(0, 256, size=(M, K), dtype=np.uint8)
+    B = rng.integers(0, 256, size=(N, K), dtype=np.uint8)
+    A[(A & 0x7F) == 0x7F] = 0x11  # no NaN codes in this test
+    B[(B & 0x7C) == 0x7C] = 0x22  # no infinities or NaNs
+    sa = rng.integers(118, 137, size=(M, K // 32)).astype(np.uint8)
+    sb = rng.integers(118, 137, size=(N, K // 32)).astype(np.uint8)
+
+    def rebuild(codes, dt, s):
+        x = torch.from_numpy(codes.copy()).view(dt).to(torch.float64).numpy()
+        return np.ldexp(x, np.repeat(s.astype(np.int64) - 127, 32, axis=1)).astype(np.float32)
+
+    a32 = rebuild(A, torch.float8_e4m3fn, sa)
+    b32 = rebuild(B, torch.float8_e5m2, sb)
+    ref = oracle.gemm(a32, np.ascontiguousarray(b32.T))
+    assert np.array_equal(oracle.gemm_fp8(A, "e4m3", B, "e5m2", sa, sb), ref)
+    tiles = oracle.gemm_fp8_tiles(A, "e4m3", B, "e5m2", [(0, 0), (3, 4)], sa, sb, tile=4)
+    assert np.array_equal(tiles[0], ref[0:4, 0:4]) and np.array_equal(tiles[1], ref[3:7, 4:8])
+
+
+def test_gemm_fp8_special_values():
+    """A NaN code or a NaN scale (255) makes its row NaN; E5M2 infinity times
+    a positive value is +inf, times zero NaN."""
+    M, N, K = 2, 2, 32
+    A = np.full((M, K), 0x38, np.uint8)
+    B = np.full((N, K), 0x3C, np.uint8)
+    C = oracle.gemm_fp8(A, "e4m3", B, "e5m2")
+    assert np.array_equal(C, np.full((2, 2), 32.0))
+    A2 = A.copy()
+    A2[0, 5] = 0x7F  # E4M3 NaN
+    C = oracle.gemm_fp8(A2, "e4m3", B, "e5m2")
+    assert np.isnan(C[0]).all() and np.array_equal(C[1], [32.0, 32.0])
+    B2 = B.copy()
+    B2[1, 3] = 0x7C  # E5M2 +inf
+    C = oracle.gemm_fp8(A, "e4m3", B2, "e5m2")
+    assert np.isposinf(C[:, 1]).all() and np.array_equal(C[:, 0], [32.0, 32.0])
+    A3 = A.copy()
+    A3[1, 3] = 0x00  # zero meets the infinity
+    C = oracle.gemm_fp8(A3, "e4m3", B2, "e5m2")
+    assert np.isnan(C[1, 1]) and np.isposinf(C[0, 1])
+    sa = np.full((M, 1), 127, np.uint8)
+    sb = np.full((N, 1), 127, np.uint8)
+    sa[1, 0] = 255
+    C = oracle.gemm_fp8(A, "e4m3", B, "e5m2", sa, sb)
+    assert np.isnan(C[1]).all() and np.array_equal(C[0], [32.0, 32.0])
+
+
+# Planted mistakes in the FP8 decode and block scaling: each must fail at
+# least one of the FP8 pins above.
+_FP8_PINS = [
+    lambda: [test_fp8_largest_value_is_the_pages_range(f) for f in ("e4m3", "e5m2")],
+    lambda: [test_fp8_decode_of_every_code_matches_torch(f, t)
+             for f, t in (("e4m3", "float8_e4m3fn"), ("e5m2", "float8_e5m2"))],
+    lambda: [test_fp8_value_ladder(f) for f in ("e4m3", "e5m2")],
+    test_e8m0_scale_exponents,
+    test_gemm_fp8_hand_values,
+    test_gemm_fp8_all_ones_with_block_scales_has_a_closed_form,
+    test_gemm_fp8_equals_the_fp32_product_of_independently_decoded_operands,
+    test_gemm_fp8_special_values,
+]
+
+
+def _fp8_mutant(bug):
+    good_decode, good_e8m0, good_scaled = oracle.fp8_decode, oracle.e8m0_decode, oracle.fp8_scaled
+
+    def decode(codes, fmt):
+        E, Mb = oracle.FP8_FORMATS[fmt]
+        bias = (1 << (E - 1)) - 1 + (1 if bug == "bias_off_by_one" else 0)
+        c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+        sign = 1.0 if bug == "sign_ignored" else np.where(c & 0x80, -1.0, 1.0)
+        e = (c >> Mb) & ((1 << E) - 1)
+        frac = (c & ((1 << Mb) - 1)) / float(1 << Mb)
+        sub_exp = -bias if bug == "subnormal_exponent" else 1 - bias
+        mag = np.where(e == 0, frac * 2.0 ** sub_exp, (1.0 + frac) * np.exp2((e - bias).astype(float)))
+        top = (1 << E) - 1
+        if fmt == "e5m2" or bug == "e4m3_ieee_specials":
+            mag = np.where((e == top) & (frac == 0), np.inf, mag)
+            mag = np.where((e == top) & (frac != 0), np.nan, mag)
+        else:
+            mag = np.where((e == top) & (frac == 1 - 1 / (1 << Mb)), np.nan, mag)
+        return sign * mag
+
+    def e8m0(codes):
+        v = good_e8m0(codes)
+        return v / 2.0 if bug == "scale_bias" else v
+
+    def scaled(codes, fmt, scales=None):
+        if scales is None or bug != "scale_blocks_tiled":
+            return good_scaled(codes, fmt, scales)
+        X = oracle.fp8_decode(codes, fmt)
+        return X * np.tile(oracle.e8m0_decode(scales), (1, 32))
+
+    patches = {}
+    if bug in ("bias_off_by_one", "sign_ignored", "subnormal_exponent", "e4m3_ieee_specials"):
+        patches["fp8_decode"] = decode
+    if bug == "scale_bias":
+        patches["e8m0_decode"] = e8m0
+    if bug == "scale_blocks_tiled":
+        patches["fp8_scaled"] = scaled
+    return patches
+
+
+FP8_BUGS = ["bias_off_by_one", "sign_ignored", "subnormal_exponent", "e4m3_ieee_specials",
+            "scale_bias", "scale_blocks_tiled"]
+
+
+@pytest.mark.parametrize("bug", FP8_BUGS)
+def test_planted_fp8_mistake_is_caught(bug, monkeypatch):
+    for name, fn in _fp8_mutant(bug).items():
+        monkeypatch.setattr(oracle, name, fn)
+    failures = 0
+    for pin in _FP8_PINS:
+        try:
+            pin()
+        except (AssertionError, ValueError, IndexError):
+            failures += 1
+    assert failures > 0, bug

@@ -15,6 +15,14 @@ seed; A is drawn first, row-major, then B):
 * a fused-epilogue workload's bias: normal(0, bias_sigma) from its own
   generator, seeded with (seed, 1), in the output's element type.
 * a workload whose B is stored N x K draws B in that order (row n, then k).
+* FP8 workloads (B always N x K): normal(0, sigma) in float64, then either
+  rounded straight to FP8 (nearest, ties to even, saturating at the largest
+  finite value), or block-scaled first as the OCP Microscaling (MX) recipe
+  does: per 32 consecutive k of a row, the shared scale is 2^s with
+  s = floor(log2(max |x|)) - emax (emax = 8 for E4M3, whose largest value
+  is 1.75 * 2^8 = 448; 15 for E5M2, 1.75 * 2^15 = 57344), stored as the
+  8-bit exponent s + 127, and every element of the block is x / 2^s rounded
+  to FP8 as above. An all-zero block gets s = 0.
 
 The bf16 format is the upper half of an IEEE fp32 word (1 sign, 8 exponent,
 7 mantissa bits), as the CS336 Lecture 5 GPU notes describe in §3.1 (table of
@@ -43,6 +51,9 @@ __all__ = [
     "pm_one_vector",
     "sample_tiles",
     "digest",
+    "encode_fp8",
+    "mx_quantize",
+    "make_fp8_inputs",
 ]
 
 
@@ -67,6 +78,10 @@ class Workload:
     # How B is stored: "kn" (K x N) or "nk" (N x K, a linear layer's weight;
     # the product is then A @ B.T).
     b_layout: str = "kn"
+    # FP8 workloads: the formats of A and B, and whether they carry block
+    # scales (one 8-bit power-of-two exponent per 32 k of each row).
+    fp8: tuple = ("e4m3", "e4m3")
+    scaled: bool = False
 
     @property
     def has_epilogue(self) -> bool:
@@ -93,6 +108,10 @@ WORKLOADS = {
         Workload("bf16_skinny_nk", "bf16", 16, 8192, 8192, 6, "normal", 1.0, 0.02,
                  b_layout="nk"),
         Workload("bf16_skinny", "bf16", 16, 8192, 8192, 4, "normal", 1.0, 0.02),
+        # The MLP up-projection in E4M3 with block scales, weight N x K,
+        # bf16 output.
+        Workload("fp8_mlp", "fp8", 8192, 14336, 4096, 7, "normal", 1.0, 0.02, out="bf16",
+                 b_layout="nk", fp8=("e4m3", "e4m3"), scaled=True),
     )
 }
 
@@ -146,9 +165,79 @@ def make_inputs(w: Workload | str):
             raise ValueError(w.dist)
         A = normal_bf16(rng, (w.M, w.K), w.sigma_a)
         B = normal_bf16(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N), w.sigma_b)
+    elif w.kind == "fp8":
+        raise ValueError("FP8 workloads come with scales: use make_fp8_inputs")
     else:
         raise ValueError(w.kind)
     return A, B
+
+
+# FP8 formats: (exponent bits, mantissa bits, exponent of the largest finite
+# value, the largest finite value).
+_FP8 = {"e4m3": (4, 3, 8, 448.0), "e5m2": (5, 2, 15, 57344.0)}
+SCALE_BLOCK = 32
+
+
+def encode_fp8(x, fmt: str) -> np.ndarray:
+    """FP8 codes (uint8) of finite float64 values: nearest representable
+    value, ties to even, magnitudes above the largest finite one saturate to
+    it. Exponent bias 2^(E-1) - 1, subnormals below 2^(1 - bias)."""
+    E, Mb, _, top = _FP8[fmt]
+    bias = (1 << (E - 1)) - 1
+    x = np.asarray(x, dtype=np.float64)
+    if not np.isfinite(x).all():
+        raise ValueError("encode_fp8 takes finite values")
+    neg = np.signbit(x)
+    a = np.abs(x)
+    _, ex = np.frexp(a)                              # a = f * 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, 1 - bias)                 # exponent of a's binade
+    q = np.ldexp(1.0, e - Mb)                        # spacing of values there
+    r = np.minimum(np.rint(a / q) * q, top)          # rint: ties to even
+    _, ex2 = np.frexp(r)
+    normal = r >= np.ldexp(1.0, 1 - bias)
+    e2 = np.where(normal, ex2 - 1, 1 - bias)
+    mant = np.ldexp(r, Mb - e2)                      # integer: 2^Mb + m, or m
+    m_field = np.where(normal, mant - (1 << Mb), mant).astype(np.int64)
+    e_field = np.where(normal, e2 + bias, 0).astype(np.int64)
+    code = (neg.astype(np.int64) << 7) | (e_field << Mb) | m_field
+    return code.astype(np.uint8)
+
+
+def mx_quantize(X, fmt: str):
+    """Block-scale a float64 [R, K] matrix (K a multiple of 32): returns
+    (codes [R, K] uint8, scale exponents [R, K/32] uint8), value =
+    fp8(code) * 2^(scale - 127)."""
+    X = np.asarray(X, dtype=np.float64)
+    R, K = X.shape
+    if K % SCALE_BLOCK:
+        raise ValueError("K must be a multiple of 32")
+    emax = _FP8[fmt][2]
+    blocks = X.reshape(R, K // SCALE_BLOCK, SCALE_BLOCK)
+    amax = np.abs(blocks).max(axis=2)
+    _, ex = np.frexp(amax)
+    s = np.where(amax > 0, ex - 1 - emax, 0)
+    s = np.clip(s, -127, 127)
+    codes = encode_fp8(np.ldexp(blocks, -s[:, :, None]), fmt).reshape(R, K)
+    return codes, (s + 127).astype(np.uint8)
+
+
+def make_fp8_inputs(w: Workload | str):
+    """(A, B, a_scale, b_scale) of an FP8 workload: codes A [M, K] and
+    B [N, K]; scale exponents [M, K/32] and [N, K/32], or None when the
+    workload is unscaled. A is drawn first, then B."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w.kind != "fp8" or w.b_layout != "nk":
+        raise ValueError("an FP8 workload with B stored N x K")
+    rng = np.random.default_rng(w.seed)
+    xa = rng.standard_normal((w.M, w.K)) * w.sigma_a
+    xb = rng.standard_normal((w.N, w.K)) * w.sigma_b
+    fa, fb = w.fp8
+    if not w.scaled:
+        return encode_fp8(xa, fa), encode_fp8(xb, fb), None, None
+    A, sa = mx_quantize(xa, fa)
+    B, sb = mx_quantize(xb, fb)
+    return A, B, sa, sb
 
 
 def make_bias(w: Workload | str) -> np.ndarray:
