@@ -49,6 +49,7 @@ import numpy as np  # noqa: E402
 
 # MI355X published peaks (dense).
 PEAK = {
+    "mfma_fp8": 5033.2,   # TFLOP/s (twice the bf16 figure; AMD quotes 5.0 PFLOP/s)
     "mfma_bf16": 2516.6,  # TFLOP/s
     "mfma_f32": 157.3,    # TFLOP/s
     "alu_f32": 157.3,     # TFLOP/s, fp32 vector
@@ -62,6 +63,7 @@ KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launc
     "skinny": ("skinny_bf16_kernel", "gemm_skinny_bf16.hip",
                ["skinny_bf16_kernel", "skinny_reduce_kernel"]),
     "skinny_nk": ("skinny_nk_bf16_kernel", "gemm_skinny_nk_bf16.hip", ["skinny_nk_bf16_kernel"]),
+    "mfma_fp8": ("mfma_fp8_kernel", "gemm_mfma_fp8.hip", ["mfma_fp8_kernel"]),
 }
 DEFAULT_WORKLOAD = "f32_4096"
 # The path each workload is specified on when --path is not given: the square
@@ -187,6 +189,8 @@ def main():
         return
 
     w = inputs.WORKLOADS[args.workload]
+    if w.kind == "fp8":
+        return main_fp8(args, w)
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
     pname_arg = args.path or DEFAULT_PATH.get(w.name, "auto")
     path = tdm.Path[pname_arg.upper()]
@@ -383,6 +387,154 @@ def main():
     if not args.no_cpu_baseline:
         B_kn = np.ascontiguousarray(B.T) if nk else B  # the oracle takes B as K x N
         line["cpu_baseline"] = cpu_baseline(w, A, B_kn, C_gpu, args.cpu_seconds, bias_np)
+    print(json.dumps(line), flush=True)
+
+
+def time_calls(step, warmup: int, steps: int, stream) -> float:
+    """Average ms per step(i) over `steps` calls after `warmup`, with events
+    on the stream the kernels run on."""
+    import torch
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        step(warmup + i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline_fp8(w, A, B, sa, sb, C_gpu, target_s: float):
+    """Time the FP8 oracle (decode, scale, fp64 sum) on the first rows of C;
+    also check those rows against the GPU output."""
+    import oracle
+    fa, fb = w.fp8
+    threads = oracle.default_threads()
+    rows = min(w.M, threads)
+    t0 = time.perf_counter()
+    oracle.gemm_fp8(A[:rows], fa, B, fb, None if sa is None else sa[:rows], sb, threads)
+    per_row = max(time.perf_counter() - t0, 1e-6) / rows
+    rows = int(max(1, min(w.M, math.floor(target_s / per_row))))
+    if rows >= threads:
+        rows -= rows % threads
+    t0 = time.perf_counter()
+    R = oracle.gemm_fp8(A[:rows], fa, B, fb, None if sa is None else sa[:rows], sb, threads)
+    if w.has_epilogue:
+        R = oracle.epilogue(R, None, None, w.gelu)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    got = oracle.widen(C_gpu[:rows]) if C_gpu.dtype == np.uint16 else C_gpu[:rows]
+    rel = float(np.linalg.norm(got - R) / max(np.linalg.norm(R), 1e-300))
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"rows 0..{rows - 1} of C ({rows}x{w.N}x{w.K}, {flops / 1e9:.1f} GFLOP) "
+                  f"in {dt:.1f} s: FP8 decode and block scales, then the fp64 triple loop",
+        "sample_parity": {"rel_fro": float(f"{rel:.3e}")},
+    }
+
+
+def main_fp8(args, w):
+    """One FP8 product per step (gemm_fp8: E4M3/E5M2 codes, block scales,
+    the workload's output type)."""
+    import torch
+    import tiled_dense_matrix_amd as tdm
+    from tiled_dense_matrix_amd import inputs
+
+    kernel, ksrc, kernels = KERNEL["mfma_fp8"]
+    A, B, sa, sb = inputs.make_fp8_inputs(w)
+    fmt = {"e4m3": tdm.Fp8Format.E4M3, "e5m2": tdm.Fp8Format.E5M2}
+    fa, fb = fmt[w.fp8[0]], fmt[w.fp8[1]]
+    out_bf16 = w.out == "bf16"
+    out_t = torch.bfloat16 if out_bf16 else torch.float32
+    out_size = 2 if out_bf16 else 4
+
+    def dev(X):
+        return None if X is None else torch.from_numpy(X).cuda()
+
+    A0, B0, sa0, sb0 = dev(A), dev(B), dev(sa), dev(sb)
+    scale_bytes = 0 if sa is None else sa.size + sb.size
+    set_bytes = A.size + B.size + scale_bytes + w.M * w.N * out_size
+    rot = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    sets = [(A0, B0, sa0, sb0, torch.empty((w.M, w.N), dtype=out_t, device="cuda"))]
+    for _ in range(rot - 1):
+        sets.append((A0.clone(), B0.clone(), None if sa0 is None else sa0.clone(),
+                     None if sb0 is None else sb0.clone(), torch.empty_like(sets[0][4])))
+    stream = torch.cuda.current_stream()
+
+    def call(i):
+        a, b, s_a, s_b, c = sets[i % rot]
+        tdm.gemm_fp8(a, b, fa, fb, s_a, s_b, D=c, gelu=w.gelu, stream=stream)
+
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    flops = 2.0 * w.M * w.N * w.K
+    alg_bytes = A.size + B.size + scale_bytes + out_size * w.M * w.N
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    traffic = traffic_record(kernels, ksrc, w.name)
+
+    C_last = sets[(args.warmup + args.steps - 1) % rot][4]
+    C_gpu = C_last.view(torch.int16).cpu().numpy().view(np.uint16) if out_bf16 else \
+        C_last.cpu().numpy()
+    if args.warmup + args.steps >= rot:
+        for st in sets[1:]:
+            assert torch.equal(st[4][:4], sets[0][4][:4]), "rotated copies disagree"
+
+    # Context only: the vendor's FP8 product through torch._scaled_mm with
+    # one scale per tensor (it takes no 32-k block scales), bf16 output.
+    vendor = None
+    if args.vendor:
+        try:
+            dt8 = {tdm.Fp8Format.E4M3: torch.float8_e4m3fn, tdm.Fp8Format.E5M2: torch.float8_e5m2}
+            one = torch.ones((), dtype=torch.float32, device="cuda")
+            vsets = [(st[0].view(dt8[fa]), st[1].view(dt8[fb])) for st in sets]
+
+            def vstep(i):
+                a, b = vsets[i % rot]
+                torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=out_t)
+
+            ms_v = time_calls(vstep, args.warmup, args.steps, stream)
+            vendor = {"op": "torch._scaled_mm with B.t(), per-tensor scales (no block scales)",
+                      "ms_per_call": round(ms_v, 6),
+                      "tflops": round(flops / (ms_v * 1e-3) / 1e12, 3),
+                      "this_library_over_vendor": round(ms_v / ms, 4)}
+        except (RuntimeError, TypeError, AttributeError) as e:
+            vendor = {"op": "torch._scaled_mm", "error": str(e).splitlines()[0][:200]}
+
+    line = {
+        "metric": "GEMM TFLOP/s and % of MFMA/VALU/HBM roofline per shape, 1x MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
+                   "inputs": f"seed {w.seed}, normal, "
+                             + ("32-k block scales" if w.scaled else "no scales"),
+                   "formats": list(w.fp8), "b_layout": "nk", "out": w.out,
+                   "path": "mfma", "kernel": kernel, "kernels_per_call": kernels,
+                   "rotated_copies": rot, "gbps_algorithmic": round(gbs, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK["mfma_fp8"],
+                     "unit": "TFLOP/s", "scope": "kernel",
+                     "frac": round(tflops / PEAK["mfma_fp8"], 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes": int(alg_bytes), "algorithmic_flops": int(flops)},
+    }
+    if vendor is not None:
+        line["vendor_blas"] = vendor
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_fp8(w, A, B, sa, sb, C_gpu, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -146,7 +146,7 @@ TDM_API tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t
                                                int64_t N, int64_t K, tdm_path path,
                                                void* stream);
 
-/* How B is stored (NEXT-2 of the scope: transposed operands). */
+/* How B is stored. */
 typedef enum tdm_layout {
   TDM_LAYOUT_KN = 0,  /* B is K x N, row-major: C = A * B (every gemm_* call)  */
   TDM_LAYOUT_NK = 1   /* B is N x K, row-major -- a linear layer's weight, as a
@@ -178,6 +178,45 @@ TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path pa
                                  int misalign_c);
 TDM_API tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout b_layout, int64_t M, int64_t N,
                                     int64_t K);
+
+/* FP8 element formats (CS336 Lecture 5 GPU notes, §3.1, table of
+ * floating-point formats): 1 sign bit, then exponent and mantissa bits. */
+typedef enum tdm_fp8_format {
+  TDM_FP8_E4M3 = 0,  /* 4 exponent bits (bias 7), 3 mantissa bits, range +-448;
+                        S.1111.111 is NaN, no infinities                      */
+  TDM_FP8_E5M2 = 1   /* 5 exponent bits (bias 15), 2 mantissa bits, range
+                        +-57344; IEEE-style infinities and NaNs               */
+} tdm_fp8_format;
+
+/* D = epilogue(A * B^T) for FP8 operands, with optional block scales: the
+ * 8-bit formats of CS336 Lecture 5 GPU notes, §3.1 (E4M3 / E5M2, each
+ * halving of the element width doubles the matrix-core peak) and the
+ * fine-grained per-tile scaling that section says FP8 needs, taken here as
+ * OCP Microscaling block scales along K. Per output element:
+ *   t = sum_k (sa[i,k/32] * A[i,k]) * (sb[j,k/32] * B[j,k])   in fp32
+ * then bias, GELU, residual and the store exactly as gemm_bf16_epilogue.
+ *   A: M x K FP8 codes (uint8), row-major, format a_format;
+ *   B: N x K FP8 codes, row-major -- the layout of a linear layer's weight,
+ *      so C = A * B^T; format b_format;
+ *   a_scale, b_scale: M x (K/32) and N x (K/32) bytes, row-major; byte e
+ *      stands for the factor 2^(e-127) (e = 255: NaN) and applies to k in
+ *      [32q, 32q + 32) of its row; both NULL for no scaling (factor 1);
+ *   D, bias, residual: as gemm_bf16_epilogue (device, element type d_type).
+ * All pointers are device pointers; the caller keeps ownership. Errors:
+ * TDM_ERROR_INVALID_VALUE for a negative size, an unknown format or d_type,
+ * a NULL operand (K > 0) or D, exactly one scale pointer NULL, a misaligned
+ * D/bias/residual, or D overlapping an input (residual == D is allowed);
+ * TDM_ERROR_NOT_SUPPORTED for K not a multiple of 32, A or B not 16-byte
+ * aligned, or M*K or N*K of 2^32 bytes or more. M == 0 or N == 0: nothing
+ * is done; K == 0: D = epilogue(0). */
+TDM_API tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_scale,
+                            const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale,
+                            void* D, tdm_dtype d_type, const void* bias, const void* residual,
+                            int gelu, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Host-only: 1 if gemm_fp8 runs this shape with A and B at these byte
+ * offsets modulo 16, else 0. */
+TDM_API int tdm_fp8_supports(int64_t M, int64_t N, int64_t K, int misalign_a, int misalign_b);
 
 /* Host-only cost query; touches no device. FLOPs = 2MNK (a multiply-add is
  * two operations) and bytes = reading A and B once and writing C once

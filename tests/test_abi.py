@@ -259,3 +259,52 @@ def test_epilogue_in_place_residual_and_k_zero_pass_validation():
     S, D = tdm.Status, tdm.DType
     assert f(FAKE, FAKE_B, FAKE_C, D.BF16, FAKE_BIAS, FAKE_C, 1, 64, 64, 64, None) == S.ERROR_NO_DEVICE
     assert f(None, None, FAKE_C, D.F32, FAKE_BIAS, FAKE_RES, 1, 64, 64, 0, None) == S.ERROR_NO_DEVICE
+
+
+def test_fp8_validation():
+    """gemm_fp8 rejects bad arguments on the host: formats, d_type, sizes,
+    null operands, one scale pointer alone, K not a multiple of 32,
+    misaligned operands, overlapping outputs."""
+    f = tdm.load().gemm_fp8
+    S, D, F = tdm.Status, tdm.DType, tdm.Fp8Format
+    E4, E5 = F.E4M3, F.E5M2
+    M = N = K = 64
+    ok = dict(A=FAKE, fa=E4, sa=None, B=FAKE_B, fb=E5, sb=None, D=FAKE_C, dt=D.BF16, bias=None,
+              res=None, gelu=0, M=M, N=N, K=K)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["A"], a["fa"], a["sa"], a["B"], a["fb"], a["sb"], a["D"], a["dt"], a["bias"],
+                 a["res"], a["gelu"], a["M"], a["N"], a["K"], None)
+
+    assert call(fa=2) == S.ERROR_INVALID_VALUE
+    assert call(fb=-1) == S.ERROR_INVALID_VALUE
+    assert call(dt=5) == S.ERROR_INVALID_VALUE
+    assert call(M=-1) == S.ERROR_INVALID_VALUE
+    assert call(A=None) == S.ERROR_INVALID_VALUE
+    assert call(D=None) == S.ERROR_INVALID_VALUE
+    assert call(sa=FAKE_BIAS) == S.ERROR_INVALID_VALUE          # b_scale missing
+    assert call(sb=FAKE_BIAS) == S.ERROR_INVALID_VALUE          # a_scale missing
+    assert call(D=FAKE_C + 2, dt=D.F32) == S.ERROR_INVALID_VALUE
+    assert call(D=FAKE + 32) == S.ERROR_INVALID_VALUE           # D overlaps A
+    assert call(bias=FAKE_C + 64) == S.ERROR_INVALID_VALUE      # bias inside D
+    assert call(sa=FAKE_C + 8, sb=FAKE_RES) == S.ERROR_INVALID_VALUE  # a scale inside D
+    assert call(K=48) == S.ERROR_NOT_SUPPORTED                  # not a multiple of 32
+    assert call(A=FAKE + 8) == S.ERROR_NOT_SUPPORTED            # A not 16-byte aligned
+    assert call(M=1 << 20, K=1 << 12) == S.ERROR_NOT_SUPPORTED  # M*K = 2^32 bytes
+    assert call(M=0) == S.SUCCESS and call(N=0, A=None, B=None) == S.SUCCESS
+    assert tdm.tdm_fp8_supports(M, N, K) and tdm.tdm_fp8_supports(5, 7, 96)
+    assert not tdm.tdm_fp8_supports(M, N, 40) and not tdm.tdm_fp8_supports(M, N, K, 8, 0)
+    assert not tdm.tdm_fp8_supports((1 << 20) + 1, N, 4096)
+
+
+def test_fp8_valid_calls_reach_the_device_check():
+    skip_if_gpu()
+    f = tdm.load().gemm_fp8
+    S, D, F = tdm.Status, tdm.DType, tdm.Fp8Format
+    assert f(FAKE, F.E4M3, None, FAKE_B, F.E4M3, None, FAKE_C, D.F32, None, None, 0, 64, 64, 64,
+             None) == S.ERROR_NO_DEVICE
+    assert f(FAKE, F.E5M2, FAKE_BIAS, FAKE_B, F.E4M3, FAKE_RES, FAKE_C, D.BF16, None, FAKE_C, 1,
+             64, 64, 96, None) == S.ERROR_NO_DEVICE
+    assert f(None, F.E4M3, None, None, F.E4M3, None, FAKE_C, D.BF16, FAKE_BIAS, None, 1, 8, 8, 0,
+             None) == S.ERROR_NO_DEVICE

@@ -7,6 +7,7 @@ input generator used by tests and the benchmark.
 """
 from ._lib import (  # noqa: F401
     DType,
+    Fp8Format,
     Kind,
     Layout,
     Path,
@@ -17,6 +18,7 @@ from ._lib import (  # noqa: F401
     gemm_bf16_ex,
     gemm_bf16_f32acc,
     gemm_f32,
+    gemm_fp8,
     gemm_roofline,
     load,
     path_name,
@@ -24,6 +26,7 @@ from ._lib import (  # noqa: F401
     tdm_gemm_bf16_epilogue_path,
     tdm_gemm_bf16_ex_path,
     tdm_gemm_bf16_f32acc_path,
+    tdm_fp8_supports,
     tdm_gemm_f32_path,
     tdm_path_supports,
     tdm_path_supports_ex,

@@ -51,6 +51,9 @@ SIGNATURES = {
                                             _i64, _i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int]),
     "tdm_select_path_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64]),
+    "gemm_fp8": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, ctypes.c_int,
+                                _p, _p, ctypes.c_int, _i64, _i64, _i64, _p]),
+    "tdm_fp8_supports": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int]),
 }
 
 
@@ -85,6 +88,12 @@ class Layout(enum.IntEnum):
 class DType(enum.IntEnum):
     F32 = 0
     BF16 = 1
+
+
+class Fp8Format(enum.IntEnum):
+    """FP8 element formats: E4M3 (range +-448) and E5M2 (range +-57344)."""
+    E4M3 = 0
+    E5M2 = 1
 
 
 class TdmError(RuntimeError):
@@ -360,3 +369,93 @@ def _bf16_dtypes():
     if hasattr(torch, "uint16"):
         dts.append(torch.uint16)
     return tuple(dts)
+
+
+# ---------------------------------------------------------------------------
+# FP8
+# ---------------------------------------------------------------------------
+
+def _fp8_format(name: str, t, fmt):
+    """The format of an FP8 operand: given, or taken from a torch float8 dtype
+    (raw uint8 codes default to E4M3)."""
+    torch = _torch()
+    from_dtype = {getattr(torch, "float8_e4m3fn", None): Fp8Format.E4M3,
+                  getattr(torch, "float8_e5m2", None): Fp8Format.E5M2}.get(t.dtype)
+    if fmt is None:
+        return from_dtype if from_dtype is not None else Fp8Format.E4M3
+    fmt = Fp8Format(fmt)
+    if from_dtype is not None and from_dtype != fmt:
+        raise ValueError(f"{name} has dtype {t.dtype} but format {fmt.name} was given")
+    return fmt
+
+
+def _fp8_dtypes():
+    torch = _torch()
+    dts = [torch.uint8]
+    for n in ("float8_e4m3fn", "float8_e5m2"):
+        if hasattr(torch, n):
+            dts.append(getattr(torch, n))
+    return tuple(dts)
+
+
+def gemm_fp8(A, B, a_format=None, b_format=None, a_scale=None, b_scale=None, D=None,
+             out_dtype=None, bias=None, residual=None, gelu=False, stream=None):
+    """D = epilogue(A @ B.T) for FP8 A [M, K] and B [N, K] (uint8 codes or torch
+    float8 tensors; a uint8 operand is E4M3 unless its format is given).
+    a_scale [M, K/32] and b_scale [N, K/32] (uint8 exponents e, factor
+    2^(e-127) per 32 k of a row) come together or not at all. The epilogue
+    and D are as in gemm_bf16_epilogue; without D a new tensor of out_dtype
+    (default torch.bfloat16) is returned."""
+    torch = _torch()
+    fp8 = _fp8_dtypes()
+    _check_matrix("A", A, fp8)
+    M, K = A.shape
+    _check_matrix("B", B, fp8, cols=K)
+    N = B.shape[0]
+    fa, fb = _fp8_format("A", A, a_format), _fp8_format("B", B, b_format)
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    if (a_scale is None) != (b_scale is None):
+        raise ValueError("a_scale and b_scale come together")
+    if a_scale is not None:
+        if K % 32:
+            raise ValueError("block scales need K a multiple of 32")
+        _check_matrix("a_scale", a_scale, (torch.uint8,), rows=M, cols=K // 32)
+        _check_matrix("b_scale", b_scale, (torch.uint8,), rows=N, cols=K // 32)
+        if a_scale.device != A.device or b_scale.device != A.device:
+            raise ValueError("scales are on another device than A and B")
+    bf16 = _bf16_dtypes()
+    if D is None:
+        out_dtype = out_dtype or torch.bfloat16
+        if out_dtype not in (torch.float32, torch.bfloat16):
+            raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    dt = DType.F32 if D.dtype == torch.float32 else DType.BF16
+    same = (torch.float32,) if dt == DType.F32 else bf16
+    _check_matrix("D", D, same, rows=M, cols=N)
+    if D.device != A.device:
+        raise ValueError("D is on another device than A and B")
+    if bias is not None:
+        if not isinstance(bias, torch.Tensor) or bias.dim() != 1 or bias.shape[0] != N:
+            raise ValueError(f"bias must be a 1-D tensor of {N} elements")
+        if bias.dtype not in same or not bias.is_cuda or not bias.is_contiguous() \
+                or bias.device != A.device:
+            raise ValueError("bias must be a contiguous tensor of D's element type on A's device")
+    if residual is not None:
+        _check_matrix("residual", residual, same, rows=M, cols=N)
+        if residual.device != A.device:
+            raise ValueError("residual is on another device than A and B")
+    fn = load().gemm_fp8
+    with torch.cuda.device(A.device):
+        st = fn(A.data_ptr() or None, int(fa), None if a_scale is None else a_scale.data_ptr(),
+                B.data_ptr() or None, int(fb), None if b_scale is None else b_scale.data_ptr(),
+                D.data_ptr() or None, int(dt), None if bias is None else bias.data_ptr(),
+                None if residual is None else residual.data_ptr(), 1 if gelu else 0, M, N, K,
+                _stream_handle(stream))
+    if st != Status.SUCCESS:
+        raise TdmError(st, "gemm_fp8")
+    return D
+
+
+def tdm_fp8_supports(M: int, N: int, K: int, misalign_a: int = 0, misalign_b: int = 0) -> bool:
+    return bool(load().tdm_fp8_supports(M, N, K, misalign_a, misalign_b))

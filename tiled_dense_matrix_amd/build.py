@@ -29,6 +29,7 @@ SOURCES = [
     "gemm_mfma_f32.hip",
     "gemm_skinny_bf16.hip",
     "gemm_skinny_nk_bf16.hip",
+    "gemm_mfma_fp8.hip",
 ]
 
 # Packed fp32 instructions are switched off for all device code: the kernels

@@ -22,6 +22,15 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
+// Same with 4 bytes per lane (global_load_lds_dword): lane l's 4 bytes land
+// at lds_addr + 4*l. The global address must be 4-byte aligned.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds_addr)
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory operations are in flight
 // (they complete in issue order).
 template <int N>

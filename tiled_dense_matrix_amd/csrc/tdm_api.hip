@@ -210,9 +210,67 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layou
   }
 }
 
+tdm_status run_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_scale,
+                   const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale, void* D,
+                   tdm_dtype d_type, const void* bias, const void* residual, int gelu, int64_t M,
+                   int64_t N, int64_t K, void* stream) {
+  auto valid_fmt = [](tdm_fp8_format f) { return f == TDM_FP8_E4M3 || f == TDM_FP8_E5M2; };
+  if (!valid_fmt(a_format) || !valid_fmt(b_format)) return TDM_ERROR_INVALID_VALUE;
+  if (d_type != TDM_DTYPE_F32 && d_type != TDM_DTYPE_BF16) return TDM_ERROR_INVALID_VALUE;
+  if (M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
+  if ((a_scale == nullptr) != (b_scale == nullptr)) return TDM_ERROR_INVALID_VALUE;
+  if (M == 0 || N == 0) return TDM_SUCCESS;
+  if (D == nullptr) return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && (A == nullptr || B == nullptr)) return TDM_ERROR_INVALID_VALUE;
+  const uint64_t dsize = d_type == TDM_DTYPE_BF16 ? 2 : 4;
+  auto aligned = [](const void* p, uint64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+  if (!aligned(D, dsize) || !aligned(bias, dsize) || !aligned(residual, dsize))
+    return TDM_ERROR_INVALID_VALUE;
+  if (too_big(M, N, K)) return TDM_ERROR_NOT_SUPPORTED;
+  const int ma = K > 0 ? misalign(A) : 0, mb = K > 0 ? misalign(B) : 0;
+  if (!tdm::mfma_fp8_supports(M, N, K, ma, mb)) return TDM_ERROR_NOT_SUPPORTED;
+  const uint64_t d_bytes = uint64_t(M) * uint64_t(N) * dsize;
+  const uint64_t a_bytes = uint64_t(M) * uint64_t(K), b_bytes = uint64_t(N) * uint64_t(K);
+  if (K > 0 && (overlaps(D, d_bytes, A, a_bytes) || overlaps(D, d_bytes, B, b_bytes)))
+    return TDM_ERROR_INVALID_VALUE;
+  if (K > 0 && a_scale != nullptr &&
+      (overlaps(D, d_bytes, a_scale, a_bytes / 32) || overlaps(D, d_bytes, b_scale, b_bytes / 32)))
+    return TDM_ERROR_INVALID_VALUE;
+  if (bias != nullptr && overlaps(D, d_bytes, bias, uint64_t(N) * dsize))
+    return TDM_ERROR_INVALID_VALUE;
+  if (residual != nullptr && residual != D && overlaps(D, d_bytes, residual, d_bytes))
+    return TDM_ERROR_INVALID_VALUE;
+  tdm_status st = check_device();
+  if (st != TDM_SUCCESS) return st;
+  tdm::Epilogue e;
+  e.bias = bias;
+  e.residual = residual;
+  e.gelu = gelu != 0;
+  e.d_bf16 = d_type == TDM_DTYPE_BF16;
+  const bool scaled = K > 0 && a_scale != nullptr;
+  return to_status(tdm::launch_mfma_fp8(A, static_cast<int>(a_format), B,
+                                        static_cast<int>(b_format), scaled ? a_scale : nullptr,
+                                        scaled ? b_scale : nullptr, D, static_cast<int>(M),
+                                        static_cast<int>(N), static_cast<int>(K), e,
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
+
+tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_scale,
+                    const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale, void* D,
+                    tdm_dtype d_type, const void* bias, const void* residual, int gelu, int64_t M,
+                    int64_t N, int64_t K, void* stream) {
+  return run_fp8(A, a_format, a_scale, B, b_format, b_scale, D, d_type, bias, residual, gelu, M,
+                 N, K, stream);
+}
+
+int tdm_fp8_supports(int64_t M, int64_t N, int64_t K, int misalign_a, int misalign_b) {
+  if (M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
+  return tdm::mfma_fp8_supports(M, N, K, misalign_a, misalign_b) ? 1 : 0;
+}
 
 tdm_status gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N,
                     int64_t K, void* stream) {

@@ -81,6 +81,12 @@ bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
 bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                         int mis_c);
 // ... with B stored N x K (C = A * B^T): 16-byte chunks along K only.
+// FP8 product (gemm_mfma_fp8.hip): A M x K, B N x K, formats 0 = E4M3,
+// 1 = E5M2; a_scale/b_scale both null (unscaled) or both block exponents.
+bool mfma_fp8_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b);
+hipError_t launch_mfma_fp8(const uint8_t* A, int a_fmt, const uint8_t* B, int b_fmt,
+                           const uint8_t* a_scale, const uint8_t* b_scale, void* D, int M, int N,
+                           int K, const Epilogue& e, hipStream_t s);
 bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                            int mis_c);
 
