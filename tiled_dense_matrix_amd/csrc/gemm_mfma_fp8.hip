@@ -62,43 +62,62 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGroupM = 8;
-constexpr int kStepK = 128;        // k (= bytes) per step and LDS row
-constexpr int kChunks = kStepK / 16;
-constexpr int kBlocksPerStep = kStepK / 32;  // scale blocks per step
+constexpr int kSpanK = 128;        // k covered by one 4-byte scale word (four blocks)
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <int BM_, int BN_, int WM_, int WN_>
+// BK: k (= bytes) per step and LDS row, 64 or 128; STAGES: ring slots.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_>
 struct Fp8Cfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
+  static constexpr int kStages = STAGES_;
+  static constexpr int kChunks = BK / 16;  // 16-byte chunks per row
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
-  static constexpr int kStageA = BM * kStepK, kStageB = BN * kStepK;
+  static constexpr int kStageA = BM * BK, kStageB = BN * BK;
   static constexpr int kScaleOff = kStageA + kStageB;  // scale words: A rows, then B rows
   static constexpr int kStage = kScaleOff + 4 * (BM + BN);
   static constexpr int kScaleCopies = (BM + BN) / 64;  // 64 words per copy
-  static constexpr int kLdsBytes = 2 * kStage;  // double buffer
+  static constexpr int kScaleCopiesPerWave = (kScaleCopies + kWaves - 1) / kWaves;
+  static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
   static constexpr int kFragM = kWaveM / 32, kFragN = kWaveN / 32;
   static constexpr int kCopyA = kStageA / 1024 / kWaves;  // 1 KB copies per wave and step
   static constexpr int kCopyB = kStageB / 1024 / kWaves;
-  static constexpr int kRowsPerCopy = 1024 / kStepK;
-  static constexpr int kSub = kStepK / 64;  // MFMA k-steps per step
+  static constexpr int kCopies = kCopyA + kCopyB;         // (every wave; scale copies extra)
+  static constexpr int kRowsPerCopy = 1024 / BK;
+  static constexpr int kSub = BK / 64;  // MFMA k-steps per step
   static constexpr int kReads = 2 * (kFragM + kFragN);  // 16-byte LDS reads per sub-step
   static constexpr int kMfmas = kFragM * kFragN;
+  static_assert(kChunks == 4 || kChunks == 8, "64- or 128-byte rows");
   static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
                 "whole 1 KB copies per wave");
   static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
                 "masked copy: whole 16-byte chunks per lane");
-  static_assert(kSub == 2, "fragment double buffer alternates per sub-step");
-  static_assert(kScaleCopies <= kWaves && BM % 64 == 0 && BN % 64 == 0, "one scale copy per wave");
-  static_assert(BM + BN <= kThreads, "one scale word per thread in the register path");
+  static_assert(BM % 64 == 0 && BN % 64 == 0, "whole 64-row scale copies");
+  static_assert(kStages >= 2 && (kStages - 2) * (kCopies + kScaleCopiesPerWave) <= 63,
+                "vmcnt range");
   static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-using LargeTile = Fp8Cfg<256, 256, 2, 4>;
-using SmallTile = Fp8Cfg<128, 128, 2, 4>;
+// 128 k per step, double-buffered: whole 128-byte lines per row. (64 k with
+// four slots, three steps of copies in flight, measured 15% slower on
+// 8192 x 14336 x 4096: the half-line row pieces double the L2 requests per
+// byte, and the copies were not waiting on latency.)
+using LargeTile = Fp8Cfg<256, 256, 2, 4, 128, 2>;
+using SmallTile = Fp8Cfg<128, 128, 2, 4, 128, 2>;
 
-__device__ __forceinline__ int swz(int m) { return (m >> 1) & 7; }
+// Chunk c of row m sits at chunk c ^ swz(m). 128-byte rows: two rows share
+// a 256-byte bank window, rows that differ in bits 1-3 take different
+// chunks; 64-byte rows: four rows share it, bits 2-3 decide. Either way the
+// 16 rows one read phase touches cover all 64 banks, and the swizzle is the
+// same for rows 16 apart.
+template <int kChunks>
+__device__ __forceinline__ int swz(int m) {
+  if constexpr (kChunks == 8)
+    return (m >> 1) & 7;
+  else
+    return (m >> 2) & 3;
+}
 
 // Per-lane byte offsets of this wave's copies from A + k0 and B + k0: copy q
 // fills LDS bytes [1024q, 1024q + 1024) of its operand's stage with rows
@@ -116,14 +135,14 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
   CopyPlan<T> p;
 #pragma unroll
   for (int j = 0; j < T::kCopyA; ++j) {
-    const int row = (wave * T::kCopyA + j) * T::kRowsPerCopy + lane / kChunks;
-    const int c = (lane % kChunks) ^ swz(row);
+    const int row = (wave * T::kCopyA + j) * T::kRowsPerCopy + lane / T::kChunks;
+    const int c = (lane % T::kChunks) ^ swz<T::kChunks>(row);
     p.a[j] = static_cast<uint32_t>(static_cast<int64_t>(min(m0 + row, M - 1)) * K + 16 * c);
   }
 #pragma unroll
   for (int j = 0; j < T::kCopyB; ++j) {
-    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopy + lane / kChunks;
-    const int c = (lane % kChunks) ^ swz(row);
+    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopy + lane / T::kChunks;
+    const int c = (lane % T::kChunks) ^ swz<T::kChunks>(row);
     p.b[j] = static_cast<uint32_t>(static_cast<int64_t>(min(n0 + row, N - 1)) * K + 16 * c);
   }
   return p;
@@ -151,7 +170,7 @@ __device__ __forceinline__ void copy_step_masked(const uint8_t* __restrict__ A,
 #pragma unroll
   for (int i = 0; i < (T::kStageA + T::kStageB) / 16 / T::kThreads; ++i) {
     const int id = tid + T::kThreads * i;
-    const int row = id / kChunks, c = id % kChunks;  // rows of A, then rows of B
+    const int row = id / T::kChunks, c = id % T::kChunks;  // rows of A, then rows of B
     const int gk = k0 + 16 * c;
     u32x4 v = zero;
     if (row < T::BM) {
@@ -161,7 +180,7 @@ __device__ __forceinline__ void copy_step_masked(const uint8_t* __restrict__ A,
       v = *reinterpret_cast<const u32x4*>(
           B + static_cast<int64_t>(min(n0 + row - T::BM, N - 1)) * K + gk);
     }
-    *(LDS_PTR(u32x4))(stage + row * kStepK + ((c ^ swz(row)) << 4)) = v;
+    *(LDS_PTR(u32x4))(stage + row * T::BK + ((c ^ swz<T::kChunks>(row)) << 4)) = v;
   }
 }
 
@@ -170,8 +189,9 @@ __device__ __forceinline__ void copy_step_masked(const uint8_t* __restrict__ A,
 // k 64s + 32x + 16*lg + 0..15 of the fragment's row lr, i.e. chunk
 // 4s + 2x + lg. Every fragment starts at a multiple of 16 rows, so the
 // swizzle only sees lr.
+template <class T>
 __device__ __forceinline__ int frag_off(int lr, int lg, int s, int x) {
-  return lr * kStepK + (((4 * s + 2 * x + lg) ^ swz(lr)) << 4);
+  return lr * T::BK + (((4 * s + 2 * x + lg) ^ swz<T::kChunks>(lr)) << 4);
 }
 
 // The lane's 32 k of a fragment starting at `frag` (off0/off1: frag_off for
@@ -185,15 +205,15 @@ __device__ __forceinline__ i32x8 read_frag(LDS_PTR(const uint8_t) frag, int off0
                static_cast<int32_t>(hi.z), static_cast<int32_t>(hi.w)};
 }
 
-// Exponents of the four scale blocks of one step (k0/32 .. k0/32 + 3) of one
-// row, byte q = block k0/32 + q; blocks beyond K read as 127 (2^0).
+// Exponents of the four scale blocks kb0 .. kb0 + 3 (128 k) of one row,
+// byte q = block kb0 + q; blocks beyond K read as 127 (2^0).
 __device__ __forceinline__ uint32_t scale_word(const uint8_t* __restrict__ row_scales, int kb0,
                                                int nkb, bool dword_ok) {
-  if (dword_ok && kb0 + kBlocksPerStep <= nkb)
+  if (dword_ok && kb0 + 4 <= nkb)
     return *reinterpret_cast<const uint32_t*>(row_scales + kb0);
   uint32_t w = 0;
 #pragma unroll
-  for (int q = 0; q < kBlocksPerStep; ++q)
+  for (int q = 0; q < 4; ++q)
     w |= (kb0 + q < nkb ? static_cast<uint32_t>(row_scales[kb0 + q]) : 127u) << (8 * q);
   return w;
 }
@@ -234,17 +254,17 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
   const int row_b = T::BM + wn * T::kWaveN + lr;    // + 32 j: its rows of B, after A's in LDS
   // LDS offsets of the wave's first A and B fragment rows (uniform) and the
   // lane's chunk offsets for sub-steps 0 and 1.
-  const int frag_a0 = wm * T::kWaveM * kStepK, frag_b0 = (T::BM + wn * T::kWaveN) * kStepK;
-  int offs[2][2];
+  const int frag_a0 = wm * T::kWaveM * T::BK, frag_b0 = (T::BM + wn * T::kWaveN) * T::BK;
+  int offs[T::kSub][2];
 #pragma unroll
-  for (int s = 0; s < 2; ++s)
+  for (int s = 0; s < T::kSub; ++s)
 #pragma unroll
-    for (int x = 0; x < 2; ++x) offs[s][x] = frag_off(lr, lg, s, x);
+    for (int x = 0; x < 2; ++x) offs[s][x] = frag_off<T>(lr, lg, s, x);
   auto frag_a = [&](LDS_PTR(const uint8_t) slot, int i, int s) {
-    return read_frag(slot + frag_a0 + 32 * i * kStepK, offs[s][0], offs[s][1]);
+    return read_frag(slot + frag_a0 + 32 * i * T::BK, offs[s][0], offs[s][1]);
   };
   auto frag_b = [&](LDS_PTR(const uint8_t) slot, int j, int s) {
-    return read_frag(slot + frag_b0 + 32 * j * kStepK, offs[s][0], offs[s][1]);
+    return read_frag(slot + frag_b0 + 32 * j * T::BK, offs[s][0], offs[s][1]);
   };
 
   f32x16 acc[T::kFragM][T::kFragN];
@@ -255,36 +275,42 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Order of the K steps: a partial step (K not a multiple of 128) comes
+  // Order of the K steps: a partial step (K not a multiple of BK) comes
   // first, in the prologue, so the masked register copy stays out of the
-  // loop; then the full steps from a start staggered as in the bf16 kernel
-  // (neighbours on one XCD begin up to seven steps apart), wrapping round.
-  const int steps = (K + kStepK - 1) / kStepK;
-  const int full_steps = K / kStepK;
+  // loop; then the full steps from a staggered start, wrapping round. As in
+  // the bf16 kernel, rows lie K bytes apart and a common start sends a
+  // step's lines to a few L2 channels; here 16 neighbours on one XCD begin
+  // up to 15 steps apart (8192 x 14336 x 4096: 0.574 ms with no stagger,
+  // 0.551 ms over 8 steps, 0.542 ms over 16, 0.560 ms over 32).
+  const int steps = (K + T::BK - 1) / T::BK;
+  const int full_steps = K / T::BK;
   const int partial = steps - full_steps;  // 0 or 1
   const int rot = full_steps > 0
-                      ? static_cast<int>(((blockIdx.x >> 3) & 7u) % static_cast<unsigned>(full_steps))
+                      ? static_cast<int>(((blockIdx.x >> 3) & 15u) % static_cast<unsigned>(full_steps))
                       : 0;
   auto step_k0 = [&](int st) {  // k0 of the step at loop position st
-    if (st < partial) return full_steps * kStepK;
+    if (st < partial) return full_steps * T::BK;
     int ks = st - partial + rot;
     if (ks >= full_steps) ks -= full_steps;
-    return ks * kStepK;
+    return ks * T::BK;
   };
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
 
-  // Scale words. Copy q (wave q, q < kScaleCopies) moves rows 64q..64q+63
-  // of the tile's scale rows (A's BM rows, then B's BN rows); in the
-  // register path thread t assembles row t.
+  // Scale words. Copy q (by wave q % kWaves) moves rows 64q..64q+63 of the
+  // tile's scale rows (A's BM rows, then B's BN rows); in the register path
+  // thread t assembles rows t, t + kThreads, ...
   const int nkb = K / 32;
-  const bool sc_first_b = kScaled && wave * 64 >= T::BM;  // this wave copies B's scales
-  const uint8_t* sc_base = sc_first_b ? SB : SA;
-  uint32_t sc_off = 0;
+  uint32_t sc_off[T::kScaleCopiesPerWave];
   if constexpr (kScaled) {
-    const int r = wave * 64 + lane - (sc_first_b ? T::BM : 0);
-    sc_off = static_cast<uint32_t>(sc_first_b ? min(n0 + r, N - 1) : min(m0 + r, M - 1)) *
-             static_cast<uint32_t>(nkb);
+#pragma unroll
+    for (int j = 0; j < T::kScaleCopiesPerWave; ++j) {
+      const int q = wave + T::kWaves * j;
+      const bool of_b = q * 64 >= T::BM;
+      const int r = q * 64 + lane - (of_b ? T::BM : 0);
+      sc_off[j] = static_cast<uint32_t>(of_b ? min(n0 + r, N - 1) : min(m0 + r, M - 1)) *
+                  static_cast<uint32_t>(nkb);
+    }
   }
 
   // Copy the step at loop position st into ring slot `slot`; `masked`: it
@@ -296,16 +322,24 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
     else
       copy_step_masked<T>(A, B, M, N, K, m0, n0, step_k0(st), tid, lds + slot * T::kStage);
     if constexpr (kScaled) {
-      const int kb0 = step_k0(st) / 32;
+      // The word of the 128-k span the step lies in (a 64-k step uses half).
+      const int kb0 = step_k0(st) / kSpanK * 4;
       if (scale_dw != 0 && !masked) {
-        if (wave < T::kScaleCopies)
-          dma4(sc_base + kb0, sc_off, lds0 + slot * T::kStage + T::kScaleOff + wave * 256);
-      } else if (tid < T::BM + T::BN) {
-        const uint8_t* row = tid < T::BM
-            ? SA + static_cast<int64_t>(min(m0 + tid, M - 1)) * nkb
-            : SB + static_cast<int64_t>(min(n0 + tid - T::BM, N - 1)) * nkb;
-        *(LDS_PTR(uint32_t))(lds + slot * T::kStage + T::kScaleOff + 4 * tid) =
-            scale_word(row, kb0, nkb, scale_dw != 0);
+#pragma unroll
+        for (int j = 0; j < T::kScaleCopiesPerWave; ++j) {
+          const int q = wave + T::kWaves * j;  // wave-uniform
+          if (q < T::kScaleCopies)
+            dma4((q * 64 >= T::BM ? SB : SA) + kb0, sc_off[j],
+                 lds0 + slot * T::kStage + T::kScaleOff + q * 256);
+        }
+      } else {
+        for (int t = tid; t < T::BM + T::BN; t += T::kThreads) {
+          const uint8_t* row = t < T::BM
+              ? SA + static_cast<int64_t>(min(m0 + t, M - 1)) * nkb
+              : SB + static_cast<int64_t>(min(n0 + t - T::BM, N - 1)) * nkb;
+          *(LDS_PTR(uint32_t))(lds + slot * T::kStage + T::kScaleOff + 4 * t) =
+              scale_word(row, kb0, nkb, scale_dw != 0);
+        }
       }
     }
   };
@@ -321,8 +355,21 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
     }
   };
 
-  issue(0, 0, partial != 0);
-  wait_vm<0>();
+  // Before reading the step at position `next`: its copies, and all earlier
+  // ones, have landed. Copies complete in issue order; the S-2 later steps
+  // may still be in flight when they have all been issued (a wave with
+  // scale copies has more in flight than counted, which only waits longer).
+  constexpr int S = T::kStages;
+  auto wait_step = [&](int next) {
+    if (S > 2 && next + S - 2 < steps)
+      wait_vm<(S > 2 ? (S - 2) * T::kCopies : 0)>();
+    else
+      wait_vm<0>();
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st, st, st < partial);
+  wait_step(0);
   __syncthreads();
 
   // Fragments of the next sub-step are read while the current one is
@@ -338,11 +385,12 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
 
   int cur = 0;
   for (int t = 0; t < steps; ++t) {
-    const int nxt = cur ^ 1;
-    // Step t+1 goes into the other slot, which every wave finished reading
-    // before the barrier that ended step t-1.
+    const int nxt = cur + 1 == S ? 0 : cur + 1;
+    // Step t+S-1 goes into the slot step t-1 used, which every wave finished
+    // reading before the barrier that ended step t-1.
     read_scales(cur);
-    issue(t + 1, nxt, false);
+    const int kq = step_k0(t) % kSpanK / 32;  // first block of this step in its word
+    issue(t + S - 1, cur == 0 ? S - 1 : cur - 1, false);
 #pragma unroll
     for (int s = 0; s < T::kSub; ++s) {
       const int c = s & 1, n = c ^ 1;
@@ -354,16 +402,16 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
         // read before this point); the next fragments come from step t+1
         // while the last MFMAs of step t run (stale and unused after the last
         // step).
-        wait_vm<0>();
+        wait_step(t + 1);
         __syncthreads();
         rb = lds + nxt * T::kStage;
         rs = 0;
       }
 #pragma unroll
       for (int j = 0; j < T::kFragN; ++j) b[n][j] = frag_b(rb, j, rs);
-      // The lane's block within the step: 2s + lg; the instruction takes the
+      // The lane's block: kq + 2s + lg of the word; the instruction takes the
       // scale from the low byte of its operand.
-      const int sh = 8 * (2 * s + lg);
+      const int sh = 8 * (kq + 2 * s + lg);
 #pragma unroll
       for (int i = 0; i < T::kFragM; ++i) {
 #pragma unroll
@@ -380,6 +428,10 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
         a[i] = frag_a(rb, i, rs);
       }
       interleave_hint<T>();
+    }
+    if constexpr (T::kSub % 2 == 1) {  // the next step's B fragments are in b[1]
+#pragma unroll
+      for (int j = 0; j < T::kFragN; ++j) b[0][j] = b[1][j];
     }
     cur = nxt;
   }
