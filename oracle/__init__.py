@@ -50,6 +50,15 @@ What it computes, and the passage each function follows:
   multiplied by its block's scale. The product is then
   C[i,j] = sum_k (sa[i,k/32] A[i,k]) (sb[j,k/32] B[j,k]), every term exact
   in fp64 and summed in fp64 by the C loop.
+* ``attention`` / ``attention_rows`` -- the attention the pages' FlashAttention
+  section computes exactly (CS336 Lecture 5 GPU notes, §6.2; GPU/attention
+  notes, "why attention is memory-bound" and "online softmax"): per head,
+  S = Q K^T * scale (scale 1/sqrt(d) there), P = the row softmax of S with
+  its row maximum subtracted, O = P V, and the per-row logsumexp
+  lse = m + log(l) that the backward pass keeps instead of P. Optionally
+  causal (key j > query i masked out; the pages' sketch leaves the mask
+  out). Written as the definition, in fp64 with NumPy matrix products, not
+  as the blocked online recurrence the kernel uses.
 * ``round_to_bf16`` -- bf16 bits of fp64 values that fp32 holds exactly,
   rounded to nearest with ties to even (CS336 Lecture 5 GPU notes, §3.1 on
   bf16 as the upper half of an fp32 word).
@@ -390,3 +399,42 @@ def gemm_fp8_tiles(A, a_fmt: str, B, b_fmt: str, tiles, a_scale=None, b_scale=No
         b = fp8_scaled(B[c:c1], b_fmt, None if b_scale is None else b_scale[c:c1])
         out.append(gemm_f64_nt_block(a, b, (0, r1 - r), (0, c1 - c), threads))
     return out
+
+
+# ---------------------------------------------------------------------------
+# Attention (the FlashAttention forward's result)
+# ---------------------------------------------------------------------------
+
+def attention_rows(Q, K, V, rows, scale: float, causal: bool = False):
+    """fp64 (O[rows], lse[rows]) of one head: Q [n_q, d], K and V [n_kv, d]
+    (float arrays or bf16 bits), `rows` the query indices wanted."""
+    q = widen(np.asarray(Q))[np.asarray(rows)]
+    k = widen(np.asarray(K))
+    v = widen(np.asarray(V))
+    S = (q @ k.T) * float(scale)
+    if causal:
+        keys = np.arange(k.shape[0])[None, :]
+        S = np.where(keys > np.asarray(rows)[:, None], -np.inf, S)
+    m = S.max(axis=1, keepdims=True)
+    P = np.exp(S - m)
+    l = P.sum(axis=1, keepdims=True)
+    O = (P @ v) / l
+    return O, (m + np.log(l))[:, 0]
+
+
+def attention(Q, K, V, scale: float, causal: bool = False):
+    """fp64 (O, lse) for Q [..., n_q, d], K and V [..., n_kv, d] (leading
+    batch/head dimensions alike): every head separately."""
+    Q = np.asarray(Q)
+    K = np.asarray(K)
+    V = np.asarray(V)
+    lead = Q.shape[:-2]
+    n_q, d = Q.shape[-2:]
+    Qf = Q.reshape(-1, n_q, d)
+    Kf = K.reshape(-1, K.shape[-2], d)
+    Vf = V.reshape(-1, V.shape[-2], d)
+    O = np.empty((Qf.shape[0], n_q, d))
+    L = np.empty((Qf.shape[0], n_q))
+    for h in range(Qf.shape[0]):
+        O[h], L[h] = attention_rows(Qf[h], Kf[h], Vf[h], np.arange(n_q), scale, causal)
+    return O.reshape(*lead, n_q, d), L.reshape(*lead, n_q)

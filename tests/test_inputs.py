@@ -153,3 +153,16 @@ def test_fp8_workload():
     assert sa3 is None and sb3 is None and A3.shape == (40, 96)
     with pytest.raises(ValueError):
         inputs.make_inputs("fp8_mlp")
+
+
+def test_attention_workloads():
+    w = inputs.ATTN_WORKLOADS["attn_fwd"]
+    assert (w.batch, w.heads, w.seq, w.head_dim, w.causal) == (4, 32, 4096, 128, False)
+    assert w.flops == 4.0 * 4 * 32 * 128 * 4096 * 4096
+    c = inputs.ATTN_WORKLOADS["attn_fwd_causal"]
+    assert c.causal and c.flops == 4.0 * 4 * 32 * 128 * (4096 * 4097 // 2)
+    small = inputs.AttnWorkload("t", 1, 2, 50, 64, True, 3)
+    Q, K, V = inputs.make_attention_inputs(small)
+    assert Q.shape == K.shape == V.shape == (1, 2, 50, 64) and Q.dtype == np.uint16
+    Q2, _, V2 = inputs.make_attention_inputs(small)
+    assert np.array_equal(Q, Q2) and np.array_equal(V, V2) and not np.array_equal(Q, K)

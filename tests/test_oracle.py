@@ -690,3 +690,135 @@ def test_planted_fp8_mistake_is_caught(bug, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             failures += 1
     assert failures > 0, bug
+
+
+# ---------------------------------------------------------------------------
+# Attention: O = softmax(Q K^T * scale) V per head, and the row logsumexp.
+# ---------------------------------------------------------------------------
+
+def _sdpa(Q, K, V, scale, causal):
+    torch = pytest.importorskip("torch")
+    t = lambda X: torch.tensor(oracle.widen(np.asarray(X)))  # noqa: E731
+    return torch.nn.functional.scaled_dot_product_attention(
+        t(Q), t(K), t(V), is_causal=causal, scale=scale).numpy()
+
+
+@pytest.mark.parametrize("shape,causal", [((2, 3, 17, 23, 16), False), ((1, 2, 40, 40, 64), True),
+                                          ((1, 1, 1, 9, 8), False), ((2, 2, 33, 33, 128), True)])
+def test_attention_matches_torch_sdpa_in_fp64(shape, causal):
+    """PyTorch's own scaled_dot_product_attention on the CPU in fp64 (an
+    independent library routine), with and without the causal mask."""
+    B, H, nq, nk, d = shape
+    rng = np.random.default_rng(nq * 31 + d)
+    Q = rng.standard_normal((B, H, nq, d))
+    K = rng.standard_normal((B, H, nk, d))
+    V = rng.standard_normal((B, H, nk, d))
+    O, _ = oracle.attention(Q, K, V, d ** -0.5, causal)
+    assert np.abs(O - _sdpa(Q, K, V, d ** -0.5, causal)).max() < 1e-13
+
+
+def test_attention_closed_forms():
+    """Equal keys: every weight is 1/n, O = the mean of V's rows and lse =
+    s + log n. One key: O = that value row, lse = its score. Causal row 0
+    sees key 0 only."""
+    rng = np.random.default_rng(5)
+    d, n = 8, 6
+    Q = rng.standard_normal((4, d))
+    k = rng.standard_normal(d)
+    K = np.tile(k, (n, 1))
+    V = rng.standard_normal((n, d))
+    O, L = oracle.attention(Q, K, V, 0.5)
+    assert np.allclose(O, V.mean(axis=0)[None, :], rtol=0, atol=1e-15)
+    assert np.allclose(L, 0.5 * (Q @ k) + np.log(n), rtol=0, atol=1e-14)
+    O1, L1 = oracle.attention(Q, K[:1], V[:1], 0.5)
+    assert np.array_equal(O1, np.tile(V[0], (4, 1))) and np.allclose(L1, 0.5 * (Q @ k), atol=1e-15)
+    Kr = rng.standard_normal((4, d))
+    Oc, Lc = oracle.attention(Q, Kr, V[:4], 0.3, causal=True)
+    assert np.array_equal(Oc[0], V[0]) and abs(Lc[0] - 0.3 * Q[0] @ Kr[0]) < 1e-15
+
+
+def test_attention_brute_force_and_logsumexp():
+    """A 3 x 5 head by explicit loops with math.exp and math.fsum; lse
+    against scipy's logsumexp."""
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(6)
+    Q, K, V = rng.standard_normal((3, 4)), rng.standard_normal((5, 4)), rng.standard_normal((5, 4))
+    sc = 0.7
+    O, L = oracle.attention(Q, K, V, sc)
+    for i in range(3):
+        s = [sc * math.fsum(Q[i, t] * K[j, t] for t in range(4)) for j in range(5)]
+        w = [math.exp(x) for x in s]
+        tot = math.fsum(w)
+        for c in range(4):
+            assert abs(O[i, c] - math.fsum(w[j] * V[j, c] for j in range(5)) / tot) < 1e-14
+        assert abs(L[i] - logsumexp(s)) < 1e-14
+
+
+def test_attention_is_stable_for_large_scores_and_takes_bf16():
+    """Scores near 1000 (exp would overflow without the row maximum taken
+    out) stay finite and agree with torch; bf16 bits are widened exactly."""
+    rng = np.random.default_rng(7)
+    Q = rng.standard_normal((5, 16)) * 30.0
+    K = rng.standard_normal((9, 16)) * 30.0
+    V = rng.standard_normal((9, 16))
+    O, L = oracle.attention(Q, K, V, 0.25)
+    assert np.isfinite(O).all() and np.isfinite(L).all() and np.abs(L).max() > 100
+    assert np.abs(O - _sdpa(Q[None], K[None], V[None], 0.25, False)[0]).max() < 1e-12
+    Qb, Kb, Vb = (inputs.fp32_to_bf16_bits(X.astype(np.float32)) for X in (Q, K, V))
+    Ob, _ = oracle.attention(Qb, Kb, Vb, 0.25)
+    Ow, _ = oracle.attention(oracle.widen(Qb), oracle.widen(Kb), oracle.widen(Vb), 0.25)
+    assert np.array_equal(Ob, Ow)
+    rows = [0, 3, 4]
+    Or, Lr = oracle.attention_rows(Q, K, V, rows, 0.25)
+    assert np.allclose(Or, O[rows], atol=1e-15) and np.allclose(Lr, L[rows], atol=1e-13)
+
+
+def _attention_mutant(bug):
+    def f(Q, K, V, scale, causal=False):
+        q, k, v = (oracle.widen(np.asarray(X)) for X in (Q, K, V))
+        S = q @ k.T * (1.0 if bug == "no_scale" else scale)
+        if causal:
+            keys = np.arange(k.shape[0])[None, :]
+            rows = np.arange(q.shape[0])[:, None]
+            S = np.where(keys >= rows if bug == "mask_diagonal" else keys > rows, -np.inf, S)
+        axis = 0 if bug == "softmax_axis" else 1
+        m = 0.0 if bug == "no_max" else S.max(axis=axis, keepdims=True)
+        P = np.exp(S - m)
+        l = P.sum(axis=axis, keepdims=True)
+        vv = v.T if bug == "v_transposed" else v
+        O = (P @ vv) / l
+        lse = (np.log(l) if bug == "lse_without_m" else m + np.log(l))
+        return O, np.broadcast_to(lse, (q.shape[0], 1))[:, 0]
+    return f
+
+
+@pytest.mark.parametrize("bug", ["no_scale", "mask_diagonal", "softmax_axis", "no_max",
+                                 "v_transposed", "lse_without_m"])
+def test_planted_attention_mistake_is_caught(bug):
+    """Each plausible mistake disagrees with torch (or the closed forms) on
+    one of these square heads; the correct copy agrees."""
+    rng = np.random.default_rng(8)
+    caught = False
+    for causal, big in ((False, 1.0), (True, 1.0), (False, 40.0)):
+        n, d = 12, 12
+        Q = rng.standard_normal((n, d)) * big
+        K = rng.standard_normal((n, d)) * big
+        V = rng.standard_normal((n, d))
+        from scipy.special import logsumexp
+        S = Q @ K.T * d ** -0.5
+        if causal:
+            S = np.where(np.arange(n)[None, :] > np.arange(n)[:, None], -np.inf, S)
+        ref_O = _sdpa(Q[None], K[None], V[None], d ** -0.5, causal)[0]
+        ref_L = logsumexp(S, axis=1)
+        with np.errstate(all="ignore"):
+            for f, expect_ok in ((_attention_mutant(None), True), (_attention_mutant(bug), False)):
+                try:
+                    O, L = f(Q, K, V, d ** -0.5, causal)
+                    ok = np.allclose(O, ref_O, atol=1e-10) and np.allclose(L, ref_L, atol=1e-9)
+                except ValueError:  # a mistake that breaks the shapes is caught too
+                    ok = False
+                if expect_ok:
+                    assert ok
+                elif not ok:
+                    caught = True
+    assert caught, bug

@@ -23,6 +23,8 @@ seed; A is drawn first, row-major, then B):
   is 1.75 * 2^8 = 448; 15 for E5M2, 1.75 * 2^15 = 57344), stored as the
   8-bit exponent s + 127, and every element of the block is x / 2^s rounded
   to FP8 as above. An all-zero block gets s = 0.
+* attention workloads: Q, then K, then V, each [batch, heads, seq, head_dim]
+  normal(0, 1) rounded to bf16 (as the bf16 workloads).
 
 The bf16 format is the upper half of an IEEE fp32 word (1 sign, 8 exponent,
 7 mantissa bits), as the CS336 Lecture 5 GPU notes describe in §3.1 (table of
@@ -54,6 +56,9 @@ __all__ = [
     "encode_fp8",
     "mx_quantize",
     "make_fp8_inputs",
+    "AttnWorkload",
+    "ATTN_WORKLOADS",
+    "make_attention_inputs",
 ]
 
 
@@ -281,3 +286,45 @@ def digest(*arrays: np.ndarray) -> str:
     for a in arrays:
         h.update(np.ascontiguousarray(a).tobytes())
     return h.hexdigest()
+
+
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """One attention forward: softmax(Q K^T / sqrt(d)) V per (batch, head),
+    Q, K, V and O [batch, heads, seq, head_dim] in bf16."""
+
+    name: str
+    batch: int
+    heads: int
+    seq: int
+    head_dim: int
+    causal: bool
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return self.head_dim ** -0.5
+
+    @property
+    def flops(self) -> float:
+        """2 * 2 * d per (query, visible key) pair: Q K^T and P V."""
+        pairs = self.seq * (self.seq + 1) // 2 if self.causal else self.seq * self.seq
+        return 4.0 * self.batch * self.heads * self.head_dim * pairs
+
+
+ATTN_WORKLOADS = {
+    w.name: w
+    for w in (
+        AttnWorkload("attn_fwd", 4, 32, 4096, 128, False, 8),
+        AttnWorkload("attn_fwd_causal", 4, 32, 4096, 128, True, 9),
+    )
+}
+
+
+def make_attention_inputs(w: AttnWorkload | str):
+    """(Q, K, V) as bf16 bits, each [batch, heads, seq, head_dim]."""
+    if isinstance(w, str):
+        w = ATTN_WORKLOADS[w]
+    rng = np.random.default_rng(w.seed)
+    shape = (w.batch, w.heads, w.seq, w.head_dim)
+    return tuple(normal_bf16(rng, shape, 1.0) for _ in range(3))
