@@ -64,6 +64,7 @@ KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launc
                ["skinny_bf16_kernel", "skinny_reduce_kernel"]),
     "skinny_nk": ("skinny_nk_bf16_kernel", "gemm_skinny_nk_bf16.hip", ["skinny_nk_bf16_kernel"]),
     "mfma_fp8": ("mfma_fp8_kernel", "gemm_mfma_fp8.hip", ["mfma_fp8_kernel"]),
+    "attention": ("attention_fwd_kernel", "attention_fwd.hip", ["attention_fwd_kernel"]),
 }
 DEFAULT_WORKLOAD = "f32_4096"
 # The path each workload is specified on when --path is not given: the square
@@ -188,6 +189,8 @@ def main():
         copy_probe(args.copy_probe_mib)
         return
 
+    if args.workload in inputs.ATTN_WORKLOADS:
+        return main_attention(args, inputs.ATTN_WORKLOADS[args.workload])
     w = inputs.WORKLOADS[args.workload]
     if w.kind == "fp8":
         return main_fp8(args, w)
@@ -535,6 +538,119 @@ def main_fp8(args, w):
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_fp8(w, A, B, sa, sb, C_gpu, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_attention(w, Q, K, V, O_gpu, target_s: float):
+    """Time the attention oracle on the first query rows of head 0; also
+    check them against the GPU output."""
+    import oracle
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.attention_rows(Q[0, 0], K[0, 0], V[0, 0], np.arange(rows), w.scale, w.causal)
+    per_row = max(time.perf_counter() - t0, 1e-6) / rows
+    rows = int(max(1, min(w.seq, math.floor(target_s / per_row))))
+    r = np.arange(rows)
+    t0 = time.perf_counter()
+    R, _ = oracle.attention_rows(Q[0, 0], K[0, 0], V[0, 0], r, w.scale, w.causal)
+    dt = time.perf_counter() - t0
+    visible = (r + 1).sum() if w.causal else rows * w.seq
+    flops = 4.0 * w.head_dim * visible
+    got = oracle.widen(O_gpu[0, 0][:rows])
+    rel = float(np.linalg.norm(got - R) / max(np.linalg.norm(R), 1e-300))
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.default_threads(),
+        "kind": "oracle",
+        "sample": f"query rows 0..{rows - 1} of head 0 ({flops / 1e9:.2f} GFLOP) in {dt:.1f} s: "
+                  "fp64 scores, softmax and P V with NumPy",
+        "sample_parity": {"rel_fro": float(f"{rel:.3e}")},
+    }
+
+
+def main_attention(args, w):
+    """One attention forward per step (attention_fwd: bf16 Q, K, V, O, the
+    row logsumexp in fp32)."""
+    import torch
+    import tiled_dense_matrix_amd as tdm
+    from tiled_dense_matrix_amd import inputs
+
+    kernel, ksrc, kernels = KERNEL["attention"]
+    Q, K, V = inputs.make_attention_inputs(w)
+
+    def dev(X):
+        return torch.from_numpy(X.view(np.int16)).cuda().view(torch.bfloat16)
+
+    base = (dev(Q), dev(K), dev(V))
+    bh = w.batch * w.heads
+    set_bytes = 4 * Q.size * 2 + bh * w.seq * 4
+    rot = max(2, math.ceil(ROTATE_BYTES / set_bytes))
+    sets = [base + (torch.empty_like(base[0]), torch.empty((w.batch, w.heads, w.seq),
+                                                           dtype=torch.float32, device="cuda"))]
+    for _ in range(rot - 1):
+        sets.append(tuple(t.clone() for t in base) + (torch.empty_like(base[0]),
+                                                      torch.empty_like(sets[0][4])))
+    stream = torch.cuda.current_stream()
+    lib = tdm.load()
+
+    def call(i):
+        q, k, v, o, lse = sets[i % rot]
+        st = lib.attention_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               lse.data_ptr(), bh, w.seq, w.seq, w.head_dim, w.scale,
+                               1 if w.causal else 0, stream.cuda_stream)
+        assert st == 0, st
+
+    ms = time_calls(call, args.warmup, args.steps, stream)
+    flops = w.flops
+    alg_bytes = 4 * Q.size * 2 + bh * w.seq * 4  # Q, K, V read once; O and lse written
+    tflops = flops / (ms * 1e-3) / 1e12
+    traffic = traffic_record(kernels, ksrc, w.name)
+    O_last = sets[(args.warmup + args.steps - 1) % rot][3]
+    O_gpu = O_last.view(torch.int16).cpu().numpy().view(np.uint16)
+    if args.warmup + args.steps >= rot:
+        for st in sets[1:]:
+            assert torch.equal(st[3][0, 0, :4], sets[0][3][0, 0, :4]), "rotated copies disagree"
+
+    # Context only: PyTorch's fused attention on the same resident inputs.
+    vendor = None
+    if args.vendor:
+        def vstep(i):
+            q, k, v = sets[i % rot][:3]
+            torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=w.causal,
+                                                             scale=w.scale)
+        ms_v = time_calls(vstep, args.warmup, args.steps, stream)
+        vendor = {"op": "torch.nn.functional.scaled_dot_product_attention (bf16)",
+                  "ms_per_call": round(ms_v, 6),
+                  "tflops": round(flops / (ms_v * 1e-3) / 1e12, 3),
+                  "this_library_over_vendor": round(ms_v / ms, 4)}
+
+    line = {
+        "metric": "GEMM TFLOP/s and % of MFMA/VALU/HBM roofline per shape, 1x MI355X",
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "heads": w.heads, "seq": w.seq,
+                   "head_dim": w.head_dim, "causal": w.causal,
+                   "inputs": f"seed {w.seed}, normal", "kernel": kernel,
+                   "kernels_per_call": kernels, "rotated_copies": rot,
+                   "flops_counted": "4 * head_dim per visible (query, key) pair"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK["mfma_bf16"],
+                     "unit": "TFLOP/s", "scope": "kernel",
+                     "frac": round(tflops / PEAK["mfma_bf16"], 4),
+                     "traffic": None if traffic is None else round(traffic),
+                     "algorithmic_bytes": int(alg_bytes), "algorithmic_flops": int(flops)},
+    }
+    if vendor is not None:
+        line["vendor_blas"] = vendor
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_attention(w, Q, K, V, O_gpu, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

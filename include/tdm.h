@@ -218,6 +218,32 @@ TDM_API tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uin
  * offsets modulo 16, else 0. */
 TDM_API int tdm_fp8_supports(int64_t M, int64_t N, int64_t K, int misalign_a, int misalign_b);
 
+/* Attention forward: O = softmax(Q K^T * scale) V for every (batch, head),
+ * computed the FlashAttention way (CS336 Lecture 5 GPU notes, §6.2: Q, K and
+ * V tiled along the sequence, an online softmax keeping each row's running
+ * maximum and normalizer, and the whole chain fused in one kernel, so the
+ * n_q x n_kv scores never reach memory; GPU/attention notes, online
+ * softmax). bf16 inputs and output, fp32 accumulation; the probabilities
+ * are rounded to bf16 before they multiply V.
+ *   Q: [batch_heads][n_q][head_dim], K and V: [batch_heads][n_kv][head_dim],
+ *      O: [batch_heads][n_q][head_dim], all bf16 (uint16_t bits), row-major;
+ *   lse: [batch_heads][n_q] fp32, the natural-log logsumexp of each row of
+ *      scale * Q K^T over the visible keys (what a backward pass keeps), or
+ *      NULL;
+ *   scale: usually 1/sqrt(head_dim); causal != 0 masks key j > query i
+ *      (requires n_q == n_kv).
+ * Device pointers, owned by the caller. Errors: TDM_ERROR_INVALID_VALUE for
+ * a negative size, n_kv == 0 with queries to compute, a NULL or misaligned
+ * pointer (O 8-byte, lse 4-byte aligned), a non-finite scale, causal with
+ * n_q != n_kv, or O overlapping Q, K, V or lse; TDM_ERROR_NOT_SUPPORTED for
+ * head_dim other than 64 or 128, Q, K or V not 16-byte aligned, more than
+ * 65535 batch_heads, or a sequence of 2^22 rows or more. batch_heads == 0 or
+ * n_q == 0: nothing is done. */
+TDM_API tdm_status attention_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                 uint16_t* O, float* lse, int64_t batch_heads, int64_t n_q,
+                                 int64_t n_kv, int64_t head_dim, float scale, int causal,
+                                 void* stream);
+
 /* Host-only cost query; touches no device. FLOPs = 2MNK (a multiply-add is
  * two operations) and bytes = reading A and B once and writing C once
  * (compute- vs memory-bound lesson, counting a matrix multiply; CS336

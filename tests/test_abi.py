@@ -308,3 +308,40 @@ def test_fp8_valid_calls_reach_the_device_check():
              64, 64, 96, None) == S.ERROR_NO_DEVICE
     assert f(None, F.E4M3, None, None, F.E4M3, None, FAKE_C, D.BF16, FAKE_BIAS, None, 1, 8, 8, 0,
              None) == S.ERROR_NO_DEVICE
+
+
+def test_attention_validation():
+    """attention_fwd rejects bad arguments on the host."""
+    f = tdm.load().attention_fwd
+    S = tdm.Status
+    nan, inf = float("nan"), float("inf")
+    ok = dict(Q=FAKE, K=FAKE_B, V=FAKE_BIAS, O=FAKE_C, lse=None, bh=4, nq=128, nkv=128, d=128,
+              scale=0.088, causal=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["Q"], a["K"], a["V"], a["O"], a["lse"], a["bh"], a["nq"], a["nkv"], a["d"],
+                 a["scale"], a["causal"], None)
+
+    assert call(bh=-1) == S.ERROR_INVALID_VALUE
+    assert call(nkv=0) == S.ERROR_INVALID_VALUE
+    assert call(Q=None) == S.ERROR_INVALID_VALUE and call(O=None) == S.ERROR_INVALID_VALUE
+    assert call(O=FAKE_C + 4) == S.ERROR_INVALID_VALUE
+    assert call(lse=FAKE_RES + 2) == S.ERROR_INVALID_VALUE
+    assert call(scale=nan) == S.ERROR_INVALID_VALUE and call(scale=inf) == S.ERROR_INVALID_VALUE
+    assert call(causal=1, nkv=64) == S.ERROR_INVALID_VALUE
+    assert call(O=FAKE + 1024) == S.ERROR_INVALID_VALUE        # O overlaps Q
+    assert call(lse=FAKE_C + 64) == S.ERROR_INVALID_VALUE      # lse inside O
+    assert call(d=96) == S.ERROR_NOT_SUPPORTED
+    assert call(K=FAKE_B + 8) == S.ERROR_NOT_SUPPORTED          # not 16-byte aligned
+    assert call(bh=65536) == S.ERROR_NOT_SUPPORTED
+    assert call(nq=1 << 22, nkv=1 << 22) == S.ERROR_NOT_SUPPORTED
+    assert call(bh=0) == S.SUCCESS and call(nq=0, Q=None, O=None) == S.SUCCESS
+
+
+def test_attention_valid_calls_reach_the_device_check():
+    skip_if_gpu()
+    f = tdm.load().attention_fwd
+    S = tdm.Status
+    assert f(FAKE, FAKE_B, FAKE_BIAS, FAKE_C, FAKE_RES, 2, 100, 100, 64, 0.125, 1, None) == S.ERROR_NO_DEVICE
+    assert f(FAKE, FAKE_B, FAKE_BIAS, FAKE_C, None, 1, 7, 300, 128, -0.5, 0, None) == S.ERROR_NO_DEVICE

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     Roofline,
     Status,
     TdmError,
+    attention_fwd,
     gemm_bf16_epilogue,
     gemm_bf16_ex,
     gemm_bf16_f32acc,

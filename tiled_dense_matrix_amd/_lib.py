@@ -54,6 +54,8 @@ SIGNATURES = {
     "gemm_fp8": (ctypes.c_int, [_p, ctypes.c_int, _p, _p, ctypes.c_int, _p, _p, ctypes.c_int,
                                 _p, _p, ctypes.c_int, _i64, _i64, _i64, _p]),
     "tdm_fp8_supports": (ctypes.c_int, [_i64, _i64, _i64, ctypes.c_int, ctypes.c_int]),
+    "attention_fwd": (ctypes.c_int, [_p, _p, _p, _p, _p, _i64, _i64, _i64, _i64, ctypes.c_float,
+                                     ctypes.c_int, _p]),
 }
 
 
@@ -459,3 +461,46 @@ def gemm_fp8(A, B, a_format=None, b_format=None, a_scale=None, b_scale=None, D=N
 
 def tdm_fp8_supports(M: int, N: int, K: int, misalign_a: int = 0, misalign_b: int = 0) -> bool:
     return bool(load().tdm_fp8_supports(M, N, K, misalign_a, misalign_b))
+
+
+# ---------------------------------------------------------------------------
+# Attention
+# ---------------------------------------------------------------------------
+
+def attention_fwd(Q, K, V, causal=False, scale=None, O=None, return_lse=False, stream=None):
+    """O = softmax(Q K^T * scale) V per (batch, head) for bf16 tensors
+    Q [..., n_q, d], K and V [..., n_kv, d] (same leading dimensions,
+    contiguous); scale defaults to 1/sqrt(d). Returns O (bf16, Q's shape), or
+    (O, lse) with the fp32 row logsumexp [..., n_q] when return_lse."""
+    torch = _torch()
+    bf16 = _bf16_dtypes()
+    for name, t in (("Q", Q), ("K", K), ("V", V)):
+        if not isinstance(t, torch.Tensor) or t.dim() < 2:
+            raise ValueError(f"{name} must be a tensor of at least 2 dimensions")
+        if t.dtype not in bf16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bf16 tensor on a GPU")
+    lead, (n_q, d) = Q.shape[:-2], Q.shape[-2:]
+    if K.shape[:-2] != lead or V.shape != K.shape or K.shape[-1] != d:
+        raise ValueError(f"shapes do not match: Q {tuple(Q.shape)}, K {tuple(K.shape)}, "
+                         f"V {tuple(V.shape)}")
+    if K.device != Q.device or V.device != Q.device:
+        raise ValueError("Q, K and V are on different devices")
+    n_kv = K.shape[-2]
+    bh = 1
+    for x in lead:
+        bh *= x
+    if O is None:
+        O = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device)
+    elif O.shape != Q.shape or O.dtype not in bf16 or not O.is_contiguous() or O.device != Q.device:
+        raise ValueError("O must be a contiguous bf16 tensor shaped like Q, on Q's device")
+    lse = torch.empty(tuple(lead) + (n_q,), dtype=torch.float32, device=Q.device) \
+        if return_lse else None
+    sc = float(d) ** -0.5 if scale is None else float(scale)
+    fn = load().attention_fwd
+    with torch.cuda.device(Q.device):
+        st = fn(Q.data_ptr() or None, K.data_ptr() or None, V.data_ptr() or None,
+                O.data_ptr() or None, None if lse is None else lse.data_ptr(), bh, n_q, n_kv, d,
+                sc, 1 if causal else 0, _stream_handle(stream))
+    if st != Status.SUCCESS:
+        raise TdmError(st, "attention_fwd")
+    return (O, lse) if return_lse else O

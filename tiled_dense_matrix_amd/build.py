@@ -30,6 +30,7 @@ SOURCES = [
     "gemm_skinny_bf16.hip",
     "gemm_skinny_nk_bf16.hip",
     "gemm_mfma_fp8.hip",
+    "attention_fwd.hip",
 ]
 
 # Packed fp32 instructions are switched off for all device code: the kernels

@@ -1,0 +1,295 @@
+// Attention forward on the gfx950 matrix cores: the FlashAttention scheme of
+// the pages (CS336 Lecture 5 GPU notes, §6.2: tiling Q, K and V along the
+// sequence, online softmax with a running row maximum m and normalizer l
+// that rescale what was accumulated when a new block raises the maximum, and
+// the three steps fused in one kernel so S and P never reach HBM; GPU/
+// attention notes, "online softmax" and "why FlashAttention saves memory").
+//
+// Per (batch*head, 128-query block) one workgroup of four waves; wave w owns
+// queries q0 + 32w .. q0 + 32w + 31 and walks the keys in blocks of 64:
+//   1. S^T = K Q^T on v_mfma_f32_32x32x16_bf16, keys as rows: A = 32 rows of
+//      the K block (16-byte LDS reads), B = the wave's queries, held in
+//      registers for the whole kernel. Lane l then holds query l%32 and, of
+//      each 32-key half, keys 8*(v/4) + 4*(l/32) + v%4 (v = 0..15);
+//   2. online softmax per query, in base 2 (scores times scale * log2 e):
+//      block maximum over the lane's 32 values and its partner lane l^32,
+//      m_new = max(m, block max), alpha = 2^(m - m_new), p = 2^(s - m_new),
+//      l = l * alpha + sum p, O *= alpha;
+//   3. O^T += V^T P^T: the p values, rounded to bf16, already sit where the
+//      MFMA's B operand wants them, for the key order of step 1 (within a
+//      16-key window lane l holds keys 4*(l/32) + 0..3 and 8 + 4*(l/32) +
+//      0..3); the A operand V^T is read from the row-major V block with two
+//      ds_read_b64_tr_b16 that return exactly those keys for row d = l%32.
+//      Any key order works as long as both operands share it.
+// K and V blocks are double-buffered in LDS by global_load_lds copies. At
+// the end O = O / l is stored in bf16 and lse = (m + log2 l) * ln 2 (the
+// natural-log logsumexp of the scaled scores) in fp32.
+//
+// LDS rows are head_dim * 2 bytes. K: 16-byte chunk c of row r sits at
+// c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64), so the 16 rows of
+// one 16-byte read phase cover all banks. V: chunk c of row r at c ^ ((r & 3)
+// << 1), so the four rows and two chunks of one transposing read phase hit
+// eight distinct chunks.
+//
+// Ragged sizes: key rows past n_kv load row n_kv - 1 and are masked out
+// (score -inf); query rows past n_q load row n_q - 1 and are not stored.
+// Causal (key j > query i masked; n_q == n_kv): key blocks wholly above the
+// diagonal are skipped, and the query blocks run heaviest first.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "lds_copy.h"
+#include "tdm_internal.h"
+
+namespace tdm {
+namespace {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int kBQ = 32 * kWaves;  // queries per workgroup
+constexpr int kBKV = 64;          // keys per block
+
+template <int D>
+struct AttnCfg {
+  static constexpr int kRow = D * 2;           // bytes per LDS row
+  static constexpr int kChunks = kRow / 16;
+  static constexpr int kBlock = kBKV * kRow;   // one K or V block
+  static constexpr int kStage = 2 * kBlock;    // K block, then V block
+  static constexpr int kLdsBytes = 2 * kStage;
+  static constexpr int kRowsPerCopy = 1024 / kRow;
+  static constexpr int kCopies = kBlock / 1024 / kWaves;  // per wave, per operand
+  static constexpr int kKSteps = D / 16;       // MFMA k-steps of Q K^T
+  static constexpr int kDBlocks = D / 32;      // 32-row blocks of O^T
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(kCopies * kWaves * 1024 == kBlock, "whole 1 KB copies");
+};
+
+template <int D>
+__device__ __forceinline__ int swz_k(int r) {
+  if constexpr (D == 128)
+    return r & 15;
+  else
+    return (r >> 1) & 7;
+}
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ lse, int n_q,
+    int n_kv, float scale_log2, int causal) {
+  using T = AttnCfg<D>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
+  LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int lr = lane & 31, lg = lane >> 5;
+  const int n_qblocks = (n_q + kBQ - 1) / kBQ;
+  // Causal: the last query blocks see the most keys; run them first.
+  const int qb = causal ? n_qblocks - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x);
+  const int q0 = qb * kBQ;
+  const int64_t bh = blockIdx.y;
+  const uint16_t* Qh = Q + bh * n_q * D;
+  const uint16_t* Kh = K + bh * n_kv * D;
+  const uint16_t* Vh = V + bh * n_kv * D;
+
+  // This lane's query and its Q operand: d = 16*ks + 8*lg + 0..7.
+  const int query = q0 + 32 * wave + lr;
+  bf16x8 qf[T::kKSteps];
+  {
+    const uint16_t* qrow = Qh + static_cast<int64_t>(min(query, n_q - 1)) * D;
+#pragma unroll
+    for (int ks = 0; ks < T::kKSteps; ++ks)
+      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * lg));
+  }
+
+  // Keys this workgroup visits: all, or (causal) up to its last query.
+  const int kv_end = causal ? min(n_kv, q0 + kBQ) : n_kv;
+  const int blocks = (kv_end + kBKV - 1) / kBKV;
+
+  // Copy plan: copy j of this wave fills rows (wave + 4j) * kRowsPerCopy ..
+  // of the block; lane L takes row +L/kChunks, LDS chunk L%kChunks.
+  uint32_t off_k[T::kCopies], off_v[T::kCopies];
+  const int crow = lane / T::kChunks, cslot = lane % T::kChunks;
+#pragma unroll
+  for (int j = 0; j < T::kCopies; ++j) {
+    const int r = (wave + kWaves * j) * T::kRowsPerCopy + crow;
+    off_k[j] = static_cast<uint32_t>(r * T::kRow + ((cslot ^ swz_k<D>(r)) << 4));
+    off_v[j] = static_cast<uint32_t>(r * T::kRow + ((cslot ^ swz_v(r)) << 4));
+  }
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
+  // Rows past n_kv read row n_kv - 1 into their own (swizzled) LDS places;
+  // their scores are masked.
+  auto issue = [&](int t, int slot) {
+    if (t >= blocks) return;
+    const int kb0 = t * kBKV;
+    const uint32_t stage = lds0 + slot * T::kStage;
+#pragma unroll
+    for (int j = 0; j < T::kCopies; ++j) {
+      const int r = (wave + kWaves * j) * T::kRowsPerCopy + crow;
+      const int over = kb0 + r - (n_kv - 1);
+      const uint32_t back = over > 0 ? static_cast<uint32_t>(over * T::kRow) : 0u;
+      dma16(Kh + static_cast<int64_t>(kb0) * D, off_k[j] - back, stage + (wave + kWaves * j) * 1024);
+      dma16(Vh + static_cast<int64_t>(kb0) * D, off_v[j] - back,
+            stage + T::kBlock + (wave + kWaves * j) * 1024);
+    }
+  };
+
+  f32x16 acc_o[T::kDBlocks];
+#pragma unroll
+  for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  issue(0, 0);
+  for (int t = 0; t < blocks; ++t) {
+    const int cur = t & 1;
+    wait_vm<0>();
+    __syncthreads();  // block t landed; every wave is done with block t-1's slot
+    issue(t + 1, cur ^ 1);
+    LDS_PTR(const uint8_t) kblk = lds + cur * T::kStage;
+    LDS_PTR(const uint8_t) vblk = kblk + T::kBlock;
+    const int kb0 = t * kBKV;
+
+    // 1. S^T for the two 32-key halves.
+    f32x16 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
+      const int r = 32 * h + lr;
+#pragma unroll
+      for (int ks = 0; ks < T::kKSteps; ++ks) {
+        const int c = 2 * ks + lg;
+        const u32x4 a = *(LDS_PTR(const u32x4))(kblk + r * T::kRow + ((c ^ swz_k<D>(r)) << 4));
+        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
+                                                       0, 0, 0);
+      }
+    }
+
+    // 2. Online softmax (base 2). Masked scores are -inf.
+    const bool need_mask = kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        float x = s[h][v] * scale_log2;
+        if (need_mask) {
+          const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
+          if (key >= n_kv || (causal && key > query)) x = -INFINITY;
+        }
+        s[h][v] = x;
+        bmax = fmaxf(bmax, x);
+      }
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+    const float m_new = fmaxf(m_run, bmax);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(s[h][v] - m_use);
+        s[h][v] = p;
+        psum += p;
+      }
+    psum += __shfl_xor(psum, 32);
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    // Rescale O only when some query of the wave raised its maximum (after
+    // the first blocks most do not).
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+#pragma unroll
+      for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+    }
+
+    // 3. O^T += V^T P^T over the four 16-key windows.
+#pragma unroll
+    for (int w16 = 0; w16 < 4; ++w16) {
+      const int h = w16 >> 1, e0 = 8 * (w16 & 1);
+      // fp32 -> bf16 (v_cvt_pk_bf16_f32: nearest even, two per instruction).
+      bf16x8 pop;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pop[e] = static_cast<__bf16>(s[h][e0 + e]);
+      // Transposing reads: in each 16-lane group G, lane i points at key row
+      // base + i/4 and d columns 4*(i%4)..+3 of its 16-column half; lane j
+      // gets 4 consecutive keys of column j.
+      const int G = lane >> 4, i = lane & 15;
+      const int key_lo = 16 * w16 + 4 * (G >> 1) + (i >> 2);
+#pragma unroll
+      for (int db = 0; db < T::kDBlocks; ++db) {
+        const int col = 32 * db + 16 * (G & 1) + 4 * (i & 3);
+        const int c = col >> 3, half = (col & 7) << 1;
+        const int r0 = key_lo, r1 = key_lo + 8;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(s16x4))(vblk + r0 * T::kRow + ((c ^ swz_v(r0)) << 4) + half));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (LDS_PTR(s16x4))(vblk + r1 * T::kRow + ((c ^ swz_v(r1)) << 4) + half));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop,
+                                                            acc_o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // O = acc / l (bf16), lse = (m + log2 l) * ln 2. Lane l holds query lr,
+  // d = 32*db + 8*(v/4) + 4*lg + v%4: four consecutive d per 8-byte store.
+  if (query < n_q) {
+    const float inv = 1.0f / l_run;
+    uint16_t* orow = O + bh * n_q * D + static_cast<int64_t>(query) * D;
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d = 32 * db + 8 * q4 + 4 * lg;
+        bf16x4 ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc_o[db][4 * q4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d) = ov;
+      }
+    if (lse != nullptr && lg == 0)
+      lse[bh * n_q + query] = (m_run + __log2f(l_run)) * 0.693147180559945309f;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O,
+                    float* lse, int bh, int n_q, int n_kv, float scale, int causal,
+                    hipStream_t s) {
+  static std::atomic<uint64_t> lds_ok{0};
+  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(attention_fwd_kernel<D>),
+                           AttnCfg<D>::kLdsBytes);
+  if (e != hipSuccess) return e;
+  const float scale_log2 = scale * 1.44269504088896341f;
+  const dim3 grid((n_q + kBQ - 1) / kBQ, bh);
+  return launch(attention_fwd_kernel<D>, grid, dim3(kThreads), AttnCfg<D>::kLdsBytes, s, Q, K, V,
+                O, lse, n_q, n_kv, scale_log2, causal);
+}
+
+}  // namespace
+
+bool attention_supports(int64_t head_dim) { return head_dim == 64 || head_dim == 128; }
+
+hipError_t launch_attention_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                uint16_t* O, float* lse, int bh, int n_q, int n_kv, int head_dim,
+                                float scale, int causal, hipStream_t s) {
+  if (head_dim == 64) return launch_d<64>(Q, K, V, O, lse, bh, n_q, n_kv, scale, causal, s);
+  return launch_d<128>(Q, K, V, O, lse, bh, n_q, n_kv, scale, causal, s);
+}
+
+}  // namespace tdm

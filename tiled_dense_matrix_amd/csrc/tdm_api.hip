@@ -255,9 +255,44 @@ tdm_status run_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_s
                                         static_cast<hipStream_t>(stream)));
 }
 
+tdm_status run_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O,
+                         float* lse, int64_t bh, int64_t n_q, int64_t n_kv, int64_t d,
+                         float scale, int causal, void* stream) {
+  if (bh < 0 || n_q < 0 || n_kv < 0 || d < 0) return TDM_ERROR_INVALID_VALUE;
+  if (!(scale == scale) || scale - scale != 0.0f) return TDM_ERROR_INVALID_VALUE;  // NaN or inf
+  if (causal != 0 && n_q != n_kv) return TDM_ERROR_INVALID_VALUE;
+  if (bh == 0 || n_q == 0) return TDM_SUCCESS;
+  if (n_kv == 0) return TDM_ERROR_INVALID_VALUE;
+  if (Q == nullptr || K == nullptr || V == nullptr || O == nullptr) return TDM_ERROR_INVALID_VALUE;
+  auto aligned = [](const void* p, uint64_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; };
+  if (!aligned(O, 8) || !aligned(lse, 4)) return TDM_ERROR_INVALID_VALUE;
+  if (!tdm::attention_supports(d)) return TDM_ERROR_NOT_SUPPORTED;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16)) return TDM_ERROR_NOT_SUPPORTED;
+  if (bh > 65535 || n_q >= (int64_t{1} << 22) || n_kv >= (int64_t{1} << 22))
+    return TDM_ERROR_NOT_SUPPORTED;
+  const uint64_t o_bytes = uint64_t(bh) * uint64_t(n_q) * uint64_t(d) * 2;
+  const uint64_t kv_bytes = uint64_t(bh) * uint64_t(n_kv) * uint64_t(d) * 2;
+  if (overlaps(O, o_bytes, Q, o_bytes) || overlaps(O, o_bytes, K, kv_bytes) ||
+      overlaps(O, o_bytes, V, kv_bytes) ||
+      (lse != nullptr && overlaps(O, o_bytes, lse, uint64_t(bh) * uint64_t(n_q) * 4)))
+    return TDM_ERROR_INVALID_VALUE;
+  tdm_status st = check_device();
+  if (st != TDM_SUCCESS) return st;
+  return to_status(tdm::launch_attention_fwd(Q, K, V, O, lse, static_cast<int>(bh),
+                                             static_cast<int>(n_q), static_cast<int>(n_kv),
+                                             static_cast<int>(d), scale, causal,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
+
+tdm_status attention_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uint16_t* O,
+                         float* lse, int64_t batch_heads, int64_t n_q, int64_t n_kv,
+                         int64_t head_dim, float scale, int causal, void* stream) {
+  return run_attention(Q, K, V, O, lse, batch_heads, n_q, n_kv, head_dim, scale, causal, stream);
+}
 
 tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_scale,
                     const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale, void* D,

@@ -81,6 +81,13 @@ bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
 bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                         int mis_c);
 // ... with B stored N x K (C = A * B^T): 16-byte chunks along K only.
+// Attention forward (attention_fwd.hip): Q [bh][n_q][d], K and V
+// [bh][n_kv][d], O [bh][n_q][d] bf16; lse [bh][n_q] fp32 or null; d 64 or 128.
+bool attention_supports(int64_t head_dim);
+hipError_t launch_attention_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
+                                uint16_t* O, float* lse, int bh, int n_q, int n_kv, int head_dim,
+                                float scale, int causal, hipStream_t s);
+
 // FP8 product (gemm_mfma_fp8.hip): A M x K, B N x K, formats 0 = E4M3,
 // 1 = E5M2; a_scale/b_scale both null (unscaled) or both block exponents.
 bool mfma_fp8_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b);
