@@ -26,15 +26,20 @@
 // natural-log logsumexp of the scaled scores) in fp32.
 //
 // LDS rows are head_dim * 2 bytes. K: 16-byte chunk c of row r sits at
-// c ^ (r & 15) (d = 128) or c ^ ((r >> 1) & 7) (d = 64), so the 16 rows of
-// one 16-byte read phase cover all banks. V: chunk c of row r at c ^ ((r & 3)
-// << 1), so the four rows and two chunks of one transposing read phase hit
-// eight distinct chunks.
+// c ^ f(r), f(r) = 2*(r % 8) + (r / 8) % 2 (d = 128) or (r >> 1) & 7
+// (d = 64): the 16 rows one 16-byte read phase touches fall in 16
+// different chunks, and so do rows r..r+7 read at chunks c and c+1. V:
+// chunk c of row r at c ^ 4*(r % 4) (d = 128) or c ^ 4*((r / 2) % 2)
+// (d = 64): the four rows and four chunks that 32 lanes of a transposing
+// read touch land in 16 distinct chunks of the bank space (with
+// c ^ 2*(r % 4), rows r and r+1 shared a chunk set: rocprof counted
+// 6.7e7 bank-conflict cycles per call at sequence 4096, 32% of the LDS
+// active cycles; now 0).
 //
 // Ragged sizes: key rows past n_kv load row n_kv - 1 and are masked out
 // (score -inf); query rows past n_q load row n_q - 1 and are not stored.
 // Causal (key j > query i masked; n_q == n_kv): key blocks wholly above the
-// diagonal are skipped, and the query blocks run heaviest first.
+// diagonal are skipped, and the query blocks run heaviest first (work_item).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -72,19 +77,49 @@ struct AttnCfg {
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
   if constexpr (D == 128)
-    return r & 15;
+    return ((r & 7) << 1) | ((r >> 3) & 1);
   else
     return (r >> 1) & 7;
 }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 1; }
+template <int D>
+__device__ __forceinline__ int swz_v(int r) {
+  if constexpr (D == 128)
+    return (r & 3) << 2;
+  else
+    return ((r >> 1) & 1) << 2;
+}
 
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+
+// Workgroup id -> (query block, head). Without the mask every workgroup does
+// the same work: consecutive ids take the query blocks of one head. With
+// the causal mask query block b sees b+1 key blocks; consecutive ids are
+// dealt round-robin to the 8 XCDs, so id -> block b = id mod n_qblocks would
+// give XCD x blocks x, x+8, ... of every head (1.5x the work of XCD 7 at
+// 32 blocks per head). Instead heads go in groups of 16 and, within a
+// group, the heaviest blocks of all its heads come first: each XCD gets an
+// even share of every weight, the short blocks fill the end, and the
+// group's K and V stay warm in the caches.
+__device__ __forceinline__ void work_item(int id, int n_qblocks, int n_heads, int causal,
+                                          int& qb, int& head) {
+  if (!causal) {
+    qb = id % n_qblocks;
+    head = id / n_qblocks;
+    return;
+  }
+  constexpr int kGroup = 16;
+  const int group = id / (kGroup * n_qblocks);
+  const int in_group = id - group * kGroup * n_qblocks;
+  const int heads = min(kGroup, n_heads - group * kGroup);  // last group may be short
+  qb = n_qblocks - 1 - in_group / heads;
+  head = group * kGroup + in_group % heads;
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ lse, int n_q,
-    int n_kv, float scale_log2, int causal) {
+    int n_kv, int n_heads, float scale_log2, int causal) {
   using T = AttnCfg<D>;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
@@ -94,10 +129,10 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   const int lane = tid & 63;
   const int lr = lane & 31, lg = lane >> 5;
   const int n_qblocks = (n_q + kBQ - 1) / kBQ;
-  // Causal: the last query blocks see the most keys; run them first.
-  const int qb = causal ? n_qblocks - 1 - static_cast<int>(blockIdx.x) : static_cast<int>(blockIdx.x);
+  int qb, head;
+  work_item(static_cast<int>(blockIdx.x), n_qblocks, n_heads, causal, qb, head);
   const int q0 = qb * kBQ;
-  const int64_t bh = blockIdx.y;
+  const int64_t bh = head;
   const uint16_t* Qh = Q + bh * n_q * D;
   const uint16_t* Kh = K + bh * n_kv * D;
   const uint16_t* Vh = V + bh * n_kv * D;
@@ -124,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   for (int j = 0; j < T::kCopies; ++j) {
     const int r = (wave + kWaves * j) * T::kRowsPerCopy + crow;
     off_k[j] = static_cast<uint32_t>(r * T::kRow + ((cslot ^ swz_k<D>(r)) << 4));
-    off_v[j] = static_cast<uint32_t>(r * T::kRow + ((cslot ^ swz_v(r)) << 4));
+    off_v[j] = static_cast<uint32_t>(r * T::kRow + ((cslot ^ swz_v<D>(r)) << 4));
   }
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
   // Rows past n_kv read row n_kv - 1 into their own (swizzled) LDS places;
@@ -236,9 +271,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
         const int c = col >> 3, half = (col & 7) << 1;
         const int r0 = key_lo, r1 = key_lo + 8;
         const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(s16x4))(vblk + r0 * T::kRow + ((c ^ swz_v(r0)) << 4) + half));
+            (LDS_PTR(s16x4))(vblk + r0 * T::kRow + ((c ^ swz_v<D>(r0)) << 4) + half));
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(s16x4))(vblk + r1 * T::kRow + ((c ^ swz_v(r1)) << 4) + half));
+            (LDS_PTR(s16x4))(vblk + r1 * T::kRow + ((c ^ swz_v<D>(r1)) << 4) + half));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop,
@@ -276,9 +311,9 @@ hipError_t launch_d(const uint16_t* Q, const uint16_t* K, const uint16_t* V, uin
                            AttnCfg<D>::kLdsBytes);
   if (e != hipSuccess) return e;
   const float scale_log2 = scale * 1.44269504088896341f;
-  const dim3 grid((n_q + kBQ - 1) / kBQ, bh);
+  const dim3 grid(((n_q + kBQ - 1) / kBQ) * bh);
   return launch(attention_fwd_kernel<D>, grid, dim3(kThreads), AttnCfg<D>::kLdsBytes, s, Q, K, V,
-                O, lse, n_q, n_kv, scale_log2, causal);
+                O, lse, n_q, n_kv, bh, scale_log2, causal);
 }
 
 }  // namespace
