@@ -145,3 +145,19 @@ def test_full_size_workload(name):
     rows = sorted(set(rng.choice(w.seq, 46, replace=False).tolist()) | {0, w.seq - 1})
     worst = check(Q, K, V, w.causal, w.scale, O, L, heads, rows)
     log(f"  {name}: worst err/bound {worst:.3f}")
+
+
+def test_zero_scale_with_the_causal_mask_averages_the_visible_values():
+    """scale = 0: every visible key weighs the same, so row i is the mean of
+    V[0..i] (masked keys must not turn into NaN on the way)."""
+    rng = np.random.default_rng(12)
+    n = 150
+    Q = inputs.normal_bf16(rng, (1, 1, n, 64), 1.0)
+    K = inputs.normal_bf16(rng, (1, 1, n, 64), 1.0)
+    V = inputs.normal_bf16(rng, (1, 1, n, 64), 1.0)
+    O, L = run(Q, K, V, True, scale=0.0)
+    v = oracle.widen(V)[0, 0]
+    mean = np.cumsum(v, axis=0) / np.arange(1, n + 1)[:, None]
+    assert np.isfinite(O).all()
+    assert np.all(np.abs(O[0, 0] - mean) <= 2.0 ** -8 * np.abs(mean) + 2.0 ** -9 * np.abs(v).max())
+    assert np.allclose(L[0, 0], np.log(np.arange(1, n + 1)), atol=1e-5)

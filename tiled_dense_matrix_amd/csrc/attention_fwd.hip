@@ -179,6 +179,26 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     }
   };
 
+  // Per-lane LDS offsets, fixed for the whole kernel: the K reads of k-step
+  // ks (row lr of a 32-row half; the other half is 32 rows further) and the
+  // transposing V reads of d-block db (key rows 4*(G/2) + i/4 of a 16-key
+  // window; the window and the +8 rows of the second read are further
+  // rows). The swizzles see only the row modulo 16, so these offsets hold
+  // for every half and window (computing them per read cost 4%).
+  int koff[T::kKSteps], voff[T::kDBlocks];
+#pragma unroll
+  for (int ks = 0; ks < T::kKSteps; ++ks)
+    koff[ks] = lr * T::kRow + (((2 * ks + lg) ^ swz_k<D>(lr)) << 4);
+  {
+    const int G = lane >> 4, i = lane & 15;
+    const int r = 4 * (G >> 1) + (i >> 2);
+#pragma unroll
+    for (int db = 0; db < T::kDBlocks; ++db) {
+      const int col = 32 * db + 16 * (G & 1) + 4 * (i & 3);
+      voff[db] = r * T::kRow + (((col >> 3) ^ swz_v<D>(r)) << 4) + ((col & 7) << 1);
+    }
+  }
+
   f32x16 acc_o[T::kDBlocks];
 #pragma unroll
   for (int db = 0; db < T::kDBlocks; ++db)
@@ -202,11 +222,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
-      const int r = 32 * h + lr;
 #pragma unroll
       for (int ks = 0; ks < T::kKSteps; ++ks) {
-        const int c = 2 * ks + lg;
-        const u32x4 a = *(LDS_PTR(const u32x4))(kblk + r * T::kRow + ((c ^ swz_k<D>(r)) << 4));
+        const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 32 * h * T::kRow + koff[ks]);
         s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
                                                        0, 0, 0);
       }
@@ -262,18 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
       for (int e = 0; e < 8; ++e) pop[e] = static_cast<__bf16>(s[h][e0 + e]);
       // Transposing reads: in each 16-lane group G, lane i points at key row
       // base + i/4 and d columns 4*(i%4)..+3 of its 16-column half; lane j
-      // gets 4 consecutive keys of column j.
-      const int G = lane >> 4, i = lane & 15;
-      const int key_lo = 16 * w16 + 4 * (G >> 1) + (i >> 2);
+      // gets 4 consecutive keys of column j (rows of the window, then 8
+      // rows further).
 #pragma unroll
       for (int db = 0; db < T::kDBlocks; ++db) {
-        const int col = 32 * db + 16 * (G & 1) + 4 * (i & 3);
-        const int c = col >> 3, half = (col & 7) << 1;
-        const int r0 = key_lo, r1 = key_lo + 8;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(s16x4))(vblk + r0 * T::kRow + ((c ^ swz_v<D>(r0)) << 4) + half));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (LDS_PTR(s16x4))(vblk + r1 * T::kRow + ((c ^ swz_v<D>(r1)) << 4) + half));
+        LDS_PTR(const uint8_t) vw = vblk + 16 * w16 * T::kRow + voff[db];
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 8 * T::kRow));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
         acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop,
