@@ -92,7 +92,8 @@ __device__ __forceinline__ int swz_v(int r) {
 typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // Workgroup id -> (query block, head). Without the mask every workgroup does
-// the same work: consecutive ids take the query blocks of one head. With
+// the same work; the query blocks of a head share its K and V, so they go to
+// one XCD (4096-sequence attention: 6% faster than consecutive ids). With
 // the causal mask query block b sees b+1 key blocks; consecutive ids are
 // dealt round-robin to the 8 XCDs, so id -> block b = id mod n_qblocks would
 // give XCD x blocks x, x+8, ... of every head (1.5x the work of XCD 7 at
@@ -103,8 +104,18 @@ typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 __device__ __forceinline__ void work_item(int id, int n_qblocks, int n_heads, int causal,
                                           int& qb, int& head) {
   if (!causal) {
-    qb = id % n_qblocks;
-    head = id / n_qblocks;
+    // All query blocks of a head on one XCD (ids are dealt round-robin to
+    // the 8 XCDs), so that XCD's L2 serves the head's K and V to all of
+    // them; with a head count that is not a multiple of 8, heads in order.
+    constexpr int kXcds = 8;
+    if (n_heads % kXcds == 0) {
+      const int xcd = id % kXcds, k = id / kXcds;
+      head = (k / n_qblocks) * kXcds + xcd;
+      qb = k % n_qblocks;
+    } else {
+      qb = id % n_qblocks;
+      head = id / n_qblocks;
+    }
     return;
   }
   constexpr int kGroup = 16;
