@@ -11,8 +11,11 @@ applied to |V|):
   2^-8 W      the probabilities rounded to bf16 (2^-9 relative each) and
               the normalizer summed from the unrounded ones (2^-9);
   2^-9 |O|    the bf16 output;
-  2^-12 W     scores summed in fp32 over head_dim products and the
-              hardware exp2 (relative errors near 2^-14 in p).
+  (2^-12 + 2 e) W, e = head_dim * 2^-24 * |scale| * max_j sum_t |q_t k_jt|:
+              each score is an fp32 sum of head_dim exact products, off by
+              at most e (times log2 e, which the base-2 exponent turns back
+              into a relative error of e in p), once in O's numerator and
+              once in its normalizer; 2^-12 for the hardware exp2.
 lse: the fp32 score error bound (head_dim * 2^-24 * scale * sum_t |q_t k_t|
 at the row's largest) plus 2^-20 (1 + |lse|) for exp2, log2 and the sums.
 """
@@ -51,12 +54,13 @@ def check(Q, K, V, causal, scale, got_O, got_L, heads=None, rows=None):
         r = np.arange(Qf.shape[1]) if rows is None else np.asarray(rows)
         O, L = oracle.attention_rows(Qf[h], Kf[h], Vf[h], r, scale, causal)
         W, _ = oracle.attention_rows(Qf[h], Kf[h], np.abs(oracle.widen(Vf[h])), r, scale, causal)
-        tol = 2.0 ** -8 * W + 2.0 ** -9 * np.abs(O) + 2.0 ** -12 * W + 1e-30
+        qa, ka = np.abs(oracle.widen(Qf[h][r])), np.abs(oracle.widen(Kf[h]))
+        smax = (qa @ ka.T).max(axis=1) * abs(scale)
+        e = (Qf.shape[-1] * 2.0 ** -24 * smax)[:, None]
+        tol = 2.0 ** -8 * W + 2.0 ** -9 * np.abs(O) + (2.0 ** -12 + 2 * e) * W + 1e-30
         err = np.abs(gO[h][r] - O)
         worst = max(worst, float((err / tol).max()))
         assert np.all(err <= tol), (h, float((err / tol).max()))
-        qa, ka = np.abs(oracle.widen(Qf[h][r])), np.abs(oracle.widen(Kf[h]))
-        smax = (qa @ ka.T).max(axis=1) * abs(scale)
         tol_l = Qf.shape[-1] * 2.0 ** -24 * smax + 2.0 ** -20 * (1 + np.abs(L))
         assert np.all(np.abs(gL[h][r] - L) <= tol_l), (h, float((np.abs(gL[h][r] - L) / tol_l).max()))
     return worst

@@ -241,23 +241,36 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
       }
     }
 
-    // 2. Online softmax (base 2). Masked scores are -inf.
-    const bool need_mask = kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
+    // 2. Online softmax (base 2). Masked scores are -inf; the mask is one
+    // uniform branch (the last key block, and blocks on the causal diagonal).
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[h][v] *= scale_log2;
+    if (kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave)) {
+      const int lim = causal ? min(n_kv - 1, query) : n_kv - 1;  // last visible key
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
+          s[h][v] = key > lim ? -INFINITY : s[h][v];
+        }
+    }
     float bmax = -INFINITY;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float x = s[h][v] * scale_log2;
-        if (need_mask) {
-          const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
-          if (key >= n_kv || (causal && key > query)) x = -INFINITY;
-        }
-        s[h][v] = x;
-        bmax = fmaxf(bmax, x);
-      }
+      for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
     bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    const float m_new = fmaxf(m_run, bmax);
+    // The reference maximum moves only when the block's maximum exceeds it
+    // by more than 8 (in log2 units): until then p = 2^(x - m) stays below
+    // 256, which fp32 sums and bf16 operands carry without loss, and O and l
+    // remain scaled by the same m, so the result is unchanged. O is then
+    // rescaled in few blocks instead of most (with 32 queries per wave, one
+    // of them raises its exact maximum in most blocks).
+    constexpr float kSlack = 8.0f;
+    const float m_new = bmax > m_run + kSlack ? bmax : m_run;
     const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
     float psum = 0.f;
