@@ -5,8 +5,8 @@
 // LLM course ch. 15 "GPU", §15.6 table of GEMM techniques):
 //   * one workgroup owns a BM x BN tile of C (256 x 256, or 128 x 128 when a
 //     product has too few large tiles to occupy the CUs) and walks K in steps
-//     of BK, from a start staggered by up to seven steps between neighbouring
-//     workgroups (spreads the L2 channels a step's loads hit);
+//     of BK, from a start staggered by up to fifteen steps between
+//     neighbouring workgroups (spreads the L2 channels a step's loads hit);
 //   * each step copies a BM x BK slice of A and a BK x BN slice of B from HBM
 //     into LDS with 16-byte row-contiguous loads that write LDS directly
 //     (global_load_lds), so the copy costs no registers and no LDS stores;
@@ -281,15 +281,16 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
   const int full_steps = K / T::BK;  // steps whose BK k are all in range
   // Staggered start: the full steps run from step rot and wrap round (the
   // partial step stays last). Workgroups are dealt round-robin to the eight
-  // XCDs, so blockIdx/8 numbers the workgroups of one XCD; eight neighbours
-  // there start up to seven steps apart. Rows of A (and of an N x K B) lie
+  // XCDs, so blockIdx/8 numbers the workgroups of one XCD; sixteen
+  // neighbours there start up to fifteen steps apart (4096^3 with B stored
+  // N x K: 150 us with eight, 137 us with sixteen). Rows of A (and of an N x K B) lie
   // K*2 bytes apart, so with one common start every line a step fetches sits
   // at the same offset of its row and the requests crowd into a few L2
   // channels; a small stagger spreads them while workgroups that share
   // operand rows stay within a few steps of each other, which keeps their
   // reuse in L2 (a stagger over the whole K range loses it and is slower).
   const int rot = full_steps > 0
-                      ? static_cast<int>(((blockIdx.x >> 3) & 7u) % static_cast<unsigned>(full_steps))
+                      ? static_cast<int>(((blockIdx.x >> 3) & 15u) % static_cast<unsigned>(full_steps))
                       : 0;
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
