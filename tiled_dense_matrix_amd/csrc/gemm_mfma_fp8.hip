@@ -383,12 +383,12 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
 #pragma unroll
   for (int j = 0; j < T::kFragN; ++j) b[0][j] = frag_b(lds, j, 0);
 
+  read_scales(0);
   int cur = 0;
   for (int t = 0; t < steps; ++t) {
     const int nxt = cur + 1 == S ? 0 : cur + 1;
     // Step t+S-1 goes into the slot step t-1 used, which every wave finished
     // reading before the barrier that ended step t-1.
-    read_scales(cur);
     const int kq = step_k0(t) % kSpanK / 32;  // first block of this step in its word
     issue(t + S - 1, cur == 0 ? S - 1 : cur - 1, false);
 #pragma unroll
@@ -435,6 +435,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_fp8_kernel(
         for (int i = 0; i < T::kFragM; ++i) a[i] = frag_a(rb, i, 0);
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j) b[n][j] = frag_b(rb, j, 0);
+        // Its scale words too, so that its first MFMAs do not wait on them.
+        read_scales(nxt);
       }
     }
     if constexpr (T::kSub % 2 == 1) {  // the next step's B fragments are in b[1]
