@@ -8,11 +8,13 @@ tdm_gemm_bf16_f32acc_path, which with the auto path are gemm_f32 /
 gemm_bf16_f32acc) on one set of synthetic inputs already resident in HBM:
 cost model and path choice on the host, then the tiled kernel (tile
 schedule, coalesced loads, LDS staging, pipelined K loop, MFMA/FMA
-accumulation, C write-back). The square fp32 4096 product runs on the
-vector-ALU kernel by default; the matrix-core kernel that the auto path
-picks for it is then timed as well and reported under config.auto_path
-(--path mfma makes it the main measurement). Every other workload runs on
-the auto path; bf16_mlp_gelu is the MLP product finished in the kernel (+
+accumulation, C write-back). With no flags the workload is the square bf16
+8192 product (bf16 in, fp32 accumulate and out) on the matrix cores, the
+largest square product of the measured set. The square fp32 4096 product
+(--workload f32_4096) runs on the vector-ALU kernel; the matrix-core kernel
+that the auto path picks for it is then timed as well and reported under
+config.auto_path (--path mfma makes it the main measurement). Every other
+workload runs on the auto path; bf16_mlp_gelu is the MLP product finished in the kernel (+
 bias, GELU, bf16 output, through gemm_bf16_epilogue), and its line also
 times the same steps unfused (config.unfused).
 Consecutive steps rotate over several copies of (A, B, C) whose total size
@@ -20,8 +22,11 @@ exceeds the 256 MB last-level cache, so every step reads its operands from
 HBM.
 
 The timed region is bracketed by device synchronisation, with HIP events
-recorded on the stream the kernels are launched on. One JSON line is
-printed; besides the throughput it carries:
+recorded on the stream the kernels are launched on. It is also the only
+region a profiler started with `rocprofv3 --selected-regions` records
+(roctxProfilerResume before its first launch, roctxProfilerPause after its
+last), so a kernel trace of the same command covers exactly the timed
+launches. One JSON line is printed; besides the throughput it carries:
   roofline      achieved rate of the product's kernel (algorithmic FLOPs or
                 bytes per launch / average launch time) against MI355X's
                 published peak for the bound that applies; `traffic` is the
@@ -66,7 +71,7 @@ KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launc
     "mfma_fp8": ("mfma_fp8_kernel", "gemm_mfma_fp8.hip", ["mfma_fp8_kernel"]),
     "attention": ("attention_fwd_kernel", "attention_fwd.hip", ["attention_fwd_kernel"]),
 }
-DEFAULT_WORKLOAD = "f32_4096"
+DEFAULT_WORKLOAD = "bf16_8192"
 # The path each workload is specified on when --path is not given: the square
 # fp32 4096 product is the register- and LDS-tiled vector-ALU kernel; the
 # others take the library's own choice (matrix cores, or the streaming path
@@ -103,6 +108,45 @@ def src_digest(fname: str) -> str:
     path = os.path.join(ROOT, "tiled_dense_matrix_amd", "csrc", fname)
     with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+class ProfilerRegion:
+    """roctxProfilerResume / roctxProfilerPause of the ROCm profiler SDK.
+
+    Under `rocprofv3 --selected-regions` only the launches between the two
+    calls are recorded; without a profiler the calls do nothing. When the
+    library cannot be loaded the region is a no-op too."""
+
+    def __init__(self):
+        import ctypes
+        self._lib = None
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                lib = ctypes.CDLL(name)
+            except OSError:
+                continue
+            lib.roctxProfilerResume.argtypes = [ctypes.c_uint64]
+            lib.roctxProfilerPause.argtypes = [ctypes.c_uint64]
+            self._lib = lib
+            break
+
+    def resume(self):
+        if self._lib is not None:
+            self._lib.roctxProfilerResume(0)
+
+    def pause(self):
+        if self._lib is not None:
+            self._lib.roctxProfilerPause(0)
+
+
+REGION = None
+
+
+def timed_region():
+    global REGION
+    if REGION is None:
+        REGION = ProfilerRegion()
+    return REGION
 
 
 def traffic_record(kernels, src: str, workload: str):
@@ -247,17 +291,25 @@ def main():
         torch.cuda.synchronize()
         start = torch.cuda.Event(enable_timing=True)
         end = torch.cuda.Event(enable_timing=True)
+        region = timed_region() if profiled else None
+        if region:
+            region.resume()
         start.record(stream)
         for i in range(args.steps):
             step(args.warmup + i)
         end.record(stream)
         torch.cuda.synchronize()
+        if region:
+            region.pause()
         return start.elapsed_time(end) / args.steps
+
+    profiled = True  # only the main measurement is the profiler's region
 
     def timed(p) -> float:
         return time_steps(lambda i: call(i, p))
 
     ms = timed(path)
+    profiled = False
 
     roof = tdm.gemm_roofline(kind, w.M, w.N, w.K)
     # Bytes with every array crossing HBM once: A and B read, the bias read,
@@ -291,10 +343,18 @@ def main():
     if path != tdm.Path.AUTO and auto_choice != pname:
         ms_auto = timed(tdm.Path.AUTO)
         tf_auto = roof.flops / (ms_auto * 1e-3) / 1e12
-        peak_auto = PEAK["mfma_f32" if w.kind == "f32" else "mfma_bf16"] \
-            if auto_choice == "mfma" else PEAK["alu_f32"]
+        gb_auto = alg_bytes / (ms_auto * 1e-3) / 1e9
+        # the bound of the path the library chose, as for the main measurement
+        if auto_choice == "skinny":
+            bound_auto, ach_auto, peak_auto = "hbm", gb_auto, PEAK["hbm"]
+        elif auto_choice == "mfma":
+            bound_auto, ach_auto = "mfma", tf_auto
+            peak_auto = PEAK["mfma_f32" if w.kind == "f32" else "mfma_bf16"]
+        else:
+            bound_auto, ach_auto, peak_auto = "alu", tf_auto, PEAK["alu_f32"]
         auto_info = {"path": auto_choice, "ms_per_call": round(ms_auto, 6),
-                     "tflops": round(tf_auto, 3), "roofline_frac": round(tf_auto / peak_auto, 4)}
+                     "tflops": round(tf_auto, 3), "bound": bound_auto,
+                     "roofline_frac": round(ach_auto / peak_auto, 4)}
 
     # The same epilogue unfused: this library's product with fp32 output, then
     # the bias add, GELU and bf16 conversion as separate torch operations.
@@ -393,7 +453,7 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def time_calls(step, warmup: int, steps: int, stream) -> float:
+def time_calls(step, warmup: int, steps: int, stream, profiled: bool = False) -> float:
     """Average ms per step(i) over `steps` calls after `warmup`, with events
     on the stream the kernels run on."""
     import torch
@@ -402,11 +462,16 @@ def time_calls(step, warmup: int, steps: int, stream) -> float:
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    region = timed_region() if profiled else None
+    if region:
+        region.resume()
     start.record(stream)
     for i in range(steps):
         step(warmup + i)
     end.record(stream)
     torch.cuda.synchronize()
+    if region:
+        region.pause()
     return start.elapsed_time(end) / steps
 
 
@@ -474,7 +539,7 @@ def main_fp8(args, w):
         a, b, s_a, s_b, c = sets[i % rot]
         tdm.gemm_fp8(a, b, fa, fb, s_a, s_b, D=c, gelu=w.gelu, stream=stream)
 
-    ms = time_calls(call, args.warmup, args.steps, stream)
+    ms = time_calls(call, args.warmup, args.steps, stream, profiled=True)
     flops = 2.0 * w.M * w.N * w.K
     alg_bytes = A.size + B.size + scale_bytes + out_size * w.M * w.N
     tflops = flops / (ms * 1e-3) / 1e12
@@ -599,7 +664,7 @@ def main_attention(args, w):
                                1 if w.causal else 0, stream.cuda_stream)
         assert st == 0, st
 
-    ms = time_calls(call, args.warmup, args.steps, stream)
+    ms = time_calls(call, args.warmup, args.steps, stream, profiled=True)
     flops = w.flops
     alg_bytes = 4 * Q.size * 2 + bh * w.seq * 4  # Q, K, V read once; O and lse written
     tflops = flops / (ms * 1e-3) / 1e12

@@ -12,13 +12,29 @@ from tiled_dense_matrix_amd import inputs
 DIGESTS = os.path.join(os.path.dirname(__file__), "golden", "input_digests.json")
 
 
-def test_digests_are_stable():
+def _golden_digests():
     with open(DIGESTS) as fh:
-        want = json.load(fh)
-    for name, d in want.items():
-        A, B = inputs.make_inputs(name)
-        assert inputs.digest(A) == d["A"], name
-        assert inputs.digest(B) == d["B"], name
+        return json.load(fh)
+
+
+def _digest_module():
+    import importlib.util
+    path = os.path.join(os.path.dirname(__file__), "golden", "make_input_digests.py")
+    spec = importlib.util.spec_from_file_location("make_input_digests", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_every_workload_has_a_digest():
+    assert sorted(_golden_digests()) == sorted(_digest_module().names())
+
+
+@pytest.mark.parametrize("name", sorted(_golden_digests()))
+def test_digests_are_stable(name):
+    """Every array of every workload (operands, block scales, bias, Q/K/V)
+    hashes to the committed value: the recipe is pinned at full size."""
+    assert _digest_module().workload_digests(name) == _golden_digests()[name], name
 
 
 def test_workload_shapes_and_types():

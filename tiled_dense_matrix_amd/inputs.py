@@ -50,6 +50,7 @@ __all__ = [
     "uniform_fp32",
     "normal_bf16",
     "small_int_matrix",
+    "make_integer_inputs",
     "pm_one_vector",
     "sample_tiles",
     "digest",
@@ -261,6 +262,24 @@ def small_int_matrix(rng: np.random.Generator, shape, lo: int = -3, hi: int = 3,
     """Integer values in [lo, hi], stored as fp32 or bf16 bits (both exact)."""
     x = rng.integers(lo, hi + 1, size=shape).astype(np.float32)
     return x if kind == "f32" else fp32_to_bf16_bits(x)
+
+
+def make_integer_inputs(w: Workload | str, lo: int = -3, hi: int = 3):
+    """(A, B) with the workload's shapes, storage types and B layout, but
+    i.i.d. integers in [lo, hi] from a PCG64 generator seeded with (seed, 2)
+    (A drawn first). With |values| <= 3 every partial sum of a product with
+    K <= 8192 is an integer of magnitude at most 9K < 2^24, exact in fp32
+    under any summation order, so any correct kernel returns the exact
+    product bit for bit."""
+    if isinstance(w, str):
+        w = WORKLOADS[w]
+    if w.kind not in ("f32", "bf16"):
+        raise ValueError(w.kind)
+    rng = np.random.default_rng((w.seed, 2))
+    A = small_int_matrix(rng, (w.M, w.K), lo, hi, kind=w.kind)
+    B = small_int_matrix(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N), lo, hi,
+                         kind=w.kind)
+    return A, B
 
 
 def pm_one_vector(rng: np.random.Generator, n: int) -> np.ndarray:
