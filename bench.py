@@ -222,6 +222,9 @@ def main():
               "supported: this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    # The profiler's region markers register with the profiler when their
+    # library loads, which has to happen before the GPU runtime starts.
+    timed_region()
     import torch
     import tiled_dense_matrix_amd as tdm
     from tiled_dense_matrix_amd import inputs

@@ -15,13 +15,15 @@
  *     notes, §4.1, on row-major storage). There are no leading dimensions;
  *     a strided or transposed view must be made contiguous by the caller.
  *   - A, B and C are DEVICE pointers on the current HIP device, owned by the
- *     caller. The only memory the library allocates is the small-M path's
- *     workspace for partial sums, one per device and stream (about 8 MB for
- *     M <= 16, N = 8192), allocated on the first small-M call on that stream
- *     and kept until the process ends. Calls on different streams therefore
- *     do not share it. Up to 32 streams per device keep their own; a call
- *     from a 33rd stream reuses the least recently used one after waiting
- *     for the device to go idle (hipDeviceSynchronize).
+ *     caller. No call allocates memory or waits for the device. The small-M
+ *     path (M <= 16, B K x N) splits K over workgroups and adds their
+ *     partial sums in a second kernel; the partial sums live in static
+ *     device memory of the library (8 buffers of 4 MB per device, present
+ *     from its first use until the process ends). The first eight streams
+ *     that run that path on a device each own one buffer, so calls on
+ *     different streams never share one; on any further stream the call
+ *     runs the matrix-core kernel instead (the same product, summed in
+ *     another order).
  *   - A and B are read only. C is overwritten (there is no alpha/beta). C
  *     must not overlap A or B.
  *   - Element sizes: fp32 = 4 bytes; bf16 = 2 bytes passed as raw uint16_t
@@ -39,17 +41,17 @@
  *   - a matrix with 2^31 or more elements, or a forced path that cannot run
  *     the given shape/alignment                         -> TDM_ERROR_NOT_SUPPORTED
  *   - no HIP device is visible                          -> TDM_ERROR_NO_DEVICE
- *   - a HIP call failed (kernel launch, the small-M path's workspace
- *     allocation or the kernels' LDS attribute)         -> TDM_ERROR_LAUNCH
+ *   - a HIP call failed (kernel launch, the address of the small-M path's
+ *     buffers or the kernels' LDS attribute)             -> TDM_ERROR_LAUNCH
  *   - M == 0 or N == 0: nothing to do, TDM_SUCCESS without any HIP call.
  *   - K == 0: C is filled with zeros (the empty sum), TDM_SUCCESS.
  *
  * Threading: the calls may be made from several host threads; work on one
  * stream is ordered as usual. The only mutable global state is the small-M
- * workspace table (guarded by a mutex) and a per-device record of the
- * kernels' LDS attribute. A graph captured from a stream keeps using that
- * stream's workspace when replayed: do not replay it concurrently with other
- * small-M work on the stream it was captured from.
+ * path's table of which stream owns which buffer (guarded by a mutex) and a
+ * per-device record of the kernels' LDS attribute. A graph captured from a
+ * stream keeps using that stream's buffer when replayed: do not replay it
+ * concurrently with other small-M work on the stream it was captured from.
  */
 #ifndef TDM_H
 #define TDM_H
@@ -207,8 +209,8 @@ typedef enum tdm_fp8_format {
  * a NULL operand (K > 0) or D, exactly one scale pointer NULL, a misaligned
  * D/bias/residual, or D overlapping an input (residual == D is allowed);
  * TDM_ERROR_NOT_SUPPORTED for K not a multiple of 32, A or B not 16-byte
- * aligned, or M*K or N*K of 2^32 bytes or more. M == 0 or N == 0: nothing
- * is done; K == 0: D = epilogue(0). */
+ * aligned, or a matrix (A, B or D) of 2^31 elements or more. M == 0 or N ==
+ * 0: nothing is done; K == 0: D = epilogue(0). */
 TDM_API tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_scale,
                             const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale,
                             void* D, tdm_dtype d_type, const void* bias, const void* residual,
@@ -232,13 +234,13 @@ TDM_API int tdm_fp8_supports(int64_t M, int64_t N, int64_t K, int misalign_a, in
  *      NULL;
  *   scale: usually 1/sqrt(head_dim); causal != 0 masks key j > query i
  *      (requires n_q == n_kv).
- * Device pointers, owned by the caller. Errors: TDM_ERROR_INVALID_VALUE for
- * a negative size, n_kv == 0 with queries to compute, a NULL or misaligned
- * pointer (O 8-byte, lse 4-byte aligned), a non-finite scale, causal with
- * n_q != n_kv, or O overlapping Q, K, V or lse; TDM_ERROR_NOT_SUPPORTED for
- * head_dim other than 64 or 128, Q, K or V not 16-byte aligned, more than
- * 65535 batch_heads, or a sequence of 2^22 rows or more. batch_heads == 0 or
- * n_q == 0: nothing is done. */
+ * Device pointers, owned by the caller. Errors: TDM_ERROR_INVALID_VALUE for a
+ * negative size, n_kv == 0 with queries to compute, a NULL or misaligned
+ * pointer (O 8-byte, lse 4-byte aligned), a non-finite scale, causal with n_q
+ * != n_kv, O overlapping Q, K, V or lse, or lse overlapping Q, K or V;
+ * TDM_ERROR_NOT_SUPPORTED for head_dim other than 64 or 128, Q, K or V not
+ * 16-byte aligned, more than 65535 batch_heads, or a sequence of 2^22 rows or
+ * more. batch_heads == 0 or n_q == 0: nothing is done. */
 TDM_API tdm_status attention_fwd(const uint16_t* Q, const uint16_t* K, const uint16_t* V,
                                  uint16_t* O, float* lse, int64_t batch_heads, int64_t n_q,
                                  int64_t n_kv, int64_t head_dim, float scale, int causal,

@@ -332,6 +332,9 @@ def test_attention_validation():
     assert call(causal=1, nkv=64) == S.ERROR_INVALID_VALUE
     assert call(O=FAKE + 1024) == S.ERROR_INVALID_VALUE        # O overlaps Q
     assert call(lse=FAKE_C + 64) == S.ERROR_INVALID_VALUE      # lse inside O
+    assert call(lse=FAKE + 256) == S.ERROR_INVALID_VALUE       # lse inside Q
+    assert call(lse=FAKE_B + 1024) == S.ERROR_INVALID_VALUE    # lse inside K
+    assert call(lse=FAKE_BIAS) == S.ERROR_INVALID_VALUE        # lse at V
     assert call(d=96) == S.ERROR_NOT_SUPPORTED
     assert call(K=FAKE_B + 8) == S.ERROR_NOT_SUPPORTED          # not 16-byte aligned
     assert call(bh=65536) == S.ERROR_NOT_SUPPORTED

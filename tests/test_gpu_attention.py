@@ -165,3 +165,35 @@ def test_zero_scale_with_the_causal_mask_averages_the_visible_values():
     assert np.isfinite(O).all()
     assert np.all(np.abs(O[0, 0] - mean) <= 2.0 ** -8 * np.abs(mean) + 2.0 ** -9 * np.abs(v).max())
     assert np.allclose(L[0, 0], np.log(np.arange(1, n + 1)), atol=1e-5)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_infinite_value_in_the_last_key_row_of_a_ragged_block(d):
+    """n_kv = 100 leaves 28 padded rows in the second 64-key block, which
+    hold copies of key row 99. With +Inf in one element of V[99] every query
+    sees that key with a nonzero probability, so O is +Inf in that column
+    and finite elsewhere, as the fp64 definition gives; a padded copy of the
+    row taken with probability 0 must not turn it into NaN."""
+    rng = np.random.default_rng(90 + d)
+    Q, K, V = (inputs.normal_bf16(rng, (1, 1, n, d), 1.0) for n in (40, 100, 100))
+    col = 5
+    V[0, 0, 99, col] = 0x7F80  # bf16 +Inf
+    log(f"case attention Inf in V row n_kv-1, d={d}")
+    scale = d ** -0.5
+    got_O, _ = run(Q, K, V, False, scale)
+    R, _ = oracle.attention(Q, K, V, scale)
+    assert np.all(np.isposinf(R[0, 0, :, col])) and np.all(np.isfinite(np.delete(R, col, axis=-1)))
+    assert np.array_equal(np.isposinf(got_O), np.isposinf(R))
+    assert not np.isnan(got_O).any()
+    # the other columns: the bound of the module docstring, computed with
+    # V's infinite element set to 0 (it does not reach them)
+    fin = np.delete(np.arange(d), col)
+    V2 = V.copy()
+    V2[0, 0, 99, col] = 0
+    r = np.arange(40)
+    O_ref, _ = oracle.attention_rows(Q[0, 0], K[0, 0], V2[0, 0], r, scale)
+    W, _ = oracle.attention_rows(Q[0, 0], K[0, 0], np.abs(oracle.widen(V2[0, 0])), r, scale)
+    smax = (np.abs(oracle.widen(Q[0, 0])) @ np.abs(oracle.widen(K[0, 0])).T).max(axis=1) * scale
+    e = (d * 2.0 ** -24 * smax)[:, None]
+    tol = 2.0 ** -8 * W + 2.0 ** -9 * np.abs(O_ref) + (2.0 ** -12 + 2 * e) * W + 1e-30
+    assert np.all(np.abs(got_O[0, 0][:, fin] - O_ref[:, fin]) <= tol[:, fin])

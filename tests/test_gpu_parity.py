@@ -193,7 +193,7 @@ def test_run_to_run_bitwise_determinism(kind, shape):
     Ad, Bd = to_device(A), to_device(B)
     for p in supported_paths(kind, M, N, K):
         ref = run(kind, Ad, Bd, p).clone()
-        for _ in range(5):
+        for _ in range(100):
             assert torch.equal(run(kind, Ad, Bd, p), ref), p.name
 
 
@@ -210,7 +210,7 @@ def test_nondefault_stream():
 
 
 def test_small_m_calls_on_two_streams_at_once():
-    """The split-K partial sums live in a per-stream workspace: calls queued on
+    """The split-K partial sums live in a per-stream buffer: calls queued on
     two streams at the same time must not disturb each other."""
     log("case small-M two streams")
     rng = np.random.default_rng(79)
@@ -229,14 +229,34 @@ def test_small_m_calls_on_two_streams_at_once():
         assert np.array_equal(C, gpu_product("bf16", A, B, P.SKINNY))
 
 
+def test_small_m_first_call_on_a_fresh_stream():
+    """A stream's first small-M call needs no allocation and no device-wide
+    wait: enqueued behind other work on that stream, it returns at once and
+    the result is right."""
+    log("case small-M fresh stream")
+    A, B = random_inputs("bf16", 16, 2048, 4096, 81)
+    Ad, Bd = to_device(A), to_device(B)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        C = run("bf16", Ad, Bd, P.SKINNY, stream=s)
+    s.synchronize()
+    check_full("bf16", A, B, C.cpu().numpy(), "fresh stream")
+
+
 def test_small_m_calls_on_more_streams_than_workspace_slots():
-    """34 streams: the 33rd and 34th take over the least recently used slots."""
+    """34 streams: the first eight streams of the process that call the
+    small-M path own a partial-sum buffer each; calls on the others run the
+    matrix-core kernel. Every output equals one of the two paths' results
+    bit for bit, and at least 26 of the 34 take the matrix-core kernel."""
     import ctypes
     log("case small-M 34 streams")
     hip = ctypes.CDLL("libamdhip64.so")
     A, B = random_inputs("bf16", 16, 1024, 2048, 80)
     Ad, Bd = to_device(A), to_device(B)
     ref = gpu_product("bf16", A, B, P.SKINNY)
+    ref_mfma = gpu_product("bf16", A, B, P.MFMA)
+    assert not np.array_equal(ref, ref_mfma)  # the two paths are told apart
     outs = [torch.empty((16, 1024), device="cuda") for _ in range(34)]
     handles = []
     try:
@@ -247,15 +267,20 @@ def test_small_m_calls_on_more_streams_than_workspace_slots():
         torch.cuda.synchronize()
         for h, Cd in zip(handles, outs):
             run("bf16", Ad, Bd, P.SKINNY, Cd, stream=h.value)
-        for h, Cd in zip(handles, outs):  # again, now with every slot taken
+        for h, Cd in zip(handles, outs):  # again, now with every buffer taken
             run("bf16", Ad, Bd, P.SKINNY, Cd, stream=h.value)
         torch.cuda.synchronize()
     finally:
         torch.cuda.synchronize()
         for h in handles:
             hip.hipStreamDestroy(h)
+    took_mfma = 0
     for Cd in outs:
-        assert np.array_equal(Cd.cpu().numpy(), ref)
+        C = Cd.cpu().numpy()
+        assert np.array_equal(C, ref) or np.array_equal(C, ref_mfma)
+        took_mfma += int(np.array_equal(C, ref_mfma))
+    assert took_mfma >= 34 - 8
+    check_full("bf16", A, B, ref_mfma, "fallback")
 
 
 def test_misaligned_pointers():

@@ -37,7 +37,9 @@
 // active cycles; now 0).
 //
 // Ragged sizes: key rows past n_kv load row n_kv - 1 and are masked out
-// (score -inf); query rows past n_q load row n_q - 1 and are not stored.
+// (score -inf; their V rows are zeroed in LDS, so an infinite value in row
+// n_kv - 1 cannot turn into NaN through a zero probability); query rows past
+// n_q load row n_q - 1 and are not stored.
 // Causal (key j > query i masked; n_q == n_kv): key blocks wholly above the
 // diagonal are skipped, and the query blocks run heaviest first (work_item).
 #include <hip/hip_runtime.h>
@@ -226,6 +228,19 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     LDS_PTR(const uint8_t) kblk = lds + cur * T::kStage;
     LDS_PTR(const uint8_t) vblk = kblk + T::kBlock;
     const int kb0 = t * kBKV;
+    if (kb0 + kBKV > n_kv) {
+      // The block's rows past n_kv hold copies of row n_kv - 1. Their
+      // probabilities are 0, but 0 times an infinite value of V would be
+      // NaN, so their V rows are zeroed (whole rows: the swizzle only
+      // permutes chunks within a row).
+      const int first = n_kv - kb0;
+      LDS_PTR(uint8_t) vw = lds + cur * T::kStage + T::kBlock;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      for (int i = tid; i < (kBKV - first) * (T::kRow / 16); i += kThreads)
+        *(LDS_PTR(u32x4))(vw + (first + i / (T::kRow / 16)) * T::kRow +
+                          (i % (T::kRow / 16)) * 16) = zero;
+      __syncthreads();
+    }
 
     // 1. S^T for the two 32-key halves.
     f32x16 s[2];

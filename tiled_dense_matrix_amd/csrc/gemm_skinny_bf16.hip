@@ -24,11 +24,18 @@
 //   * the workgroups of one column block each produce a partial 16 x 256
 //     sum and write it to a workspace; a second, small kernel adds the
 //     partials of each output in slice order and writes C, so the result is
-//     bitwise reproducible. (Combining them inside the first kernel needs
-//     device-coherent stores, an arrival counter and device-coherent loads
-//     by the last workgroup; those round trips sit on the critical path and
-//     measured several times slower than a second launch.) With a single
-//     slice the partial goes straight to C.
+//     bitwise reproducible. (Combining them inside the first kernel needs a
+//     device-scope release by every workgroup, which writes back its XCD's
+//     whole L2, or device-coherent stores, an arrival counter and
+//     device-coherent loads by the last workgroup; both measured slower than
+//     a second launch.) With a single slice the sums go straight to C,
+//     finished by the epilogue in the first kernel.
+//   * the workspace is static device memory of the library (no allocation
+//     at call time): a table of kSlots buffers of 4 MB per device, one per
+//     stream that calls this path, so calls on different streams never
+//     share one and calls on one stream are ordered by the stream. A stream
+//     that finds the table full runs the matrix-core kernel instead (same
+//     result up to summation order; no workspace).
 // A K that is not a multiple of 32 has its last step loaded through
 // registers with every k beyond K set to zero. Rows of A at or beyond M
 // are copied from row M-1; their products reach only rows of C that are not
@@ -161,8 +168,8 @@ __device__ __forceinline__ s16x4 read_tr(LDS_PTR(const uint8_t) stage, int k_bas
 }
 
 __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, float* __restrict__ C,
-    int M, int N, int K, int slices, int slice_steps, float* __restrict__ partials) {
+    const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, void* C, int M, int N,
+    int K, int slices, int slice_steps, float* __restrict__ partials, Epilogue epi) {
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[];
   LDS_PTR(uint8_t) lds = (LDS_PTR(uint8_t))lds_raw;
 
@@ -230,14 +237,15 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
 
   // Element v of accumulator q: row 4*(lane/16) + v, column
   // kColsPerWave*wave + 16q + lane%16. Without a partial-sum buffer (one
-  // slice, no epilogue) the sums are the outputs.
+  // slice) the sums are the outputs, finished by the epilogue here.
   if (partials == nullptr) {
 #pragma unroll
     for (int q = 0; q < kAcc; ++q)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = 4 * g + v, col = n0 + wave * kColsPerWave + q * 16 + m;
-        if (row < M && col < N) C[static_cast<int64_t>(row) * N + col] = acc[q][v];
+        if (row < M && col < N)
+          epi_store(C, static_cast<int64_t>(row) * N + col, col, acc[q][v], epi);
       }
     return;
   }
@@ -251,9 +259,8 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_bf16_kernel(
       mine[(4 * g + v) * kBlockN + wave * kColsPerWave + q * 16 + m] = acc[q][v];
 }
 
-// C[row][col] = sum over slices (in slice order) of the partials; with kEpi
-// the sum is finished by the fused epilogue (C is then the epilogue's D).
-template <bool kEpi>
+// C[row][col] = sum over slices (in slice order) of the partials, finished
+// by the fused epilogue (an empty one stores the fp32 sum).
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ partials,
                                                             void* C, int M, int N, int slices,
                                                             Epilogue epi) {
@@ -273,62 +280,59 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restr
     for (int u = 0; u < 8; ++u) sum += v[u];
   }
   for (; s < slices; ++s) sum += p[s * kPer];
-  const int64_t idx = static_cast<int64_t>(row) * N + col;
-  if constexpr (kEpi)
-    epi_store(C, idx, col, sum, epi);
-  else
-    static_cast<float*>(C)[idx] = sum;
+  epi_store(C, static_cast<int64_t>(row) * N + col, col, sum, epi);
 }
 
-// Workspace for the partial sums: one buffer per (device, stream), so calls
-// on different streams never share one and calls on one stream are ordered
-// by the stream. A buffer grows on demand and is kept until the process ends
-// (a kernel may still use the old one when it grows, so that one is never
-// freed). Up to kStreamSlots streams per device keep their own buffer; a call
-// from a further stream takes over the least recently used slot after waiting
-// for the device to go idle (hipDeviceSynchronize), since that slot's stream
-// may still have work in flight.
-constexpr int kStreamSlots = 32;
-struct StreamSlot {
-  hipStream_t stream = nullptr;  // compared only, never used
-  void* ptr = nullptr;
-  size_t bytes = 0;
-  uint64_t last_use = 0;  // 0: free
-};
-struct Workspace {
-  std::mutex mu;
-  uint64_t clock = 0;
-  StreamSlot slot[64][kStreamSlots];
-};
-Workspace g_ws;
+// Workspace for the partial sums. A launch has at most kTargetGroups
+// workgroups when it splits K (blocks * slices <= kTargetGroups), each
+// writing one kPer-float partial block, so one buffer of kSlotFloats floats
+// (4 MB) holds any call. The buffers are a static array of the library's
+// code object, present on every device the library runs on from the first
+// use until the process ends; nothing is allocated at call time.
+constexpr int kSlots = 8;
+constexpr size_t kSlotFloats = static_cast<size_t>(kTargetGroups) * kPer;
+__device__ __align__(256) float g_partials[kSlots * kSlotFloats];
 
-hipError_t workspace(hipStream_t s, size_t need, void** out) {
+// Per-device table: slot i belongs to the stream that first claimed it, for
+// the rest of the process (a stream handle is only compared, never used).
+// Calls on one stream are ordered by that stream, so its slot is never used
+// by two launches at once.
+constexpr int kMaxDevices = 64;
+struct SlotTable {
+  std::mutex mu;
+  float* base = nullptr;  // device address of g_partials on this device
+  int used = 0;
+  hipStream_t owner[kSlots] = {};
+};
+SlotTable g_tables[kMaxDevices];
+
+// The partial-sum buffer of stream s on the current device, or nullptr when
+// all kSlots are owned by other streams.
+hipError_t stream_slot(hipStream_t s, float** out) {
+  *out = nullptr;
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-  std::lock_guard<std::mutex> lock(g_ws.mu);
-  StreamSlot* slots = g_ws.slot[dev];
-  StreamSlot* w = nullptr;
-  StreamSlot* lru = &slots[0];
-  for (int i = 0; i < kStreamSlots && w == nullptr; ++i) {
-    if (slots[i].last_use != 0 && slots[i].stream == s) w = &slots[i];
-    else if (slots[i].last_use < lru->last_use) lru = &slots[i];
-  }
-  if (w == nullptr) {
-    if (lru->last_use != 0 && (e = hipDeviceSynchronize()) != hipSuccess) return e;
-    w = lru;
-    w->stream = s;
-  }
-  if (w->bytes < need) {
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  SlotTable& t = g_tables[dev];
+  std::lock_guard<std::mutex> lock(t.mu);
+  if (t.base == nullptr) {
+    // The array's name is a host-side stand-in; its address on this device
+    // comes from the runtime.
     void* p = nullptr;
-    const size_t bytes = need < (size_t{8} << 20) ? (size_t{8} << 20) : need;
-    if ((e = hipMalloc(&p, bytes)) != hipSuccess) return e;
-    w->ptr = p;
-    w->bytes = bytes;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_partials))) != hipSuccess) return e;
+    t.base = static_cast<float*>(p);
   }
-  w->last_use = ++g_ws.clock;
-  *out = w->ptr;
+  for (int i = 0; i < t.used; ++i)
+    if (t.owner[i] == s) {
+      *out = t.base + i * kSlotFloats;
+      return hipSuccess;
+    }
+  if (t.used < kSlots) {
+    t.owner[t.used] = s;
+    *out = t.base + t.used * kSlotFloats;
+    ++t.used;
+  }
   return hipSuccess;
 }
 
@@ -343,46 +347,57 @@ bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
 
 namespace {
 
-template <bool kEpi>
+// Slices of K for a product with `blocks` column blocks: as many as keep
+// the grid at one round of kTargetGroups workgroups, no empty ones.
+void split(int N, int K, int* blocks, int* slices, int* slice_steps) {
+  *blocks = (N + kBlockN - 1) / kBlockN;
+  const int steps = (K + kStepK - 1) / kStepK;
+  int sl = kTargetGroups / *blocks;  // rounded down: no second round of workgroups
+  if (sl > steps) sl = steps;
+  if (sl < 1) sl = 1;
+  *slice_steps = (steps + sl - 1) / sl;
+  *slices = (steps + *slice_steps - 1) / *slice_steps;
+}
+
 hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, int N, int K,
                          const Epilogue& epi, hipStream_t s) {
   static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
   hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(skinny_bf16_kernel), kLdsBytes);
   if (e != hipSuccess) return e;
-  const int blocks = (N + kBlockN - 1) / kBlockN;
-  const int steps = (K + kStepK - 1) / kStepK;
-  int slices = kTargetGroups / blocks;  // rounded down: no second round of workgroups
-  if (slices > steps) slices = steps;
-  if (slices < 1) slices = 1;
-  const int slice_steps = (steps + slices - 1) / slices;
-  slices = (steps + slice_steps - 1) / slice_steps;  // no empty slices
-  if (slices == 1 && !kEpi)  // the sums are the outputs: no workspace
-    return launch(skinny_bf16_kernel, dim3(blocks), dim3(kThreads), kLdsBytes, s, A, B,
-                  static_cast<float*>(C), M, N, K, slices, slice_steps,
-                  static_cast<float*>(nullptr));
-  const size_t part_bytes =
-      static_cast<size_t>(blocks) * slices * kMaxM * kBlockN * sizeof(float);
-  void* ws = nullptr;
-  if ((e = workspace(s, part_bytes, &ws)) != hipSuccess) return e;
-  float* partials = static_cast<float*>(ws);
+  int blocks, slices, slice_steps;
+  split(N, K, &blocks, &slices, &slice_steps);
+  if (slices == 1)  // the sums are the outputs: no workspace
+    return launch(skinny_bf16_kernel, dim3(blocks), dim3(kThreads), kLdsBytes, s, A, B, C, M,
+                  N, K, slices, slice_steps, static_cast<float*>(nullptr), epi);
+  float* partials = nullptr;
+  if ((e = stream_slot(s, &partials)) != hipSuccess) return e;
+  // split() keeps blocks * slices <= kTargetGroups, so the partial blocks
+  // always fit a buffer; the guard keeps a future split from writing past
+  // one.
+  if (static_cast<size_t>(blocks) * slices * kPer > kSlotFloats) return hipErrorInvalidValue;
+  if (partials == nullptr) {  // every buffer belongs to another stream
+    if (mfma_bf16_supports(M, N, K, 0, 0, 0))
+      return launch_mfma_bf16_epi(A, B, false, C, M, N, K, epi, s);
+    return launch_edge_bf16_epi(A, B, false, C, M, N, K, epi, s);
+  }
   e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B,
-             static_cast<float*>(nullptr), M, N, K, slices, slice_steps, partials);
+             static_cast<void*>(nullptr), M, N, K, slices, slice_steps, partials, epi);
   if (e != hipSuccess) return e;
-  return launch(skinny_reduce_kernel<kEpi>, dim3(blocks * (kPer / 256)), dim3(256), 0, s,
-                partials, C, M, N, slices, epi);
+  return launch(skinny_reduce_kernel, dim3(blocks * (kPer / 256)), dim3(256), 0, s, partials,
+                C, M, N, slices, epi);
 }
 
 }  // namespace
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s) {
-  return launch_skinny<false>(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_skinny(A, B, C, M, N, K, Epilogue{}, s);
 }
 
 hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
                                   int M, int N, int K, const Epilogue& e, hipStream_t s) {
   if (b_nk) return launch_skinny_nk_bf16(A, B, D, M, N, K, e, s);  // gemm_skinny_nk_bf16.hip
-  return launch_skinny<true>(A, B, D, M, N, K, e, s);
+  return launch_skinny(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

@@ -10,7 +10,9 @@
 //     full K, and streams them -- one contiguous region of R*16*K*2 bytes --
 //     through a 72 KB LDS ring with global_load_lds, 256 k per step (512
 //     contiguous bytes of each row), together with the matching 16 x 256
-//     slice of A (A is M <= 16 rows; rows past M repeat row M-1);
+//     slice of A (A is M <= 16 rows; rows past M repeat row M-1). B's copies
+//     are marked non-temporal (read once), A's are not (every workgroup
+//     reads all of A);
 //   * the K loop of workgroup g starts at step g mod (K / 256) and wraps
 //     round. Rows of B lie K*2 bytes apart, so with every workgroup at the
 //     same step the reads of the whole grid pile onto the few HBM channels
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void skinny_nk_bf16_kernel(
         dma16(A + k0, off_a[j], stage + (wave + kWaves * j) * 1024);
 #pragma unroll
       for (int j = 0; j < T::kCopyB; ++j)
-        dma16(B + k0, off_b[j], stage + kStageA + (wave + kWaves * j) * 1024);
+        dma16_stream(B + k0, off_b[j], stage + kStageA + (wave + kWaves * j) * 1024);
       return;
     }
     // Partial last step, through registers: zeros beyond K.

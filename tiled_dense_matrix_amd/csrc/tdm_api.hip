@@ -272,9 +272,15 @@ tdm_status run_attention(const uint16_t* Q, const uint16_t* K, const uint16_t* V
     return TDM_ERROR_NOT_SUPPORTED;
   const uint64_t o_bytes = uint64_t(bh) * uint64_t(n_q) * uint64_t(d) * 2;
   const uint64_t kv_bytes = uint64_t(bh) * uint64_t(n_kv) * uint64_t(d) * 2;
+  const uint64_t lse_bytes = uint64_t(bh) * uint64_t(n_q) * 4;
   if (overlaps(O, o_bytes, Q, o_bytes) || overlaps(O, o_bytes, K, kv_bytes) ||
       overlaps(O, o_bytes, V, kv_bytes) ||
-      (lse != nullptr && overlaps(O, o_bytes, lse, uint64_t(bh) * uint64_t(n_q) * 4)))
+      (lse != nullptr && overlaps(O, o_bytes, lse, lse_bytes)))
+    return TDM_ERROR_INVALID_VALUE;
+  // lse is written while other workgroups still read Q, K and V.
+  if (lse != nullptr && (overlaps(lse, lse_bytes, Q, o_bytes) ||
+                         overlaps(lse, lse_bytes, K, kv_bytes) ||
+                         overlaps(lse, lse_bytes, V, kv_bytes)))
     return TDM_ERROR_INVALID_VALUE;
   tdm_status st = check_device();
   if (st != TDM_SUCCESS) return st;
