@@ -173,6 +173,24 @@ TDM_API tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B,
                                          int64_t M, int64_t N, int64_t K, tdm_path path,
                                          void* stream);
 
+/* gemm_bf16_ex that allocates nothing and keeps no per-stream state, for
+ * callers that cannot allocate device memory at call time: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of gemm_bf16_ex, and so are the
+ * kernels. The one difference: when the small-M path (M <= 16, B K x N)
+ * splits K, its partial sums go to one static 4 MB device buffer of the
+ * library per GPU (present from the first call on that GPU until the
+ * process ends), shared by every call of this entry point on that GPU,
+ * instead of the calling stream's own buffer. Calls of this entry point
+ * that overlap in time on one GPU (several streams, or graph replays)
+ * therefore race and give wrong results; calls ordered on one stream are
+ * safe. No split needs more than the 4 MB (at most 256 workgroups write 16
+ * x 256 fp32 sums each); the buffer needs no clearing between calls. */
+TDM_API tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B,
+                                        tdm_layout b_layout, void* D, tdm_dtype d_type,
+                                        const void* bias, const void* residual, int gelu,
+                                        int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Host-only: tdm_path_supports / tdm_select_path for a given layout of B
  * (TDM_LAYOUT_NK: bf16 only; 0 / TDM_PATH_EDGE for an unknown layout). */
 TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path path, int64_t M,

@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     attention_fwd,
     gemm_bf16_epilogue,
     gemm_bf16_ex,
+    gemm_bf16_ex_noalloc,
     gemm_bf16_f32acc,
     gemm_f32,
     gemm_fp8,

@@ -47,6 +47,8 @@ SIGNATURES = {
                                     ctypes.c_int, _i64, _i64, _i64, _p]),
     "tdm_gemm_bf16_ex_path": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _p,
                                              ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, _p]),
+    "gemm_bf16_ex_noalloc": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, ctypes.c_int, _p, _p,
+                                            ctypes.c_int, _i64, _i64, _i64, _p]),
     "tdm_path_supports_ex": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64,
                                             _i64, _i64, ctypes.c_int, ctypes.c_int,
                                             ctypes.c_int]),
@@ -329,6 +331,18 @@ def gemm_bf16_ex(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None, resi
     torch = _torch()
     M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual, layout)
     return _call_ex("gemm_bf16_ex", A, B, layout, D, dt, bias, residual, gelu, M, N, K, stream)
+
+
+def gemm_bf16_ex_noalloc(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None,
+                         residual=None, gelu=False, stream=None):
+    """gemm_bf16_ex through the entry point that allocates nothing: the
+    small-M K x N partial sums use the library's one static buffer per GPU
+    (calls that overlap in time on one GPU race). Pass D to keep the call
+    itself free of allocation; without D a new tensor is returned."""
+    torch = _torch()
+    M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual, layout)
+    return _call_ex("gemm_bf16_ex_noalloc", A, B, layout, D, dt, bias, residual, gelu, M, N, K,
+                    stream)
 
 
 def tdm_gemm_bf16_ex_path(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None,

@@ -293,6 +293,37 @@ constexpr int kSlots = 8;
 constexpr size_t kSlotFloats = static_cast<size_t>(kTargetGroups) * kPer;
 __device__ __align__(256) float g_partials[kSlots * kSlotFloats];
 
+// The buffer of the allocation-free entry point (gemm_bf16_ex_noalloc): one
+// 4 MB array per device, shared by every call of that entry point on the
+// device, for callers that cannot allocate (graph capture, serving loops).
+// Calls of that entry point that overlap on one device race on it. Nothing
+// in it needs clearing: each workgroup writes its whole partial block before
+// the reduction reads it, and the reduction reads only blocks of this call.
+__device__ __align__(256) float scratch[kSlotFloats];
+
+// Device address of `scratch`, per device, looked up once with that device
+// current: the array's name is only a host-side stand-in for it.
+struct ScratchTable {
+  std::mutex mu;
+  float* ptr[64] = {};
+};
+ScratchTable g_scratch;
+
+hipError_t scratch_ptr(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch.mu);
+  if (g_scratch.ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    g_scratch.ptr[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch.ptr[dev];
+  return hipSuccess;
+}
+
 // Per-device table: slot i belongs to the stream that first claimed it, for
 // the rest of the process (a stream handle is only compared, never used).
 // Calls on one stream are ordered by that stream, so its slot is never used
@@ -359,8 +390,10 @@ void split(int N, int K, int* blocks, int* slices, int* slice_steps) {
   *slices = (steps + *slice_steps - 1) / *slice_steps;
 }
 
+// shared_scratch: take the partial sums to `scratch` instead of the
+// stream's buffer (the allocation-free entry point).
 hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, int N, int K,
-                         const Epilogue& epi, hipStream_t s) {
+                         const Epilogue& epi, hipStream_t s, bool shared_scratch) {
   static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
   hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(skinny_bf16_kernel), kLdsBytes);
   if (e != hipSuccess) return e;
@@ -370,10 +403,11 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, i
     return launch(skinny_bf16_kernel, dim3(blocks), dim3(kThreads), kLdsBytes, s, A, B, C, M,
                   N, K, slices, slice_steps, static_cast<float*>(nullptr), epi);
   float* partials = nullptr;
-  if ((e = stream_slot(s, &partials)) != hipSuccess) return e;
+  if ((e = shared_scratch ? scratch_ptr(&partials) : stream_slot(s, &partials)) != hipSuccess)
+    return e;
   // split() keeps blocks * slices <= kTargetGroups, so the partial blocks
-  // always fit a buffer; the guard keeps a future split from writing past
-  // one.
+  // always fit either buffer; the guard keeps a future split from writing
+  // past one.
   if (static_cast<size_t>(blocks) * slices * kPer > kSlotFloats) return hipErrorInvalidValue;
   if (partials == nullptr) {  // every buffer belongs to another stream
     if (mfma_bf16_supports(M, N, K, 0, 0, 0))
@@ -391,13 +425,14 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, i
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s) {
-  return launch_skinny(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_skinny(A, B, C, M, N, K, Epilogue{}, s, false);
 }
 
 hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                  int M, int N, int K, const Epilogue& e, hipStream_t s) {
+                                  int M, int N, int K, const Epilogue& e, hipStream_t s,
+                                  bool shared_scratch) {
   if (b_nk) return launch_skinny_nk_bf16(A, B, D, M, N, K, e, s);  // gemm_skinny_nk_bf16.hip
-  return launch_skinny(A, B, D, M, N, K, e, s);
+  return launch_skinny(A, B, D, M, N, K, e, s, shared_scratch);
 }
 
 }  // namespace tdm

@@ -165,7 +165,8 @@ bool valid_path(tdm_path p) {
 // D = epilogue(A * op(B)) for bf16 inputs (include/tdm.h).
 tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layout, void* D,
                         tdm_dtype d_type, const void* bias, const void* residual, int gelu,
-                        int64_t M, int64_t N, int64_t K, tdm_path path, void* stream) {
+                        int64_t M, int64_t N, int64_t K, tdm_path path, void* stream,
+                        bool shared_scratch = false) {
   if (d_type != TDM_DTYPE_F32 && d_type != TDM_DTYPE_BF16) return TDM_ERROR_INVALID_VALUE;
   if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return TDM_ERROR_INVALID_VALUE;
   const bool b_nk = b_layout == TDM_LAYOUT_NK;
@@ -205,7 +206,8 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layou
     case TDM_PATH_MFMA:
       return to_status(tdm::launch_mfma_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
     case TDM_PATH_SKINNY:
-      return to_status(tdm::launch_skinny_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
+      return to_status(
+          tdm::launch_skinny_bf16_epi(A, B, b_nk, D, m, n, k, e, s, shared_scratch));
     default: return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
   }
 }
@@ -357,6 +359,13 @@ tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout b_layou
                         int64_t M, int64_t N, int64_t K, void* stream) {
   return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
                       stream);
+}
+
+tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+                                void* D, tdm_dtype d_type, const void* bias, const void* residual,
+                                int gelu, int64_t M, int64_t N, int64_t K, void* stream) {
+  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
+                      stream, true);
 }
 
 tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,

@@ -131,8 +131,11 @@ hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk,
                                 int M, int N, int K, const Epilogue& e, hipStream_t s);
 hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
                                 int M, int N, int K, const Epilogue& e, hipStream_t s);
+// shared_scratch: the small-M K x N split-K partial sums go to the one
+// static buffer of the allocation-free entry point instead of the stream's.
 hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                  int M, int N, int K, const Epilogue& e, hipStream_t s);
+                                  int M, int N, int K, const Epilogue& e, hipStream_t s,
+                                  bool shared_scratch = false);
 hipError_t launch_skinny_nk_bf16(const uint16_t* A, const uint16_t* B, void* D, int M, int N,
                                  int K, const Epilogue& e, hipStream_t s);
 
