@@ -33,6 +33,12 @@ What it computes, and the passage each function follows:
   transpose of the stored matrix (CS336 Lecture 5 GPU notes, review question
   5: op(A) in BLAS terms; §4.1: a transposed view is another memory layout).
   The stored matrix is transposed into K x N order and handed to ``gemm``.
+* ``gemm_tn`` / ``gemm_tn_tiles`` -- the product with A stored K x M, the
+  transpose of the M x K operand: C[i,j] = sum_k At[k,i] B[k,j], i.e. the
+  pages' own example of a transposed operand, x = A.T @ B (CS336 Lecture 5
+  GPU notes, review question 5; §4.1: a transposed view is a different
+  memory layout, not a copy). The stored matrix is transposed into M x K
+  order and handed to ``gemm``.
 * ``fp8_decode``, ``e8m0_decode``, ``gemm_fp8`` / ``gemm_fp8_tiles`` -- the
   FP8 product. The two 8-bit formats are laid out as the table of
   floating-point formats in CS336 Lecture 5 GPU notes, §3.1 gives them:
@@ -181,6 +187,23 @@ def gemm_nt_tiles(A: np.ndarray, Bt: np.ndarray, tiles, tile: int = 32,
         c1 = min(c + tile, Bt.shape[0])
         B = np.ascontiguousarray(np.asarray(Bt)[c:c1].T)
         out.append(gemm_block(A, B, (r, min(r + tile, A.shape[0])), (0, c1 - c), threads))
+    return out
+
+
+def gemm_tn(At: np.ndarray, B: np.ndarray, threads: int | None = None) -> np.ndarray:
+    """fp64 At.T @ B for At[K, M] (A stored transposed, K x M) and B[K, N]:
+    C[i,j] = sum_k At[k,i] B[k,j]."""
+    return gemm(np.ascontiguousarray(np.asarray(At).T), B, threads)
+
+
+def gemm_tn_tiles(At: np.ndarray, B: np.ndarray, tiles, tile: int = 32,
+                  threads: int | None = None) -> list[np.ndarray]:
+    """fp64 tiles of At.T @ B at the given (row0, col0) corners."""
+    out = []
+    for r, c in tiles:
+        r1 = min(r + tile, At.shape[1])
+        A = np.ascontiguousarray(np.asarray(At)[:, r:r1].T)
+        out.append(gemm_block(A, B, (0, r1 - r), (c, min(c + tile, B.shape[1])), threads))
     return out
 
 

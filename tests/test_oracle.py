@@ -467,6 +467,55 @@ def test_gemm_nt_of_a_matrix_with_itself_is_its_gram_matrix():
         assert np.array_equal(T, full[r:r + 32, c:c + 32])
 
 
+def test_gemm_tn_hand_values_and_shape():
+    """C[i,j] = sum_k At[k,i] B[k,j] worked by hand for a 3x2 At (K = 3,
+    M = 2) and a 3x4 B; reading At as M x K would not even have matching
+    shapes, and on a square operand it gives other values (next test)."""
+    At = np.array([[1, 2], [3, 4], [5, 6]], np.float32)
+    B = np.array([[1, 0, 2, -1], [0, 1, 0, 1], [1, 1, -1, 0]], np.float32)
+    C = oracle.gemm_tn(At, B)
+    assert C.shape == (2, 4)
+    # row 0 of A is column 0 of At: (1, 3, 5); row 1 is (2, 4, 6)
+    assert np.array_equal(C, [[6, 8, -3, 2], [8, 10, -2, 2]])
+    for a, b in ((At, B), (inputs.fp32_to_bf16_bits(At), inputs.fp32_to_bf16_bits(B))):
+        assert np.array_equal(oracle.gemm_tn(a, b), C)
+
+
+def test_gemm_tn_of_a_matrix_with_itself_is_its_gram_matrix():
+    """A^T A (A stored K x M here, so gemm_tn(X, X) = X^T X) is symmetric with
+    the squared column norms of X on the diagonal, exact for small integers;
+    the tile helper agrees with the full product."""
+    rng = np.random.default_rng(13)
+    X = rng.integers(-3, 4, size=(53, 37)).astype(np.float32)
+    G = oracle.gemm_tn(X, X)
+    assert G.shape == (37, 37)
+    assert np.array_equal(G, G.T)
+    assert np.array_equal(np.diag(G), (X.astype(np.float64) ** 2).sum(axis=0))
+    B = rng.integers(-3, 4, size=(53, 70)).astype(np.float32)
+    full = oracle.gemm_tn(X, B)
+    tiles = [(0, 0), (32, 32), (5, 64)]
+    for (r, c), T in zip(tiles, oracle.gemm_tn_tiles(X, B, tiles, 32)):
+        assert np.array_equal(T, full[r:r + 32, c:c + 32])
+
+
+def test_gemm_tn_planted_orientation_mistake_is_caught():
+    """A copy that multiplies the stored K x M matrix as if it were M x K
+    (the mistake the pages warn about: a transpose is another layout) fails
+    both gemm_tn pins on square operands, where the shapes do not give it
+    away."""
+    def wrong_tn(At, B):
+        return oracle.gemm(At, B)
+
+    rng = np.random.default_rng(14)
+    X = rng.integers(-3, 4, size=(16, 16)).astype(np.float32)
+    B = rng.integers(-3, 4, size=(16, 16)).astype(np.float32)
+    G = wrong_tn(X, X)
+    gram_ok = np.array_equal(G, G.T) and np.array_equal(
+        np.diag(G), (X.astype(np.float64) ** 2).sum(axis=0))
+    assert not gram_ok
+    assert not np.array_equal(wrong_tn(X, B), oracle.gemm_tn(X, B))
+
+
 # ---------------------------------------------------------------------------
 # FP8 operands with block scales
 # ---------------------------------------------------------------------------
