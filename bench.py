@@ -98,6 +98,15 @@ def parse():
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.mm (PyTorch's ROCm BLAS) on the same resident inputs "
                          "and report it under vendor_blas, for context")
+    ap.add_argument("--summarize-trace", metavar="DIR", default=None,
+                    help="instead of running, summarize a rocprofv3 --kernel-trace output "
+                         "directory of a bench.py run with the same --workload/--steps/--warmup: "
+                         "per kernel, all dispatches and the timed ones (markdown on stdout)")
+    ap.add_argument("--summarize-counters", metavar="DIR", nargs="+", default=None,
+                    help="instead of running, average the per-dispatch counters of rocprofv3 "
+                         "--pmc output directories for the workload's dominant kernel (markdown)")
+    ap.add_argument("--bench-line", metavar="FILE", default=None,
+                    help="with --summarize-trace: the JSON line the profiled run printed")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the product, run a plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -167,6 +176,145 @@ def traffic_record(kernels, src: str, workload: str):
     return total
 
 
+def _csv_rows(root: str, suffix: str):
+    """Rows of every rocprofv3 CSV file under root whose name ends in suffix."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(root):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(dirpath, f), newline="") as fh:
+                    rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {root}")
+    return rows
+
+
+def _short(name: str, kernels):
+    """The kernel (of `kernels`) whose name the demangled trace name holds."""
+    for k in kernels:
+        if k in name:
+            return k
+    return None
+
+
+def workload_kernels(name: str):
+    """(dominant kernel, source, kernels of one call) of a workload on the
+    path bench.py runs it on by default."""
+    import tiled_dense_matrix_amd as tdm
+    from tiled_dense_matrix_amd import inputs
+    if name in inputs.ATTN_WORKLOADS:
+        return KERNEL["attention"]
+    w = inputs.WORKLOADS[name]
+    if w.kind == "fp8":
+        return KERNEL["mfma_fp8"]
+    kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
+    layout = tdm.Layout.NK if w.b_layout == "nk" else tdm.Layout.KN
+    pname = DEFAULT_PATH.get(name) or tdm.path_name(
+        tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K))
+    if pname == "mfma" and w.kind == "f32":
+        pname = "mfma_f32"
+    if pname == "skinny" and w.b_layout == "nk":
+        pname = "skinny_nk"
+    return KERNEL[pname]
+
+
+def summarize_trace(args):
+    """Markdown summary of a kernel trace: for each kernel of the workload,
+    all its dispatches and the timed ones (dispatches warmup .. warmup +
+    steps - 1 of that kernel, in start order), in microseconds."""
+    _, src, kernels = workload_kernels(args.workload)
+    by = {}
+    for r in _csv_rows(args.summarize_trace, "kernel_trace.csv"):
+        k = _short(r["Kernel_Name"], kernels)
+        if k is not None:
+            by.setdefault(k, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    out = ["| kernel | dispatches | average (us) | timed dispatches | timed average (us) | "
+           "timed min (us) | timed median (us) | timed max (us) |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    timed_total = 0.0
+    for k in kernels:
+        us = [(e - b) / 1e3 for b, e in sorted(by.get(k, []))]
+        t = sorted(us[args.warmup:args.warmup + args.steps])
+        if not t:
+            raise SystemExit(f"{k}: {len(us)} dispatches, none in the timed window")
+        avg_t = sum(t) / len(t)
+        timed_total += avg_t
+        out.append(f"| {k} | {len(us)} | {sum(us) / len(us):.1f} | {len(t)} | {avg_t:.1f} | "
+                   f"{t[0]:.1f} | {t[len(t) // 2]:.1f} | {t[-1]:.1f} |")
+    print("\n".join(out))
+    if args.bench_line:
+        with open(args.bench_line) as fh:
+            line = json.loads([x for x in fh.read().splitlines() if x.startswith("{")][-1])
+        step_us = line["ms_per_step"] * 1e3
+        roof = line["roofline"]
+        print(f"\nbench.py line of the same run: {step_us:.1f} us per step, {line['value']} "
+              f"{line['unit']}, roofline {roof['achieved']} {roof['unit']} of {roof['peak']} "
+              f"(frac {roof['frac']}). Timed kernel time per step {timed_total:.1f} us = "
+              f"{timed_total / step_us:.3f} of the step.")
+    print(f"\nKernel source `{src}` sha256[:16] = {src_digest(src)} when measured.")
+
+
+def summarize_counters(args):
+    """Markdown table of per-dispatch counter values (each counter summed
+    over the GPU within a dispatch, then averaged over the dispatches of the
+    workload's dominant kernel) from one or more rocprofv3 --pmc outputs,
+    with derived rates. GRBM_GUI_ACTIVE counts each XCD's engine cycles, so
+    its eighth is the cycles of the clock the counters ran at."""
+    kernel, src, _ = workload_kernels(args.workload)
+    per, durations = {}, []
+    for root in args.summarize_counters:
+        disp = {}
+        for r in _csv_rows(root, "counter_collection.csv"):
+            if kernel not in r["Kernel_Name"]:
+                continue
+            d = disp.setdefault(r.get("Dispatch_Id") or r.get("Correlation_Id"), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+                d["_us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        for d in disp.values():
+            for c, v in d.items():
+                (durations if c == "_us" else per.setdefault(c, [])).append(v)
+    if not per:
+        raise SystemExit(f"no counters of {kernel}")
+    avg = {c: sum(v) / len(v) for c, v in per.items()}
+    print("| counter | per dispatch |\n|---|---:|")
+    for c in sorted(avg):
+        print(f"| {c} | {avg[c]:,.0f} |")
+    simds, xcds = 1024, 8
+    rows = []
+    if durations:
+        rows.append(("average dispatch under the counters (us)",
+                     f"{sum(durations) / len(durations):.1f}"))
+    if avg.get("GRBM_GUI_ACTIVE"):
+        clk = avg["GRBM_GUI_ACTIVE"] / xcds
+        if durations:
+            rows.append(("engine clock from GRBM_GUI_ACTIVE (GHz)",
+                         f"{clk / (sum(durations) / len(durations)) / 1e3:.3f}"))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            rows.append(("MFMA busy / SIMD cycles at the measured clock",
+                         f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / clk:.3f}"))
+        if "SQ_ACTIVE_INST_VALU" in avg:
+            rows.append(("VALU-active / SIMD cycles at the measured clock",
+                         f"{avg['SQ_ACTIVE_INST_VALU'] / simds / clk:.3f}"))
+    if avg.get("SQ_INSTS_MFMA") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        rows.append(("MFMA busy cycles per MFMA instruction",
+                     f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / avg['SQ_INSTS_MFMA']:.1f}"))
+    if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+        rows.append(("LDS bank-conflict cycles / LDS active cycles",
+                     f"{avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.4f}"))
+    if avg.get("SQ_WAVE_CYCLES"):
+        for c, what in (("SQ_WAIT_INST_ANY", "waiting on dependencies"),
+                        ("SQ_WAIT_INST_LDS", "waiting on LDS")):
+            if c in avg:
+                rows.append((f"{what} / wave cycles", f"{avg[c] / avg['SQ_WAVE_CYCLES']:.3f}"))
+    if rows:
+        print("\n| derived | value |\n|---|---:|")
+        for k, v in rows:
+            print(f"| {k} | {v} |")
+    print(f"\nKernel source `{src}` sha256[:16] = {src_digest(src)} when measured.")
+
+
 def copy_probe(mib: int):
     import torch
     n = (mib << 20) // 4
@@ -222,6 +370,10 @@ def main():
               "supported: this library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_counters:
+        return summarize_counters(args)
     # The profiler's region markers register with the profiler when their
     # library loads, which has to happen before the GPU runtime starts.
     timed_region()

@@ -47,3 +47,53 @@ def test_vendor_comparison_is_opt_in():
     assert r.returncode == 0 and "--vendor" in r.stdout
     with open(os.path.join(ROOT, "profiles", "bench.f32_4096.json")) as fh:
         assert "vendor_blas" not in json.loads(fh.read())
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as fh:
+        w = csv.writer(fh)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_summary_takes_the_timed_dispatches(tmp_path):
+    """--summarize-trace averages dispatches warmup .. warmup+steps-1 of each
+    kernel of the call (in start order), not the warm-up ones."""
+    name = "void tdm::(anonymous namespace)::skinny_bf16_kernel(...)"
+    red = "void tdm::(anonymous namespace)::skinny_reduce_kernel(...)"
+    rows, t = [], 0
+    for i in range(8):  # 3 warm-up calls at 100 us, then 5 timed at 20 us
+        dur = 100_000 if i < 3 else 20_000
+        rows.append([i * 2, name, t, t + dur])
+        rows.append([i * 2 + 1, red, t + dur, t + dur + 3_000])
+        t += dur + 10_000
+    _write_csv(str(tmp_path / "host" / "1_run_kernel_trace.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    line = tmp_path / "line.json"
+    line.write_text(json.dumps({"ms_per_step": 0.025, "value": 1.0, "unit": "TFLOP/s",
+                                "roofline": {"achieved": 5000, "unit": "GB/s", "peak": 8000,
+                                             "frac": 0.625}}) + "\n")
+    r = run_bench("--summarize-trace", str(tmp_path), "--workload", "bf16_skinny", "--steps", "5",
+                  "--warmup", "3", "--bench-line", str(line))
+    assert r.returncode == 0, r.stderr
+    assert "| skinny_bf16_kernel | 8 | 50.0 | 5 | 20.0 |" in r.stdout
+    assert "| skinny_reduce_kernel | 8 | 3.0 | 5 | 3.0 |" in r.stdout
+    assert "Timed kernel time per step 23.0 us = 0.920 of the step" in r.stdout
+
+
+def test_counter_summary_normalizes_to_the_measured_clock(tmp_path):
+    name = "void tdm::(anonymous namespace)::mfma_bf16_kernel<...>(...)"
+    rows = []
+    for d in range(2):  # 1000 us at 1.5 GHz: 8 XCDs x 1.5e6 cycles
+        for c, v in (("GRBM_GUI_ACTIVE", 12e6), ("SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 1.2e6)):
+            rows.append([d, name, c, v / 2, 0, 1_000_000])
+            rows.append([d, name, c, v / 2, 0, 1_000_000])  # two rows per dispatch, summed
+    _write_csv(str(tmp_path / "p" / "run_counter_collection.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                "Start_Timestamp", "End_Timestamp"], rows)
+    r = run_bench("--summarize-counters", str(tmp_path / "p"), "--workload", "bf16_8192")
+    assert r.returncode == 0, r.stderr
+    assert "| engine clock from GRBM_GUI_ACTIVE (GHz) | 1.500 |" in r.stdout
+    assert "| MFMA busy / SIMD cycles at the measured clock | 0.800 |" in r.stdout
