@@ -397,7 +397,8 @@ def main():
     pname_arg = args.path or DEFAULT_PATH.get(w.name, "auto")
     path = tdm.Path[pname_arg.upper()]
     nk = w.b_layout == "nk"  # B stored N x K: C = A @ B.T
-    layout = tdm.Layout.NK if nk else tdm.Layout.KN
+    km = w.a_layout == "km"  # A stored K x M: C = A.T @ B
+    layout = tdm.Layout((tdm.Layout.NK if nk else 0) | (tdm.Layout.KM_KN if km else 0))
     chosen = tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K) if path == tdm.Path.AUTO \
         else path
     pname = tdm.path_name(chosen)
@@ -433,7 +434,7 @@ def main():
 
     def call(i, p):
         a, b, c = sets[i % rot]
-        if epi or nk:
+        if epi or nk or km:
             tdm.tdm_gemm_bf16_ex_path(a, b, layout, c, bias=bias_d, gelu=w.gelu, path=p,
                                       stream=stream)
         else:
@@ -544,7 +545,10 @@ def main():
         else:
             vsets = [(a.view(torch.bfloat16), b.view(torch.bfloat16)) for a, b, _ in sets]
             if not epi:
-                if nk:  # a 2-D product with the weight's transposed view (not batched)
+                if km:  # a 2-D product with A's transposed view (not batched)
+                    vmm = lambda a, b: torch.mm(a.t(), b, out_dtype=torch.float32)  # noqa: E731
+                    vop = "torch.mm with A.t() (out_dtype=float32)"
+                elif nk:  # a 2-D product with the weight's transposed view (not batched)
                     vmm = lambda a, b: torch.mm(a, b.t(), out_dtype=torch.float32)  # noqa: E731
                     vop = "torch.mm with B.t() (out_dtype=float32)"
                 else:
@@ -586,7 +590,7 @@ def main():
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
                    "rotated_copies": rot,
                    "auto_path": auto_info,
-                   "b_layout": w.b_layout,
+                   "b_layout": w.b_layout, "a_layout": w.a_layout,
                    "epilogue": None if not epi else {"bias": bias_np is not None,
                                                      "gelu": w.gelu, "out": w.out},
                    "unfused": unfused,
@@ -604,7 +608,8 @@ def main():
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
         B_kn = np.ascontiguousarray(B.T) if nk else B  # the oracle takes B as K x N
-        line["cpu_baseline"] = cpu_baseline(w, A, B_kn, C_gpu, args.cpu_seconds, bias_np)
+        A_mk = np.ascontiguousarray(A.T) if km else A  # ... and A as M x K
+        line["cpu_baseline"] = cpu_baseline(w, A_mk, B_kn, C_gpu, args.cpu_seconds, bias_np)
     print(json.dumps(line), flush=True)
 
 

@@ -148,27 +148,37 @@ TDM_API tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t
                                                int64_t N, int64_t K, tdm_path path,
                                                void* stream);
 
-/* How B is stored. */
+/* How A and B are stored (all row-major). Bit 0: B is N x K; bit 1: A is
+ * K x M. */
 typedef enum tdm_layout {
-  TDM_LAYOUT_KN = 0,  /* B is K x N, row-major: C = A * B (every gemm_* call)  */
-  TDM_LAYOUT_NK = 1   /* B is N x K, row-major -- a linear layer's weight, as a
-                         PyTorch Linear stores it: C = A * B^T, i.e.
-                         C[i,j] = sum_k A[i,k] * B[j,k]                        */
+  TDM_LAYOUT_KN = 0,     /* A is M x K, B is K x N: C = A * B (every gemm_* call) */
+  TDM_LAYOUT_NK = 1,     /* B is N x K -- a linear layer's weight, as a PyTorch
+                            Linear stores it: C = A * B^T, i.e.
+                            C[i,j] = sum_k A[i,k] * B[j,k]                        */
+  TDM_LAYOUT_KM_KN = 2,  /* A is K x M -- the transpose of the operand, as
+                            x = A.T @ B takes it: C = A^T * B, i.e.
+                            C[i,j] = sum_k A[k,i] * B[k,j]                        */
+  TDM_LAYOUT_KM_NK = 3   /* A is K x M and B is N x K: C = A^T * B^T, i.e.
+                            C[i,j] = sum_k A[k,i] * B[j,k]                        */
 } tdm_layout;
 
-/* gemm_bf16_epilogue with B in either layout: D = epilogue(A * op(B)), op(B)
- * = B for TDM_LAYOUT_KN and B^T for TDM_LAYOUT_NK (CS336 Lecture 5 GPU notes,
- * review question 5 and the §4.1 warning on transposed views: a transposed
- * operand is a different memory layout, not a free view). Everything else
- * -- the epilogue, D, bias, residual, errors -- as gemm_bf16_epilogue;
+/* gemm_bf16_epilogue with A and B in any layout: D = epilogue(op(A) *
+ * op(B)), op(A) = A^T when A is stored K x M, op(B) = B^T when B is stored
+ * N x K (CS336 Lecture 5 GPU notes, review question 5 on x = A.T @ B and the
+ * §4.1 warning on transposed views: a transposed operand is a different
+ * memory layout, not a free view). M, N and K are the sizes of the product
+ * C[M,N] = op(A)[M,K] * op(B)[K,N] whatever the layout. Everything else --
+ * the epilogue, D, bias, residual, errors -- as gemm_bf16_epilogue;
  * TDM_ERROR_INVALID_VALUE for an unknown layout. With no bias, residual or
- * GELU and d_type TDM_DTYPE_F32 this is the plain product. */
-TDM_API tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+ * GELU and d_type TDM_DTYPE_F32 this is the plain product. The small-M
+ * streaming path takes A as M x K only; an A stored K x M runs on the
+ * matrix cores (M a multiple of 8, 16-byte aligned A) or the edge kernel. */
+TDM_API tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout layout,
                                 void* D, tdm_dtype d_type, const void* bias,
                                 const void* residual, int gelu, int64_t M, int64_t N, int64_t K,
                                 void* stream);
 TDM_API tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B,
-                                         tdm_layout b_layout, void* D, tdm_dtype d_type,
+                                         tdm_layout layout, void* D, tdm_dtype d_type,
                                          const void* bias, const void* residual, int gelu,
                                          int64_t M, int64_t N, int64_t K, tdm_path path,
                                          void* stream);
@@ -187,16 +197,17 @@ TDM_API tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B,
  * safe. No split needs more than the 4 MB (at most 256 workgroups write 16
  * x 256 fp32 sums each); the buffer needs no clearing between calls. */
 TDM_API tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B,
-                                        tdm_layout b_layout, void* D, tdm_dtype d_type,
+                                        tdm_layout layout, void* D, tdm_dtype d_type,
                                         const void* bias, const void* residual, int gelu,
                                         int64_t M, int64_t N, int64_t K, void* stream);
 
-/* Host-only: tdm_path_supports / tdm_select_path for a given layout of B
- * (TDM_LAYOUT_NK: bf16 only; 0 / TDM_PATH_EDGE for an unknown layout). */
-TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path path, int64_t M,
+/* Host-only: tdm_path_supports / tdm_select_path for given layouts of A and
+ * B (layouts other than TDM_LAYOUT_KN: bf16 only; 0 / TDM_PATH_EDGE for an
+ * unknown layout). */
+TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout layout, tdm_path path, int64_t M,
                                  int64_t N, int64_t K, int misalign_a, int misalign_b,
                                  int misalign_c);
-TDM_API tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout b_layout, int64_t M, int64_t N,
+TDM_API tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout layout, int64_t M, int64_t N,
                                     int64_t K);
 
 /* FP8 element formats (CS336 Lecture 5 GPU notes, §3.1, table of

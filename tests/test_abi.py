@@ -253,6 +253,33 @@ def test_epilogue_validation():
     assert fp(FAKE, FAKE_B, FAKE_C, D.BF16, None, None, 0, M, N, K, 9, None) == S.ERROR_INVALID_VALUE
 
 
+def test_layouts_of_a_and_b():
+    """gemm_bf16_ex takes four layouts (bit 0: B stored N x K, bit 1: A
+    stored K x M); another value is rejected. An A stored K x M runs on the
+    matrix cores when M is a multiple of 8, never on the small-M streaming
+    path, else on the edge kernel."""
+    lib = tdm.load()
+    S, P, D, L, K_ = tdm.Status, tdm.Path, tdm.DType, tdm.Layout, tdm.Kind.BF16_F32ACC
+    f, fp = lib.gemm_bf16_ex, lib.tdm_gemm_bf16_ex_path
+    for bad in (4, -1, 7):
+        assert f(FAKE, FAKE_B, bad, FAKE_C, D.F32, None, None, 0, 64, 64, 64, None) == \
+            S.ERROR_INVALID_VALUE
+    assert fp(FAKE, FAKE_B, L.KM_KN, FAKE_C, D.F32, None, None, 0, 16, 1024, 2048, P.SKINNY,
+              None) == S.ERROR_NOT_SUPPORTED
+    assert fp(FAKE, FAKE_B, L.KM_KN, FAKE_C, D.F32, None, None, 0, 33, 64, 64, P.MFMA,
+              None) == S.ERROR_NOT_SUPPORTED
+    assert tdm.tdm_path_supports_ex(K_, L.KM_KN, P.MFMA, 256, 264, 520)
+    assert tdm.tdm_path_supports_ex(K_, L.KM_NK, P.MFMA, 256, 257, 520)  # any N with B N x K
+    assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.MFMA, 256, 257, 520)
+    assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.MFMA, 33, 64, 64)
+    assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.SKINNY, 16, 1024, 2048)
+    assert not tdm.tdm_path_supports_ex(tdm.Kind.F32, L.KM_KN, P.EDGE, 64, 64, 64)
+    assert tdm.tdm_select_path_ex(K_, L.KM_KN, 16, 8192, 8192) == P.MFMA
+    assert tdm.tdm_select_path_ex(K_, L.KM_NK, 8192, 8192, 8192) == P.MFMA
+    assert tdm.tdm_select_path_ex(K_, L.KM_KN, 33, 65, 17) == P.EDGE
+    assert tdm.tdm_select_path_ex(K_, L.KN, 16, 8192, 8192) == P.SKINNY
+
+
 def test_epilogue_in_place_residual_and_k_zero_pass_validation():
     skip_if_gpu()
     f = tdm.load().gemm_bf16_epilogue

@@ -83,10 +83,11 @@ class Path(enum.IntEnum):
 
 
 class Layout(enum.IntEnum):
-    """How B is stored: KN = K x N (C = A @ B); NK = N x K, a linear layer's
-    weight (C = A @ B.T)."""
-    KN = 0
-    NK = 1
+    """How A and B are stored (bit 0: B is N x K; bit 1: A is K x M)."""
+    KN = 0     # A M x K, B K x N: C = A @ B
+    NK = 1     # B N x K (a torch Linear weight): C = A @ B.T
+    KM_KN = 2  # A K x M: C = A.T @ B
+    KM_NK = 3  # A K x M, B N x K: C = A.T @ B.T
 
 
 class DType(enum.IntEnum):
@@ -256,8 +257,9 @@ def _epilogue_args(A, B, D, out_dtype, bias, residual, layout=Layout.KN):
     torch = _torch()
     bf16 = _bf16_dtypes()
     _check_matrix("A", A, bf16)
-    M, K = A.shape
-    if Layout(layout) == Layout.NK:
+    layout = Layout(layout)
+    K, M = A.shape if layout & Layout.KM_KN else A.shape[::-1]
+    if layout & Layout.NK:
         _check_matrix("B", B, bf16, cols=K)
         N = B.shape[0]
     else:
@@ -324,10 +326,11 @@ def tdm_gemm_bf16_epilogue_path(A, B, D=None, out_dtype=None, bias=None, residua
 
 def gemm_bf16_ex(A, B, layout=Layout.KN, D=None, out_dtype=None, bias=None, residual=None,
                  gelu=False, stream=None):
-    """D = epilogue(A @ op(B)) for bf16 A, B: op(B) = B for Layout.KN (B is
-    K x N), B.T for Layout.NK (B is N x K, like a torch Linear weight). The
-    epilogue is gemm_bf16_epilogue's; without D a new tensor of out_dtype
-    (default torch.bfloat16) is returned."""
+    """D = epilogue(op(A) @ op(B)) for bf16 A, B: op(B) = B.T when B is
+    stored N x K (Layout.NK, Layout.KM_NK; like a torch Linear weight), op(A)
+    = A.T when A is stored K x M (Layout.KM_KN, Layout.KM_NK). The epilogue
+    is gemm_bf16_epilogue's; without D a new tensor of out_dtype (default
+    torch.bfloat16) is returned."""
     torch = _torch()
     M, N, K, D, dt = _epilogue_args(A, B, D, out_dtype or torch.bfloat16, bias, residual, layout)
     return _call_ex("gemm_bf16_ex", A, B, layout, D, dt, bias, residual, gelu, M, N, K, stream)

@@ -28,8 +28,8 @@ __device__ __forceinline__ float to_f32(uint16_t h) {
 
 // kEpi: finish each output with the fused epilogue and write it to C as the
 // epilogue's type says (C is then the epilogue's D); else store the fp32 sum.
-// kBNK: B is stored N x K (C = A * B^T).
-template <typename T, bool kEpi, bool kBNK>
+// kBNK: B is stored N x K (op(B) = B^T). kAKM: A is stored K x M (op(A) = A^T).
+template <typename T, bool kEpi, bool kBNK, bool kAKM = false>
 __global__ __launch_bounds__(kThreads) void edge_kernel(
     const T* __restrict__ A, const T* __restrict__ B, void* C,
     int M, int N, int K, int tiles_n, Epilogue epi) {
@@ -53,9 +53,15 @@ __global__ __launch_bounds__(kThreads) void edge_kernel(
 #pragma unroll
     for (int p = 0; p < kT / 8; ++p) {
       const int r = lr + 8 * p;
-      const int am = m0 + r, ak = k0 + lc;
-      As[r][lc] = (am < M && ak < K)
-                      ? to_f32(A[static_cast<int64_t>(am) * K + ak]) : 0.f;
+      if constexpr (kAKM) {  // lanes along m (contiguous in A), stored transposed
+        const int ak = k0 + r, am = m0 + lc;
+        As[lc][r] = (am < M && ak < K)
+                        ? to_f32(A[static_cast<int64_t>(ak) * M + am]) : 0.f;
+      } else {
+        const int am = m0 + r, ak = k0 + lc;
+        As[r][lc] = (am < M && ak < K)
+                        ? to_f32(A[static_cast<int64_t>(am) * K + ak]) : 0.f;
+      }
       if constexpr (kBNK) {  // lanes along k (contiguous in B), stored transposed
         const int bn = n0 + r, bk = k0 + lc;
         Bs[lc][r] = (bk < K && bn < N)
@@ -102,15 +108,15 @@ __global__ void fill_zero_kernel(float* __restrict__ C, int64_t count) {
     C[i] = 0.f;
 }
 
-template <typename T, bool kEpi, bool kBNK>
+template <typename T, bool kEpi, bool kBNK, bool kAKM = false>
 hipError_t launch_edge(const T* A, const T* B, void* C, int M, int N, int K, const Epilogue& e,
                        hipStream_t s) {
   const int tiles_m = (M + kT - 1) / kT;
   const int tiles_n = (N + kT - 1) / kT;
   const int64_t tiles = static_cast<int64_t>(tiles_m) * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  return launch(edge_kernel<T, kEpi, kBNK>, dim3(static_cast<unsigned>(tiles)), dim3(kThreads), 0, s,
-                A, B, C, M, N, K, tiles_n, e);
+  return launch(edge_kernel<T, kEpi, kBNK, kAKM>, dim3(static_cast<unsigned>(tiles)),
+                dim3(kThreads), 0, s, A, B, C, M, N, K, tiles_n, e);
 }
 
 }  // namespace
@@ -132,8 +138,11 @@ hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
   return launch_edge<uint16_t, false, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
-hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                int M, int N, int K, const Epilogue& e, hipStream_t s) {
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, bool a_km,
+                                void* D, int M, int N, int K, const Epilogue& e, hipStream_t s) {
+  if (a_km)
+    return b_nk ? launch_edge<uint16_t, true, true, true>(A, B, D, M, N, K, e, s)
+                : launch_edge<uint16_t, true, false, true>(A, B, D, M, N, K, e, s);
   if (b_nk) return launch_edge<uint16_t, true, true>(A, B, D, M, N, K, e, s);
   return launch_edge<uint16_t, true, false>(A, B, D, M, N, K, e, s);
 }

@@ -28,6 +28,9 @@
 // one row of A and of one column of B.
 //   A stays row-major in LDS, As[m][k] (2*BK bytes per row), and is read with
 //   16-byte loads. Chunk c (8 k values) of row m sits at chunk c ^ swz_a(m).
+//   An A stored K x M (the product is then A^T B for the stored matrix, the
+//   pages' x = A.T @ B) is staged k-major like a K x N B, As[k][m], and read
+//   with the same transposing reads as B below.
 //   B stays row-major too, Bs[k][n] (2*BN bytes per row), and is read with
 //   ds_read_b64_tr_b16: within each group of 16 lanes, lane j receives
 //   element e from the address of lane 4e + j/4, so lanes that point at four
@@ -63,18 +66,22 @@ constexpr int kSchedDsRead = 0x100;
 
 // Tile geometry. Copies move 1 KB of LDS per wave instruction. BNK_: B is
 // stored N x K (C = A * B^T, a linear layer's weight) and is then kept in LDS
-// like A, one K-contiguous row per column n; otherwise B is K x N.
-template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool BNK_ = false>
+// like A, one K-contiguous row per column n; otherwise B is K x N. AKM_: A is
+// stored K x M and kept in LDS k-major, one M-contiguous row per k, like a
+// K x N B; otherwise A is M x K.
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int STAGES_, bool BNK_ = false,
+          bool AKM_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_;
   static constexpr int kStages = STAGES_;
   static constexpr bool kBNK = BNK_;
+  static constexpr bool kAKM = AKM_;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
-  static constexpr int kRowA = BK * 2;                // bytes per LDS row of A
-  static constexpr int kChunksA = BK / 8;             // 16-byte chunks per row of A
+  static constexpr int kRowA = kAKM ? BM * 2 : BK * 2;  // bytes per LDS row of A
+  static constexpr int kChunksA = kRowA / 16;         // 16-byte chunks per row of A
   static constexpr int kRowB = kBNK ? BK * 2 : BN * 2;  // bytes per LDS row of B
   static constexpr int kChunksB = kRowB / 16;
-  static constexpr int kStageA = BM * kRowA;
+  static constexpr int kStageA = BM * BK * 2;
   static constexpr int kStageB = BK * BN * 2;
   static constexpr int kStage = kStageA + kStageB;
   static constexpr int kLdsBytes = kStages * kStage;
@@ -86,14 +93,16 @@ struct Cfg {
   static constexpr int kRowsPerCopyA = 1024 / kRowA;
   static constexpr int kRowsPerCopyB = 1024 / kRowB;
   static constexpr int kSub = BK / 16;                // MFMA k-steps per K step
-  static constexpr int kReads = kFragM + (kBNK ? 1 : 2) * kFragN;  // LDS reads per sub-step
+  // LDS read instructions per sub-step (a transposing fragment read takes two)
+  static constexpr int kReads = (kAKM ? 2 : 1) * kFragM + (kBNK ? 1 : 2) * kFragN;
   static constexpr int kMfmas = kFragM * kFragN;      // MFMAs per sub-step
   static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
                 "each wave copies whole 1 KB blocks");
   static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
                 "masked copy: whole 16-byte chunks per lane");
-  static_assert(kChunksA == 4 || kChunksA == 8, "swizzle of A rows");
-  static_assert(!kBNK || kChunksB == kChunksA, "N x K rows of B like A's");
+  static_assert(kAKM || kChunksA == 4 || kChunksA == 8, "swizzle of A rows");
+  static_assert(!kAKM || kChunksA >= 16, "k-major A rows take the swizzle of B's");
+  static_assert(!kBNK || kChunksB == BK / 8, "N x K rows of B like A's");
   static_assert(kSub % 2 == 0, "fragment double buffer alternates per sub-step");
   static_assert(kStages >= 2 && (kStages - 2) * kCopies <= 63, "vmcnt range");
   static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
@@ -128,9 +137,15 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
 #pragma unroll
   for (int j = 0; j < T::kCopyA; ++j) {  // A: blocks of kRowsPerCopyA rows
     const int row = (wave * T::kCopyA + j) * T::kRowsPerCopyA + lane / T::kChunksA;
-    const int c = (lane % T::kChunksA) ^ swz_a<T::kChunksA>(row);
-    const int gm = min(m0 + row, M - 1);
-    p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(gm) * K + c * 8) * 2);
+    if constexpr (T::kAKM) {  // row = k of the step, chunk c = 8 rows m of A
+      const int c = (lane % T::kChunksA) ^ swz_b(row);
+      const int gm = min(m0 + c * 8, M - 8);
+      p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * M + gm) * 2);
+    } else {
+      const int c = (lane % T::kChunksA) ^ swz_a<T::kChunksA>(row);
+      const int gm = min(m0 + row, M - 1);
+      p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(gm) * K + c * 8) * 2);
+    }
   }
 #pragma unroll
   for (int j = 0; j < T::kCopyB; ++j) {  // B: blocks of kRowsPerCopyB rows
@@ -151,9 +166,10 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
 // --- global -> LDS copy of one full K step (clamped M/N) -----------------
 template <class T>
 __device__ __forceinline__ void copy_step_dma(const uint16_t* __restrict__ A,
-                                              const uint16_t* __restrict__ B, int N, int k0,
-                                              int wave, const CopyPlan<T>& p, uint32_t stage) {
-  const uint16_t* a_base = A + k0;
+                                              const uint16_t* __restrict__ B, int M, int N,
+                                              int k0, int wave, const CopyPlan<T>& p,
+                                              uint32_t stage) {
+  const uint16_t* a_base = T::kAKM ? A + static_cast<int64_t>(k0) * M : A + k0;
   const uint16_t* b_base = T::kBNK ? B + k0 : B + static_cast<int64_t>(k0) * N;
 #pragma unroll
   for (int j = 0; j < T::kCopyA; ++j)
@@ -174,11 +190,18 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
   for (int i = 0; i < T::kStageA / 16 / T::kThreads; ++i) {  // A chunks
     const int id = tid + T::kThreads * i;
     const int row = id / T::kChunksA, c = id % T::kChunksA;
-    const int gk = k0 + c * 8;
-    const int gm = min(m0 + row, M - 1);
     u32x4 v = zero;
-    if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-    *(LDS_PTR(u32x4))(stage + row * T::kRowA + ((c ^ swz_a<T::kChunksA>(row)) << 4)) = v;
+    if constexpr (T::kAKM) {  // row = k, chunk c = 8 rows m
+      const int gk = k0 + row;
+      const int gm = min(m0 + c * 8, M - 8);
+      if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gk) * M + gm);
+      *(LDS_PTR(u32x4))(stage + row * T::kRowA + ((c ^ swz_b(row)) << 4)) = v;
+    } else {
+      const int gk = k0 + c * 8;
+      const int gm = min(m0 + row, M - 1);
+      if (gk < K) v = *reinterpret_cast<const u32x4*>(A + static_cast<int64_t>(gm) * K + gk);
+      *(LDS_PTR(u32x4))(stage + row * T::kRowA + ((c ^ swz_a<T::kChunksA>(row)) << 4)) = v;
+    }
   }
   LDS_PTR(uint8_t) sb = stage + T::kStageA;
 #pragma unroll
@@ -200,10 +223,32 @@ __device__ __forceinline__ void copy_step_masked(const uint16_t* __restrict__ A,
   }
 }
 
-// Eight consecutive k (16s + 8*(lane/32) + 0..7) of row `row` of A.
+// From a k-major LDS tile (rows of kRow bytes, chunk c of row k at
+// c ^ swz_b(k)): eight consecutive k (16s + 8*(lane/32) + 0..7) of column
+// n_base + lane%32, with two transposing reads.
+template <int kRow>
+__device__ __forceinline__ bf16x8 read_kmajor(LDS_PTR(const uint8_t) base, int n_base, int s,
+                                              int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const int col = n_base + 16 * (g & 1) + 4 * (i & 3);
+  const int c = col >> 3, half = (col & 7) << 1;
+  const int r0 = 16 * s + 8 * (g >> 1) + (i >> 2);
+  const int r1 = r0 + 4;
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(s16x4))(base + r0 * kRow + ((c ^ swz_b(r0)) << 4) + half));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (LDS_PTR(s16x4))(base + r1 * kRow + ((c ^ swz_b(r1)) << 4) + half));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Eight consecutive k (16s + 8*(lane/32) + 0..7) of row m_base + lane%32 of A.
 template <class T>
-__device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int row, int s, int lg) {
-  const int chunk = 2 * s + lg;
+__device__ __forceinline__ bf16x8 read_a(LDS_PTR(const uint8_t) sa, int m_base, int s,
+                                         int lane) {
+  if constexpr (T::kAKM) return read_kmajor<T::kRowA>(sa, m_base, s, lane);
+  const int row = m_base + (lane & 31), chunk = 2 * s + (lane >> 5);
   const u32x4 v = *(LDS_PTR(const u32x4))(sa + row * T::kRowA +
                                            ((chunk ^ swz_a<T::kChunksA>(row)) << 4));
   return __builtin_bit_cast(bf16x8, v);
@@ -219,18 +264,7 @@ __device__ __forceinline__ bf16x8 read_b(LDS_PTR(const uint8_t) sb, int n_base, 
                                              ((chunk ^ swz_a<T::kChunksB>(row)) << 4));
     return __builtin_bit_cast(bf16x8, v);
   }
-  const int g = lane >> 4, i = lane & 15;
-  const int col = n_base + 16 * (g & 1) + 4 * (i & 3);
-  const int c = col >> 3, half = (col & 7) << 1;
-  const int r0 = 16 * s + 8 * (g >> 1) + (i >> 2);
-  const int r1 = r0 + 4;
-  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LDS_PTR(s16x4))(sb + r0 * T::kRowB + ((c ^ swz_b(r0)) << 4) + half));
-  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (LDS_PTR(s16x4))(sb + r1 * T::kRowB + ((c ^ swz_b(r1)) << 4) + half));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-  const u32x4 v = {l2.x, l2.y, h2.x, h2.y};
-  return __builtin_bit_cast(bf16x8, v);
+  return read_kmajor<T::kRowB>(sb, n_base, s, lane);
 }
 
 // Instruction order for the scheduler within one sub-step: one read of the
@@ -266,8 +300,8 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
   const int lane = tid & 63;
   const int wm = wave / T::WN, wn = wave % T::WN;
   const int lr = lane & 31, lg = lane >> 5;
-  const int row_a = wm * T::kWaveM + lr;  // + 32 i: this lane's rows of A
-  const int col_b = wn * T::kWaveN;       // + 32 j: this wave's columns of B
+  const int row_a = wm * T::kWaveM;  // + 32 i: this wave's rows of A
+  const int col_b = wn * T::kWaveN;  // + 32 j: this wave's columns of B
 
   f32x16 acc[T::kFragM][T::kFragN];
 #pragma unroll
@@ -302,7 +336,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
     if (st < full_steps) {
       int ks = st + rot;
       if (ks >= full_steps) ks -= full_steps;
-      copy_step_dma<T>(A, B, N, ks * T::BK, wave, plan, lds0 + slot * T::kStage);
+      copy_step_dma<T>(A, B, M, N, ks * T::BK, wave, plan, lds0 + slot * T::kStage);
     } else if (st < steps) {
       copy_step_masked<T>(A, B, M, N, K, m0, n0, st * T::BK, tid, lds + slot * T::kStage);
     }
@@ -324,7 +358,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
 
   bf16x8 a[2][T::kFragM], b[2][T::kFragN];
 #pragma unroll
-  for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lg);
+  for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lane);
 #pragma unroll
   for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(lds + T::kStageA, col_b + 32 * j, 0, lane);
 
@@ -339,7 +373,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
       const int c = s & 1, n = c ^ 1;
       if (s + 1 < T::kSub) {
 #pragma unroll
-        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, s + 1, lg);
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, s + 1, lane);
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j) b[n][j] = read_b<T>(sb, col_b + 32 * j, s + 1, lane);
       } else {
@@ -351,7 +385,7 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
         __syncthreads();
         LDS_PTR(const uint8_t) na = lds + nxt * T::kStage;
 #pragma unroll
-        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lg);
+        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lane);
 #pragma unroll
         for (int j = 0; j < T::kFragN; ++j)
           b[n][j] = read_b<T>(na + T::kStageA, col_b + 32 * j, 0, lane);
@@ -433,6 +467,16 @@ bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
          mis_b == 0;
 }
 
+bool mfma_bf16_akm_supports(int64_t M, int64_t N, int64_t K, bool b_nk, int mis_a, int mis_b,
+                            int mis_c) {
+  (void)mis_c;
+  // A stored K x M: 16-byte chunks along M, and 32-bit per-lane copy
+  // offsets (a step's rows of A and of a K x N B stay below 4 GiB).
+  if (M % 8 != 0 || M > (1 << 24) || K % 8 != 0 || K < 8 || mis_a != 0 || mis_b != 0)
+    return false;
+  return b_nk || (N % 8 == 0 && N <= (1 << 24));
+}
+
 bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                            int mis_c) {
   (void)M;
@@ -445,27 +489,34 @@ bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b
 // An N x K B takes 64 k per step, double-buffered: 128-byte row pieces of
 // both operands (one cache line each) instead of 64-byte halves measured 2-9%
 // faster there; a K x N B keeps 32 k per step and four stages.
-template <bool BNK>
-using LargeTile = Cfg<256, 256, 2, 4, BNK ? 64 : 32, BNK ? 2 : 4, BNK>;
-template <bool BNK>
-using SmallTile = Cfg<128, 128, 2, 4, 32, 4, BNK>;
+template <bool BNK, bool AKM>
+using LargeTile = Cfg<256, 256, 2, 4, BNK ? 64 : 32, BNK ? 2 : 4, BNK, AKM>;
+template <bool BNK, bool AKM>
+using SmallTile = Cfg<128, 128, 2, 4, 32, 4, BNK, AKM>;
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
   // The plain product goes through the staged store too, with no epilogue
   // terms: its row-contiguous 16-byte stores write C faster than the
   // accumulators' own layout does.
-  return launch_mfma_bf16_epi(A, B, false, C, M, N, K, Epilogue{}, s);
+  return launch_mfma_bf16_epi(A, B, false, false, C, M, N, K, Epilogue{}, s);
 }
 
-hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                int M, int N, int K, const Epilogue& e, hipStream_t s) {
-  const bool large = use_large_tiles(M, N, kLargeTileFillBf16);
-  if (b_nk)
-    return large ? launch_tile<LargeTile<true>>(A, B, D, M, N, K, e, s)
-                 : launch_tile<SmallTile<true>>(A, B, D, M, N, K, e, s);
-  return large ? launch_tile<LargeTile<false>>(A, B, D, M, N, K, e, s)
-               : launch_tile<SmallTile<false>>(A, B, D, M, N, K, e, s);
+template <bool BNK, bool AKM>
+hipError_t launch_layout(const uint16_t* A, const uint16_t* B, void* D, int M, int N, int K,
+                         const Epilogue& e, hipStream_t s) {
+  return use_large_tiles(M, N, kLargeTileFillBf16)
+             ? launch_tile<LargeTile<BNK, AKM>>(A, B, D, M, N, K, e, s)
+             : launch_tile<SmallTile<BNK, AKM>>(A, B, D, M, N, K, e, s);
+}
+
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, bool a_km,
+                                void* D, int M, int N, int K, const Epilogue& e, hipStream_t s) {
+  if (a_km)
+    return b_nk ? launch_layout<true, true>(A, B, D, M, N, K, e, s)
+                : launch_layout<false, true>(A, B, D, M, N, K, e, s);
+  return b_nk ? launch_layout<true, false>(A, B, D, M, N, K, e, s)
+              : launch_layout<false, false>(A, B, D, M, N, K, e, s);
 }
 
 }  // namespace tdm

@@ -411,8 +411,8 @@ hipError_t launch_skinny(const uint16_t* A, const uint16_t* B, void* C, int M, i
   if (static_cast<size_t>(blocks) * slices * kPer > kSlotFloats) return hipErrorInvalidValue;
   if (partials == nullptr) {  // every buffer belongs to another stream
     if (mfma_bf16_supports(M, N, K, 0, 0, 0))
-      return launch_mfma_bf16_epi(A, B, false, C, M, N, K, epi, s);
-    return launch_edge_bf16_epi(A, B, false, C, M, N, K, epi, s);
+      return launch_mfma_bf16_epi(A, B, false, false, C, M, N, K, epi, s);
+    return launch_edge_bf16_epi(A, B, false, false, C, M, N, K, epi, s);
   }
   e = launch(skinny_bf16_kernel, dim3(blocks * slices), dim3(kThreads), kLdsBytes, s, A, B,
              static_cast<void*>(nullptr), M, N, K, slices, slice_steps, partials, epi);

@@ -41,13 +41,13 @@ tdm_status check_device() {
 }
 
 // Shape/alignment admission of each path for one kind; b_nk: B is stored
-// N x K (bf16 only).
+// N x K, a_km: A is stored K x M (bf16 only).
 bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
-              int ma, int mb, int mc, bool b_nk = false) {
+              int ma, int mb, int mc, bool b_nk = false, bool a_km = false) {
   const bool kind_ok =
       (path != TDM_PATH_VALU || kind == TDM_KIND_F32) &&
       (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC) &&
-      (!b_nk || kind == TDM_KIND_BF16_F32ACC);
+      (!(b_nk || a_km) || kind == TDM_KIND_BF16_F32ACC);
   if (!kind_ok) return false;
   if (M == 0 || N == 0 || K == 0) return true;  // nothing to run, or a zero fill
   switch (path) {
@@ -58,10 +58,12 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
       return kind == TDM_KIND_F32 && tdm::valu_f32_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_MFMA:
       if (kind == TDM_KIND_F32) return tdm::mfma_f32_supports(M, N, K, ma, mb, mc);
+      if (a_km) return tdm::mfma_bf16_akm_supports(M, N, K, b_nk, ma, mb, mc);
       return b_nk ? tdm::mfma_bf16_nk_supports(M, N, K, ma, mb, mc)
                   : tdm::mfma_bf16_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_SKINNY:
-      if (kind != TDM_KIND_BF16_F32ACC) return false;
+      // the streaming kernels read A as M x K rows (M <= 16)
+      if (kind != TDM_KIND_BF16_F32ACC || a_km) return false;
       return b_nk ? tdm::skinny_bf16_nk_supports(M, N, K, ma, mb, mc)
                   : tdm::skinny_bf16_supports(M, N, K, ma, mb, mc);
   }
@@ -73,7 +75,7 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
 // small-M bf16 product is memory-bound and goes to the streaming path; above
 // it the compute paths are used.
 tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, int mc,
-                bool b_nk = false) {
+                bool b_nk = false, bool a_km = false) {
   if (M <= 0 || N <= 0 || K <= 0) return TDM_PATH_EDGE;
   const double flops = 2.0 * M * N * K;
   const double in = kind == TDM_KIND_F32 ? 4.0 : 2.0;
@@ -81,9 +83,9 @@ tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, 
   const double intensity = flops / bytes;
   if (kind == TDM_KIND_BF16_F32ACC) {
     const double ridge = kPeakMfmaBf16 / kHbmBandwidth;
-    if (intensity < ridge && supports(kind, TDM_PATH_SKINNY, M, N, K, ma, mb, mc, b_nk))
+    if (intensity < ridge && supports(kind, TDM_PATH_SKINNY, M, N, K, ma, mb, mc, b_nk, a_km))
       return TDM_PATH_SKINNY;
-    if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc, b_nk)) return TDM_PATH_MFMA;
+    if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc, b_nk, a_km)) return TDM_PATH_MFMA;
     return TDM_PATH_EDGE;
   }
   // fp32 has no streaming path; the choice is about filling the CUs. With
@@ -162,14 +164,19 @@ bool valid_path(tdm_path p) {
          p == TDM_PATH_MFMA || p == TDM_PATH_SKINNY;
 }
 
-// D = epilogue(A * op(B)) for bf16 inputs (include/tdm.h).
-tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layout, void* D,
+bool valid_layout(tdm_layout l) {
+  return l == TDM_LAYOUT_KN || l == TDM_LAYOUT_NK || l == TDM_LAYOUT_KM_KN ||
+         l == TDM_LAYOUT_KM_NK;
+}
+
+// D = epilogue(op(A) * op(B)) for bf16 inputs (include/tdm.h).
+tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout layout, void* D,
                         tdm_dtype d_type, const void* bias, const void* residual, int gelu,
                         int64_t M, int64_t N, int64_t K, tdm_path path, void* stream,
                         bool shared_scratch = false) {
   if (d_type != TDM_DTYPE_F32 && d_type != TDM_DTYPE_BF16) return TDM_ERROR_INVALID_VALUE;
-  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return TDM_ERROR_INVALID_VALUE;
-  const bool b_nk = b_layout == TDM_LAYOUT_NK;
+  if (!valid_layout(layout)) return TDM_ERROR_INVALID_VALUE;
+  const bool b_nk = (layout & TDM_LAYOUT_NK) != 0, a_km = (layout & TDM_LAYOUT_KM_KN) != 0;
   const uint64_t dsize = d_type == TDM_DTYPE_BF16 ? 2 : 4;
   if (M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
   if (M == 0 || N == 0) return TDM_SUCCESS;
@@ -189,7 +196,8 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layou
   if (residual != nullptr && residual != D && overlaps(D, d_bytes, residual, d_bytes))
     return TDM_ERROR_INVALID_VALUE;
   const int ma = misalign(A), mb = misalign(B);
-  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, 0, b_nk))
+  if (path != TDM_PATH_AUTO &&
+      !supports(TDM_KIND_BF16_F32ACC, path, M, N, K, ma, mb, 0, b_nk, a_km))
     return TDM_ERROR_NOT_SUPPORTED;
   tdm_status st = check_device();
   if (st != TDM_SUCCESS) return st;
@@ -200,15 +208,16 @@ tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout b_layou
   e.gelu = gelu != 0;
   e.d_bf16 = d_type == TDM_DTYPE_BF16;
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  if (K == 0) return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, D, m, n, 0, e, s));
-  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, 0, b_nk);
+  if (K == 0) return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, a_km, D, m, n, 0, e, s));
+  if (path == TDM_PATH_AUTO)
+    path = choose(TDM_KIND_BF16_F32ACC, M, N, K, ma, mb, 0, b_nk, a_km);
   switch (path) {
     case TDM_PATH_MFMA:
-      return to_status(tdm::launch_mfma_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
+      return to_status(tdm::launch_mfma_bf16_epi(A, B, b_nk, a_km, D, m, n, k, e, s));
     case TDM_PATH_SKINNY:
       return to_status(
           tdm::launch_skinny_bf16_epi(A, B, b_nk, D, m, n, k, e, s, shared_scratch));
-    default: return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, D, m, n, k, e, s));
+    default: return to_status(tdm::launch_edge_bf16_epi(A, B, b_nk, a_km, D, m, n, k, e, s));
   }
 }
 
@@ -354,26 +363,26 @@ tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, voi
                       stream);
 }
 
-tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout b_layout, void* D,
+tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout layout, void* D,
                         tdm_dtype d_type, const void* bias, const void* residual, int gelu,
                         int64_t M, int64_t N, int64_t K, void* stream) {
-  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
+  return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
                       stream);
 }
 
-tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B, tdm_layout layout,
                                 void* D, tdm_dtype d_type, const void* bias, const void* residual,
                                 int gelu, int64_t M, int64_t N, int64_t K, void* stream) {
-  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
+  return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
                       stream, true);
 }
 
-tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B, tdm_layout b_layout,
+tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B, tdm_layout layout,
                                  void* D, tdm_dtype d_type, const void* bias,
                                  const void* residual, int gelu, int64_t M, int64_t N,
                                  int64_t K, tdm_path path, void* stream) {
   if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
-  return run_bf16_epi(A, B, b_layout, D, d_type, bias, residual, gelu, M, N, K, path, stream);
+  return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, path, stream);
 }
 
 tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roofline* out) {
@@ -414,21 +423,22 @@ tdm_path tdm_select_path(tdm_kind kind, int64_t M, int64_t N, int64_t K) {
   return choose(kind, M, N, K, 0, 0, 0);
 }
 
-int tdm_path_supports_ex(tdm_kind kind, tdm_layout b_layout, tdm_path path, int64_t M,
+int tdm_path_supports_ex(tdm_kind kind, tdm_layout layout, tdm_path path, int64_t M,
                          int64_t N, int64_t K, int misalign_a, int misalign_b, int misalign_c) {
-  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return 0;
+  if (!valid_layout(layout)) return 0;
   if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return 0;
   if (!valid_path(path) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
   return supports(kind, path, M, N, K, misalign_a, misalign_b, misalign_c,
-                  b_layout == TDM_LAYOUT_NK) ? 1 : 0;
+                  (layout & TDM_LAYOUT_NK) != 0, (layout & TDM_LAYOUT_KM_KN) != 0) ? 1 : 0;
 }
 
-tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout b_layout, int64_t M, int64_t N,
+tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout layout, int64_t M, int64_t N,
                             int64_t K) {
   if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
-  if (b_layout != TDM_LAYOUT_KN && b_layout != TDM_LAYOUT_NK) return TDM_PATH_EDGE;
-  if (b_layout == TDM_LAYOUT_NK && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
-  return choose(kind, M, N, K, 0, 0, 0, b_layout == TDM_LAYOUT_NK);
+  if (!valid_layout(layout)) return TDM_PATH_EDGE;
+  if (layout != TDM_LAYOUT_KN && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
+  return choose(kind, M, N, K, 0, 0, 0, (layout & TDM_LAYOUT_NK) != 0,
+                (layout & TDM_LAYOUT_KM_KN) != 0);
 }
 
 const char* tdm_path_name(tdm_path p) {

@@ -96,6 +96,9 @@ hipError_t launch_mfma_fp8(const uint8_t* A, int a_fmt, const uint8_t* B, int b_
                            int K, const Epilogue& e, hipStream_t s);
 bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                            int mis_c);
+// ... with A stored K x M (C = A^T * op(B)): 16-byte chunks along M.
+bool mfma_bf16_akm_supports(int64_t M, int64_t N, int64_t K, bool b_nk, int mis_a, int mis_b,
+                            int mis_c);
 
 // bf16 small-M streaming kernel.
 bool skinny_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a,
@@ -125,12 +128,13 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* B, float* C,
                               int M, int N, int K, hipStream_t s);
 
 // The bf16 products with the fused epilogue of epilogue.h, written to D (fp32
-// or bf16 as e.d_bf16 says). b_nk: B is stored N x K (C = A * B^T). K may be
-// 0 on the edge kernel (D = epilogue(0)).
-hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                int M, int N, int K, const Epilogue& e, hipStream_t s);
-hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,
-                                int M, int N, int K, const Epilogue& e, hipStream_t s);
+// or bf16 as e.d_bf16 says). b_nk: B is stored N x K (op(B) = B^T); a_km: A
+// is stored K x M (op(A) = A^T). K may be 0 on the edge kernel (D =
+// epilogue(0)).
+hipError_t launch_edge_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, bool a_km,
+                                void* D, int M, int N, int K, const Epilogue& e, hipStream_t s);
+hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, bool a_km,
+                                void* D, int M, int N, int K, const Epilogue& e, hipStream_t s);
 // shared_scratch: the small-M K x N split-K partial sums go to the one
 // static buffer of the allocation-free entry point instead of the stream's.
 hipError_t launch_skinny_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, void* D,

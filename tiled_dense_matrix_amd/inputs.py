@@ -14,7 +14,8 @@ seed; A is drawn first, row-major, then B):
   round-to-nearest-even.
 * a fused-epilogue workload's bias: normal(0, bias_sigma) from its own
   generator, seeded with (seed, 1), in the output's element type.
-* a workload whose B is stored N x K draws B in that order (row n, then k).
+* a workload whose B is stored N x K draws B in that order (row n, then k);
+  one whose A is stored K x M draws A in that order (row k, then m).
 * FP8 workloads (B always N x K): normal(0, sigma) in float64, then either
   rounded straight to FP8 (nearest, ties to even, saturating at the largest
   finite value), or block-scaled first as the OCP Microscaling (MX) recipe
@@ -84,6 +85,9 @@ class Workload:
     # How B is stored: "kn" (K x N) or "nk" (N x K, a linear layer's weight;
     # the product is then A @ B.T).
     b_layout: str = "kn"
+    # How A is stored: "mk" (M x K) or "km" (K x M, the product is then
+    # A.T @ B, as in x = A.T @ B).
+    a_layout: str = "mk"
     # FP8 workloads: the formats of A and B, and whether they carry block
     # scales (one 8-bit power-of-two exponent per 32 k of each row).
     fp8: tuple = ("e4m3", "e4m3")
@@ -114,6 +118,8 @@ WORKLOADS = {
         Workload("bf16_skinny_nk", "bf16", 16, 8192, 8192, 6, "normal", 1.0, 0.02,
                  b_layout="nk"),
         Workload("bf16_skinny", "bf16", 16, 8192, 8192, 4, "normal", 1.0, 0.02),
+        # The square bf16 product with A stored K x M: x = A.T @ B.
+        Workload("bf16_8192_tn", "bf16", 8192, 8192, 8192, 10, "normal", a_layout="km"),
         # The MLP up-projection in E4M3 with block scales, weight N x K,
         # bf16 output.
         Workload("fp8_mlp", "fp8", 8192, 14336, 4096, 7, "normal", 1.0, 0.02, out="bf16",
@@ -155,8 +161,8 @@ def make_inputs(w: Workload | str):
     """Return (A, B) for a workload.
 
     fp32 workloads give float32 arrays; bf16 workloads give uint16 bf16 bits.
-    B comes in its stored shape: K x N, or N x K for b_layout "nk" (drawn in
-    that order).
+    A and B come in their stored shapes: A M x K, or K x M for a_layout "km";
+    B K x N, or N x K for b_layout "nk" (each drawn in that order).
     """
     if isinstance(w, str):
         w = WORKLOADS[w]
@@ -169,7 +175,7 @@ def make_inputs(w: Workload | str):
     elif w.kind == "bf16":
         if w.dist != "normal":
             raise ValueError(w.dist)
-        A = normal_bf16(rng, (w.M, w.K), w.sigma_a)
+        A = normal_bf16(rng, (w.K, w.M) if w.a_layout == "km" else (w.M, w.K), w.sigma_a)
         B = normal_bf16(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N), w.sigma_b)
     elif w.kind == "fp8":
         raise ValueError("FP8 workloads come with scales: use make_fp8_inputs")
@@ -265,7 +271,7 @@ def small_int_matrix(rng: np.random.Generator, shape, lo: int = -3, hi: int = 3,
 
 
 def make_integer_inputs(w: Workload | str, lo: int = -3, hi: int = 3):
-    """(A, B) with the workload's shapes, storage types and B layout, but
+    """(A, B) with the workload's shapes, storage types and layouts, but
     i.i.d. integers in [lo, hi] from a PCG64 generator seeded with (seed, 2)
     (A drawn first). With |values| <= 3 every partial sum of a product with
     K <= 8192 is an integer of magnitude at most 9K < 2^24, exact in fp32
@@ -276,7 +282,8 @@ def make_integer_inputs(w: Workload | str, lo: int = -3, hi: int = 3):
     if w.kind not in ("f32", "bf16"):
         raise ValueError(w.kind)
     rng = np.random.default_rng((w.seed, 2))
-    A = small_int_matrix(rng, (w.M, w.K), lo, hi, kind=w.kind)
+    A = small_int_matrix(rng, (w.K, w.M) if w.a_layout == "km" else (w.M, w.K), lo, hi,
+                         kind=w.kind)
     B = small_int_matrix(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N), lo, hi,
                          kind=w.kind)
     return A, B
