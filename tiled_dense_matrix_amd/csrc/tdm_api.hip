@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cstring>
+
 #include "tdm.h"
 #include "tdm_internal.h"
 
@@ -16,6 +18,21 @@ constexpr int64_t kMaxElems = int64_t{1} << 31;  // per matrix (32-bit indexing)
 // MI355X figures used by the dispatcher (AMD's published peaks).
 constexpr double kPeakMfmaBf16 = 2.5166e15;  // FLOP/s, dense
 constexpr double kHbmBandwidth = 8.0e12;     // B/s
+
+// The integer value of a C enum argument. A C caller may pass any int as an
+// enum parameter, but C++ may not read an enum object whose value lies
+// outside the enumeration's range, so every enum argument is range-checked
+// through its bytes before it is read as the enum.
+template <typename E>
+int raw(const E& e) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+bool valid_kind(int k) { return k == TDM_KIND_F32 || k == TDM_KIND_BF16_F32ACC; }
+bool valid_dtype(int d) { return d == TDM_DTYPE_F32 || d == TDM_DTYPE_BF16; }
+bool valid_fp8(int f) { return f == TDM_FP8_E4M3 || f == TDM_FP8_E5M2; }
 
 int misalign(const void* p) { return static_cast<int>(reinterpret_cast<uintptr_t>(p) & 15u); }
 
@@ -159,15 +176,8 @@ tdm_status run_bf16(const uint16_t* A, const uint16_t* B, float* C, int64_t M,
   }
 }
 
-bool valid_path(tdm_path p) {
-  return p == TDM_PATH_AUTO || p == TDM_PATH_EDGE || p == TDM_PATH_VALU ||
-         p == TDM_PATH_MFMA || p == TDM_PATH_SKINNY;
-}
-
-bool valid_layout(tdm_layout l) {
-  return l == TDM_LAYOUT_KN || l == TDM_LAYOUT_NK || l == TDM_LAYOUT_KM_KN ||
-         l == TDM_LAYOUT_KM_NK;
-}
+bool valid_path(int p) { return p >= TDM_PATH_AUTO && p <= TDM_PATH_SKINNY; }
+bool valid_layout(int l) { return l >= TDM_LAYOUT_KN && l <= TDM_LAYOUT_KM_NK; }
 
 // D = epilogue(op(A) * op(B)) for bf16 inputs (include/tdm.h).
 tdm_status run_bf16_epi(const uint16_t* A, const uint16_t* B, tdm_layout layout, void* D,
@@ -315,6 +325,8 @@ tdm_status gemm_fp8(const uint8_t* A, tdm_fp8_format a_format, const uint8_t* a_
                     const uint8_t* B, tdm_fp8_format b_format, const uint8_t* b_scale, void* D,
                     tdm_dtype d_type, const void* bias, const void* residual, int gelu, int64_t M,
                     int64_t N, int64_t K, void* stream) {
+  if (!valid_fp8(raw(a_format)) || !valid_fp8(raw(b_format)) || !valid_dtype(raw(d_type)))
+    return TDM_ERROR_INVALID_VALUE;
   return run_fp8(A, a_format, a_scale, B, b_format, b_scale, D, d_type, bias, residual, gelu, M,
                  N, K, stream);
 }
@@ -336,20 +348,21 @@ tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C, int6
 
 tdm_status tdm_gemm_f32_path(const float* A, const float* B, float* C, int64_t M,
                              int64_t N, int64_t K, tdm_path path, void* stream) {
-  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  if (!valid_path(raw(path))) return TDM_ERROR_INVALID_VALUE;
   return run_f32(A, B, C, M, N, K, path, stream);
 }
 
 tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B, float* C,
                                      int64_t M, int64_t N, int64_t K, tdm_path path,
                                      void* stream) {
-  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  if (!valid_path(raw(path))) return TDM_ERROR_INVALID_VALUE;
   return run_bf16(A, B, C, M, N, K, path, stream);
 }
 
 tdm_status gemm_bf16_epilogue(const uint16_t* A, const uint16_t* B, void* D, tdm_dtype d_type,
                               const void* bias, const void* residual, int gelu, int64_t M,
                               int64_t N, int64_t K, void* stream) {
+  if (!valid_dtype(raw(d_type))) return TDM_ERROR_INVALID_VALUE;
   return run_bf16_epi(A, B, TDM_LAYOUT_KN, D, d_type, bias, residual, gelu, M, N, K,
                       TDM_PATH_AUTO, stream);
 }
@@ -358,7 +371,7 @@ tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, voi
                                        tdm_dtype d_type, const void* bias, const void* residual,
                                        int gelu, int64_t M, int64_t N, int64_t K, tdm_path path,
                                        void* stream) {
-  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  if (!valid_path(raw(path)) || !valid_dtype(raw(d_type))) return TDM_ERROR_INVALID_VALUE;
   return run_bf16_epi(A, B, TDM_LAYOUT_KN, D, d_type, bias, residual, gelu, M, N, K, path,
                       stream);
 }
@@ -366,6 +379,7 @@ tdm_status tdm_gemm_bf16_epilogue_path(const uint16_t* A, const uint16_t* B, voi
 tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout layout, void* D,
                         tdm_dtype d_type, const void* bias, const void* residual, int gelu,
                         int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!valid_layout(raw(layout)) || !valid_dtype(raw(d_type))) return TDM_ERROR_INVALID_VALUE;
   return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
                       stream);
 }
@@ -373,6 +387,7 @@ tdm_status gemm_bf16_ex(const uint16_t* A, const uint16_t* B, tdm_layout layout,
 tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B, tdm_layout layout,
                                 void* D, tdm_dtype d_type, const void* bias, const void* residual,
                                 int gelu, int64_t M, int64_t N, int64_t K, void* stream) {
+  if (!valid_layout(raw(layout)) || !valid_dtype(raw(d_type))) return TDM_ERROR_INVALID_VALUE;
   return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, TDM_PATH_AUTO,
                       stream, true);
 }
@@ -381,12 +396,14 @@ tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B, tdm_layou
                                  void* D, tdm_dtype d_type, const void* bias,
                                  const void* residual, int gelu, int64_t M, int64_t N,
                                  int64_t K, tdm_path path, void* stream) {
-  if (!valid_path(path)) return TDM_ERROR_INVALID_VALUE;
+  if (!valid_path(raw(path)) || !valid_layout(raw(layout)) || !valid_dtype(raw(d_type)))
+    return TDM_ERROR_INVALID_VALUE;
   return run_bf16_epi(A, B, layout, D, d_type, bias, residual, gelu, M, N, K, path, stream);
 }
 
 tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roofline* out) {
   if (out == nullptr || M < 0 || N < 0 || K < 0) return TDM_ERROR_INVALID_VALUE;
+  if (!valid_kind(raw(kind))) return TDM_ERROR_INVALID_VALUE;
   double in_size;
   switch (kind) {
     case TDM_KIND_F32: in_size = 4.0; break;
@@ -401,7 +418,7 @@ tdm_status gemm_roofline(tdm_kind kind, int64_t M, int64_t N, int64_t K, tdm_roo
 }
 
 const char* tdm_status_string(tdm_status s) {
-  switch (s) {
+  switch (raw(s)) {
     case TDM_SUCCESS: return "success";
     case TDM_ERROR_INVALID_VALUE: return "invalid value";
     case TDM_ERROR_NOT_SUPPORTED: return "not supported";
@@ -413,36 +430,34 @@ const char* tdm_status_string(tdm_status s) {
 
 int tdm_path_supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
                       int misalign_a, int misalign_b, int misalign_c) {
-  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return 0;
-  if (!valid_path(path) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
+  if (!valid_kind(raw(kind))) return 0;
+  if (!valid_path(raw(path)) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
   return supports(kind, path, M, N, K, misalign_a, misalign_b, misalign_c) ? 1 : 0;
 }
 
 tdm_path tdm_select_path(tdm_kind kind, int64_t M, int64_t N, int64_t K) {
-  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
+  if (!valid_kind(raw(kind))) return TDM_PATH_EDGE;
   return choose(kind, M, N, K, 0, 0, 0);
 }
 
 int tdm_path_supports_ex(tdm_kind kind, tdm_layout layout, tdm_path path, int64_t M,
                          int64_t N, int64_t K, int misalign_a, int misalign_b, int misalign_c) {
-  if (!valid_layout(layout)) return 0;
-  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return 0;
-  if (!valid_path(path) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
+  if (!valid_layout(raw(layout)) || !valid_kind(raw(kind))) return 0;
+  if (!valid_path(raw(path)) || M < 0 || N < 0 || K < 0 || too_big(M, N, K)) return 0;
   return supports(kind, path, M, N, K, misalign_a, misalign_b, misalign_c,
                   (layout & TDM_LAYOUT_NK) != 0, (layout & TDM_LAYOUT_KM_KN) != 0) ? 1 : 0;
 }
 
 tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout layout, int64_t M, int64_t N,
                             int64_t K) {
-  if (kind != TDM_KIND_F32 && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
-  if (!valid_layout(layout)) return TDM_PATH_EDGE;
+  if (!valid_kind(raw(kind)) || !valid_layout(raw(layout))) return TDM_PATH_EDGE;
   if (layout != TDM_LAYOUT_KN && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
   return choose(kind, M, N, K, 0, 0, 0, (layout & TDM_LAYOUT_NK) != 0,
                 (layout & TDM_LAYOUT_KM_KN) != 0);
 }
 
 const char* tdm_path_name(tdm_path p) {
-  switch (p) {
+  switch (raw(p)) {
     case TDM_PATH_AUTO: return "auto";
     case TDM_PATH_EDGE: return "edge";
     case TDM_PATH_VALU: return "valu";
