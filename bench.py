@@ -107,6 +107,16 @@ def parse():
                          "--pmc output directories for the workload's dominant kernel (markdown)")
     ap.add_argument("--bench-line", metavar="FILE", default=None,
                     help="with --summarize-trace: the JSON line the profiled run printed")
+    ap.add_argument("--kernel", default=None,
+                    help="with --summarize-counters: the kernel to summarize (default: the "
+                         "workload's dominant kernel)")
+    ap.add_argument("--fetch-scale", type=float, default=2.0,
+                    help="bytes per FETCH_SIZE KiB / 1024, from a plain copy of known size")
+    ap.add_argument("--write-scale", type=float, default=1.0,
+                    help="bytes per WRITE_SIZE KiB / 1024, from a plain copy of known size")
+    ap.add_argument("--traffic-json", metavar="FILE", default=None,
+                    help="with --summarize-counters over FETCH_SIZE and WRITE_SIZE runs: write "
+                         "the kernel's HBM bytes per launch as the record bench.py reads")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the product, run a plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -209,7 +219,8 @@ def workload_kernels(name: str):
     if w.kind == "fp8":
         return KERNEL["mfma_fp8"]
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
-    layout = tdm.Layout.NK if w.b_layout == "nk" else tdm.Layout.KN
+    layout = tdm.Layout((tdm.Layout.NK if w.b_layout == "nk" else 0)
+                        | (tdm.Layout.KM_KN if w.a_layout == "km" else 0))
     pname = DEFAULT_PATH.get(name) or tdm.path_name(
         tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K))
     if pname == "mfma" and w.kind == "f32":
@@ -262,6 +273,7 @@ def summarize_counters(args):
     with derived rates. GRBM_GUI_ACTIVE counts each XCD's engine cycles, so
     its eighth is the cycles of the clock the counters ran at."""
     kernel, src, _ = workload_kernels(args.workload)
+    kernel = args.kernel or kernel
     per, durations = {}, []
     for root in args.summarize_counters:
         disp = {}
@@ -286,16 +298,22 @@ def summarize_counters(args):
     if durations:
         rows.append(("average dispatch under the counters (us)",
                      f"{sum(durations) / len(durations):.1f}"))
-    if avg.get("GRBM_GUI_ACTIVE"):
-        clk = avg["GRBM_GUI_ACTIVE"] / xcds
-        if durations:
-            rows.append(("engine clock from GRBM_GUI_ACTIVE (GHz)",
-                         f"{clk / (sum(durations) / len(durations)) / 1e3:.3f}"))
+    # The counters' window is a few microseconds longer than the dispatch, so
+    # GRBM_GUI_ACTIVE gives the clock only for long dispatches; short ones are
+    # rated against the 2.4 GHz peak clock over their duration.
+    us = sum(durations) / len(durations) if durations else 0.0
+    clk, where = None, ""
+    if avg.get("GRBM_GUI_ACTIVE") and us >= 200.0:
+        clk, where = avg["GRBM_GUI_ACTIVE"] / xcds, "at the measured clock"
+        rows.append(("engine clock from GRBM_GUI_ACTIVE (GHz)", f"{clk / us / 1e3:.3f}"))
+    elif us:
+        clk, where = us * 2.4e3, "at 2.4 GHz over the dispatch (too short to measure the clock)"
+    if clk:
         if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
-            rows.append(("MFMA busy / SIMD cycles at the measured clock",
+            rows.append((f"MFMA busy / SIMD cycles {where}",
                          f"{avg['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / clk:.3f}"))
         if "SQ_ACTIVE_INST_VALU" in avg:
-            rows.append(("VALU-active / SIMD cycles at the measured clock",
+            rows.append((f"VALU-active / SIMD cycles {where}",
                          f"{avg['SQ_ACTIVE_INST_VALU'] / simds / clk:.3f}"))
     if avg.get("SQ_INSTS_MFMA") and "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
         rows.append(("MFMA busy cycles per MFMA instruction",
@@ -308,6 +326,20 @@ def summarize_counters(args):
                         ("SQ_WAIT_INST_LDS", "waiting on LDS")):
             if c in avg:
                 rows.append((f"{what} / wave cycles", f"{avg[c] / avg['SQ_WAVE_CYCLES']:.3f}"))
+    if "FETCH_SIZE" in avg and "WRITE_SIZE" in avg:
+        fetch = avg["FETCH_SIZE"] * 1024 * args.fetch_scale
+        write = avg["WRITE_SIZE"] * 1024 * args.write_scale
+        rows.append(("HBM bytes read per launch (FETCH_SIZE, scaled)", f"{fetch:,.0f}"))
+        rows.append(("HBM bytes written per launch (WRITE_SIZE, scaled)", f"{write:,.0f}"))
+        rows.append(("HBM bytes per launch", f"{fetch + write:,.0f}"))
+        if args.traffic_json:
+            rec = {"kernel": kernel, "workload": args.workload, "source": src,
+                   "source_sha": src_digest(src), "fetch_kib_raw": avg["FETCH_SIZE"],
+                   "write_kib_raw": avg["WRITE_SIZE"], "fetch_scale": args.fetch_scale,
+                   "write_scale": args.write_scale, "hbm_bytes_per_launch": fetch + write}
+            with open(args.traffic_json, "w") as fh:
+                json.dump(rec, fh, indent=1)
+                fh.write("\n")
     if rows:
         print("\n| derived | value |\n|---|---:|")
         for k, v in rows:
@@ -333,11 +365,13 @@ def cpu_baseline(w, A, B, C_gpu, target_s: float, bias=None):
     if any); also check those rows."""
     import oracle
     threads = oracle.default_threads()
-    # Calibrate on one row per thread, then size the sample to ~target_s.
+    # Calibrate on one row per thread (the second of two calls: the first
+    # also starts the thread pool), then size the sample to ~target_s.
     rows = min(w.M, threads)
-    t0 = time.perf_counter()
-    oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
-    per_row = max(time.perf_counter() - t0, 1e-6) / rows
+    for _ in range(2):
+        t0 = time.perf_counter()
+        oracle.gemm_block(A, B, (0, rows), (0, w.N), threads)
+        per_row = max(time.perf_counter() - t0, 1e-6) / rows
     rows = int(max(1, min(w.M, math.floor(target_s / per_row))))
     if rows >= threads:
         rows -= rows % threads  # whole rows per thread

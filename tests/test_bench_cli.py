@@ -27,14 +27,14 @@ def test_world_size_above_one_is_refused():
 
 
 def test_committed_default_bench_line_keeps_the_contract():
-    with open(os.path.join(ROOT, "profiles", "bench.f32_4096.json")) as fh:
+    with open(os.path.join(ROOT, "profiles", "bench.bf16_8192.json")) as fh:
         line = json.loads(fh.read())
     for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
                 "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
                 "roofline", "cpu_baseline"):
         assert key in line, key
     assert line["n_gpus"] == 1 and line["data"] == "synthetic"
-    assert line["config"]["workload"] == "f32_4096"
+    assert line["config"]["workload"] == "bf16_8192"
     roof = line["roofline"]
     assert roof["bound"] in ("hbm", "mfma", "alu")
     assert abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-3
@@ -45,7 +45,7 @@ def test_committed_default_bench_line_keeps_the_contract():
 def test_vendor_comparison_is_opt_in():
     r = run_bench("--help")
     assert r.returncode == 0 and "--vendor" in r.stdout
-    with open(os.path.join(ROOT, "profiles", "bench.f32_4096.json")) as fh:
+    with open(os.path.join(ROOT, "profiles", "bench.bf16_8192.json")) as fh:
         assert "vendor_blas" not in json.loads(fh.read())
 
 
@@ -97,3 +97,39 @@ def test_counter_summary_normalizes_to_the_measured_clock(tmp_path):
     assert r.returncode == 0, r.stderr
     assert "| engine clock from GRBM_GUI_ACTIVE (GHz) | 1.500 |" in r.stdout
     assert "| MFMA busy / SIMD cycles at the measured clock | 0.800 |" in r.stdout
+
+
+def test_counter_summary_rates_short_dispatches_at_the_peak_clock(tmp_path):
+    """A 20 us dispatch: its counter window is longer than the dispatch, so no
+    clock is derived and the rates use 2.4 GHz over the duration."""
+    name = "void tdm::(anonymous namespace)::skinny_nk_bf16_kernel(...)"
+    rows = [[0, name, "GRBM_GUI_ACTIVE", 8 * 60e3, 0, 20_000],
+            [0, name, "SQ_VALU_MFMA_BUSY_CYCLES", 1024 * 4.8e3, 0, 20_000]]
+    _write_csv(str(tmp_path / "p" / "run_counter_collection.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                "Start_Timestamp", "End_Timestamp"], rows)
+    r = run_bench("--summarize-counters", str(tmp_path / "p"), "--workload", "bf16_skinny_nk")
+    assert r.returncode == 0, r.stderr
+    assert "engine clock" not in r.stdout
+    assert "| MFMA busy / SIMD cycles at 2.4 GHz over the dispatch (too short to measure " \
+           "the clock) | 0.100 |" in r.stdout
+
+
+def test_traffic_record_from_byte_counters(tmp_path):
+    """FETCH_SIZE and WRITE_SIZE (KiB per dispatch, from two runs) scaled by
+    the copy calibration give the record bench.py reads as roofline.traffic."""
+    name = "void tdm::(anonymous namespace)::mfma_bf16_kernel<...>(...)"
+    for c, v in (("FETCH_SIZE", 1000.0), ("WRITE_SIZE", 300.0)):
+        _write_csv(str(tmp_path / c / "run_counter_collection.csv"),
+                   ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"],
+                   [[d, name, c, v, 0, 500_000] for d in range(3)])
+    out = tmp_path / "t.json"
+    r = run_bench("--summarize-counters", str(tmp_path / "FETCH_SIZE"),
+                  str(tmp_path / "WRITE_SIZE"), "--workload", "bf16_8192", "--fetch-scale", "2.0",
+                  "--write-scale", "1.0", "--traffic-json", str(out))
+    assert r.returncode == 0, r.stderr
+    rec = json.loads(out.read_text())
+    assert rec["kernel"] == "mfma_bf16_kernel" and rec["workload"] == "bf16_8192"
+    assert rec["hbm_bytes_per_launch"] == (1000.0 * 2.0 + 300.0) * 1024
+    assert rec["source"] == "gemm_mfma_bf16.hip" and len(rec["source_sha"]) == 16
