@@ -208,9 +208,10 @@ def _short(name: str, kernels):
     return None
 
 
-def workload_kernels(name: str):
+def workload_kernels(name: str, path=None):
     """(dominant kernel, source, kernels of one call) of a workload on the
-    path bench.py runs it on by default."""
+    given path (a --path name), else on the path bench.py runs it on by
+    default."""
     import tiled_dense_matrix_amd as tdm
     from tiled_dense_matrix_amd import inputs
     if name in inputs.ATTN_WORKLOADS:
@@ -221,8 +222,8 @@ def workload_kernels(name: str):
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
     layout = tdm.Layout((tdm.Layout.NK if w.b_layout == "nk" else 0)
                         | (tdm.Layout.KM_KN if w.a_layout == "km" else 0))
-    pname = DEFAULT_PATH.get(name) or tdm.path_name(
-        tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K))
+    pname = path if path not in (None, "auto") else DEFAULT_PATH.get(name)
+    pname = pname or tdm.path_name(tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K))
     if pname == "mfma" and w.kind == "f32":
         pname = "mfma_f32"
     if pname == "skinny" and w.b_layout == "nk":
@@ -234,7 +235,7 @@ def summarize_trace(args):
     """Markdown summary of a kernel trace: for each kernel of the workload,
     all its dispatches and the timed ones (dispatches warmup .. warmup +
     steps - 1 of that kernel, in start order), in microseconds."""
-    _, src, kernels = workload_kernels(args.workload)
+    _, src, kernels = workload_kernels(args.workload, args.path)
     by = {}
     for r in _csv_rows(args.summarize_trace, "kernel_trace.csv"):
         k = _short(r["Kernel_Name"], kernels)
@@ -272,7 +273,7 @@ def summarize_counters(args):
     workload's dominant kernel) from one or more rocprofv3 --pmc outputs,
     with derived rates. GRBM_GUI_ACTIVE counts each XCD's engine cycles, so
     its eighth is the cycles of the clock the counters ran at."""
-    kernel, src, _ = workload_kernels(args.workload)
+    kernel, src, _ = workload_kernels(args.workload, args.path)
     kernel = args.kernel or kernel
     per, durations = {}, []
     for root in args.summarize_counters:
