@@ -242,7 +242,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
       __syncthreads();
     }
 
-    // 1. S^T for the two 32-key halves.
+    // 1. S^T for the two 32-key halves. The wave issues its MFMA sections
+    // at raised priority and its softmax at normal priority, so that on a
+    // SIMD shared by two waves the matrix core is served first (1.5-2.3%
+    // faster on 4 x 32 x 4096 x 128; results unchanged).
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -256,6 +260,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
       }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // 2. Online softmax (base 2). Masked scores are -inf; the mask is one
     // uniform branch (the last key block, and blocks on the causal diagonal).
 #pragma unroll
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     }
 
     // 3. O^T += V^T P^T over the four 16-key windows.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int w16 = 0; w16 < 4; ++w16) {
       const int h = w16 >> 1, e0 = 8 * (w16 & 1);
@@ -334,6 +340,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     }
   }
 
+  __builtin_amdgcn_s_setprio(0);
   // O = acc / l (bf16), lse = (m + log2 l) * ln 2. Lane l holds query lr,
   // d = 32*db + 8*(v/4) + 4*lg + v%4: four consecutive d per 8-byte store.
   if (query < n_q) {
