@@ -21,6 +21,12 @@ Consecutive steps rotate over several copies of (A, B, C) whose total size
 exceeds the 256 MB last-level cache, so every step reads its operands from
 HBM.
 
+Before the warm-up steps the step runs for --prewarm-s seconds of wall time
+(0.25 by default; the count is reported as config.prewarm_calls): after the
+host-side input generation the engine clock takes tens of milliseconds to
+leave its idle state, and with 5 warm-up steps the first timed steps of the
+8192^3 product ran 9% slower than in steady state.
+
 The timed region is bracketed by device synchronisation, with HIP events
 recorded on the stream the kernels are launched on. It is also the only
 region a profiler started with `rocprofv3 --selected-regions` records
@@ -89,6 +95,8 @@ def parse():
     ap.add_argument("--path", default=None,
                     help="force a path (auto/edge/valu/mfma/skinny); default: the workload's "
                          "specified path (valu for f32_4096), else auto")
+    ap.add_argument("--prewarm-s", type=float, default=0.25,
+                    help="seconds of untimed steps before the warm-up steps (0: none)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -233,9 +241,15 @@ def workload_kernels(name: str, path=None):
 
 def summarize_trace(args):
     """Markdown summary of a kernel trace: for each kernel of the workload,
-    all its dispatches and the timed ones (dispatches warmup .. warmup +
-    steps - 1 of that kernel, in start order), in microseconds."""
+    all its dispatches and the timed ones (dispatches p + warmup .. p +
+    warmup + steps - 1 of that kernel, in start order, p = the pre-warm
+    calls the run's line reports), in microseconds."""
     _, src, kernels = workload_kernels(args.workload, args.path)
+    line = None
+    if args.bench_line:
+        with open(args.bench_line) as fh:
+            line = json.loads([x for x in fh.read().splitlines() if x.startswith("{")][-1])
+    first = int((line or {}).get("config", {}).get("prewarm_calls", 0)) + args.warmup
     by = {}
     for r in _csv_rows(args.summarize_trace, "kernel_trace.csv"):
         k = _short(r["Kernel_Name"], kernels)
@@ -247,7 +261,7 @@ def summarize_trace(args):
     timed_total = 0.0
     for k in kernels:
         us = [(e - b) / 1e3 for b, e in sorted(by.get(k, []))]
-        t = sorted(us[args.warmup:args.warmup + args.steps])
+        t = sorted(us[first:first + args.steps])
         if not t:
             raise SystemExit(f"{k}: {len(us)} dispatches, none in the timed window")
         avg_t = sum(t) / len(t)
@@ -255,9 +269,7 @@ def summarize_trace(args):
         out.append(f"| {k} | {len(us)} | {sum(us) / len(us):.1f} | {len(t)} | {avg_t:.1f} | "
                    f"{t[0]:.1f} | {t[len(t) // 2]:.1f} | {t[-1]:.1f} |")
     print("\n".join(out))
-    if args.bench_line:
-        with open(args.bench_line) as fh:
-            line = json.loads([x for x in fh.read().splitlines() if x.startswith("{")][-1])
+    if line is not None:
         step_us = line["ms_per_step"] * 1e3
         roof = line["roofline"]
         print(f"\nbench.py line of the same run: {step_us:.1f} us per step, {line['value']} "
@@ -499,6 +511,7 @@ def main():
     def timed(p) -> float:
         return time_steps(lambda i: call(i, p))
 
+    prewarm_calls = prewarm(lambda i: call(i, path), args.prewarm_s)
     ms = timed(path)
     profiled = False
 
@@ -623,7 +636,7 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K,
                    "inputs": f"seed {w.seed}, {w.dist}",
                    "path": pname, "kernel": kernel, "kernels_per_call": kernels,
-                   "rotated_copies": rot,
+                   "rotated_copies": rot, "prewarm_calls": prewarm_calls,
                    "auto_path": auto_info,
                    "b_layout": w.b_layout, "a_layout": w.a_layout,
                    "epilogue": None if not epi else {"bias": bias_np is not None,
@@ -646,6 +659,20 @@ def main():
         A_mk = np.ascontiguousarray(A.T) if km else A  # ... and A as M x K
         line["cpu_baseline"] = cpu_baseline(w, A_mk, B_kn, C_gpu, args.cpu_seconds, bias_np)
     print(json.dumps(line), flush=True)
+
+
+def prewarm(step, seconds: float) -> int:
+    """Run step(i) in bursts of four until `seconds` of wall time have
+    passed; return the number of calls."""
+    import torch
+    torch.cuda.synchronize()
+    t0, n = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(4):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
 
 
 def time_calls(step, warmup: int, steps: int, stream, profiled: bool = False) -> float:
@@ -734,6 +761,7 @@ def main_fp8(args, w):
         a, b, s_a, s_b, c = sets[i % rot]
         tdm.gemm_fp8(a, b, fa, fb, s_a, s_b, D=c, gelu=w.gelu, stream=stream)
 
+    prewarm_calls = prewarm(call, args.prewarm_s)
     ms = time_calls(call, args.warmup, args.steps, stream, profiled=True)
     flops = 2.0 * w.M * w.N * w.K
     alg_bytes = A.size + B.size + scale_bytes + out_size * w.M * w.N
@@ -787,7 +815,8 @@ def main_fp8(args, w):
                              + ("32-k block scales" if w.scaled else "no scales"),
                    "formats": list(w.fp8), "b_layout": "nk", "out": w.out,
                    "path": "mfma", "kernel": kernel, "kernels_per_call": kernels,
-                   "rotated_copies": rot, "gbps_algorithmic": round(gbs, 1)},
+                   "rotated_copies": rot, "prewarm_calls": prewarm_calls,
+                   "gbps_algorithmic": round(gbs, 1)},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK["mfma_fp8"],
                      "unit": "TFLOP/s", "scope": "kernel",
                      "frac": round(tflops / PEAK["mfma_fp8"], 4),
@@ -859,6 +888,7 @@ def main_attention(args, w):
                                1 if w.causal else 0, stream.cuda_stream)
         assert st == 0, st
 
+    prewarm_calls = prewarm(call, args.prewarm_s)
     ms = time_calls(call, args.warmup, args.steps, stream, profiled=True)
     flops = w.flops
     alg_bytes = 4 * Q.size * 2 + bh * w.seq * 4  # Q, K, V read once; O and lse written
@@ -900,6 +930,7 @@ def main_attention(args, w):
                    "head_dim": w.head_dim, "causal": w.causal,
                    "inputs": f"seed {w.seed}, normal", "kernel": kernel,
                    "kernels_per_call": kernels, "rotated_copies": rot,
+                   "prewarm_calls": prewarm_calls,
                    "flops_counted": "4 * head_dim per visible (query, key) pair"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK["mfma_bf16"],
                      "unit": "TFLOP/s", "scope": "kernel",

@@ -83,6 +83,34 @@ def test_trace_summary_takes_the_timed_dispatches(tmp_path):
     assert "Timed kernel time per step 23.0 us = 0.920 of the step" in r.stdout
 
 
+def test_trace_summary_skips_the_prewarm_calls(tmp_path):
+    """The calls the run made before its warm-up (config.prewarm_calls in its
+    line) are skipped too: 4 pre-warm calls at 300 us, 2 warm-up at 100 us,
+    then 3 timed at 40 us."""
+    name = "void tdm::(anonymous namespace)::mfma_bf16_kernel<...>(...)"
+    rows, t = [], 0
+    for i in range(9):
+        dur = 300_000 if i < 4 else 100_000 if i < 6 else 40_000
+        rows.append([i, name, t, t + dur])
+        t += dur + 5_000
+    _write_csv(str(tmp_path / "host" / "1_run_kernel_trace.csv"),
+               ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp"], rows)
+    line = tmp_path / "line.json"
+    line.write_text(json.dumps({"ms_per_step": 0.041, "value": 1.0, "unit": "TFLOP/s",
+                                "config": {"prewarm_calls": 4},
+                                "roofline": {"achieved": 1.0, "unit": "TFLOP/s", "peak": 2516.6,
+                                             "frac": 0.0004}}) + "\n")
+    r = run_bench("--summarize-trace", str(tmp_path), "--workload", "bf16_8192", "--steps", "3",
+                  "--warmup", "2", "--bench-line", str(line))
+    assert r.returncode == 0, r.stderr
+    assert "| mfma_bf16_kernel | 9 | " in r.stdout and "| 3 | 40.0 | 40.0 | 40.0 | 40.0 |" in r.stdout
+
+
+def test_prewarm_option_is_documented():
+    r = run_bench("--help")
+    assert r.returncode == 0 and "--prewarm-s" in r.stdout
+
+
 def test_counter_summary_normalizes_to_the_measured_clock(tmp_path):
     name = "void tdm::(anonymous namespace)::mfma_bf16_kernel<...>(...)"
     rows = []
