@@ -481,7 +481,9 @@ def main():
 
     def call(i, p):
         a, b, c = sets[i % rot]
-        if epi or nk or km:
+        if w.kind == "f32" and (nk or km):
+            tdm.tdm_gemm_f32_ex_path(a, b, layout, c, path=p, stream=stream)
+        elif epi or nk or km:
             tdm.tdm_gemm_bf16_ex_path(a, b, layout, c, bias=bias_d, gelu=w.gelu, path=p,
                                       stream=stream)
         else:
@@ -590,6 +592,10 @@ def main():
         if w.kind == "f32":
             vsets = [(a, b) for a, b, _ in sets]
             vmm, vop = torch.mm, "torch.mm"
+            if km or nk:  # the transposed views of the stored operands
+                vmm = lambda a, b: torch.mm(a.t() if km else a, b.t() if nk else b)  # noqa: E731
+                vop = "torch.mm with " + " and ".join(
+                    x for x, on in (("A.t()", km), ("B.t()", nk)) if on)
         else:
             vsets = [(a.view(torch.bfloat16), b.view(torch.bfloat16)) for a, b, _ in sets]
             if not epi:

@@ -183,6 +183,25 @@ TDM_API tdm_status tdm_gemm_bf16_ex_path(const uint16_t* A, const uint16_t* B,
                                          int64_t M, int64_t N, int64_t K, tdm_path path,
                                          void* stream);
 
+/* gemm_f32 with A and B in any layout: C = op(A) * op(B), op(A) = A^T when
+ * A is stored K x M, op(B) = B^T when B is stored N x K (CS336 Lecture 5 GPU
+ * notes, review question 5 on x = A.T @ B and the §4.1 warning on transposed
+ * views: a transposed operand is a different memory layout, not a free
+ * view). M, N and K are the sizes of the product C[M,N] = op(A)[M,K] *
+ * op(B)[K,N] whatever the layout; C is M x N, row-major, overwritten.
+ * Arguments, ownership, validation and errors as gemm_f32;
+ * TDM_ERROR_INVALID_VALUE for an unknown layout. A transposed operand runs
+ * on the fp32 matrix cores (K a multiple of 4, N a multiple of 4 when B is
+ * K x N, M a multiple of 4 when A is K x M, 16-byte aligned A and B) or the
+ * edge kernel; the vector-ALU kernel takes TDM_LAYOUT_KN only
+ * (tdm_gemm_f32_ex_path with TDM_PATH_VALU and another layout:
+ * TDM_ERROR_NOT_SUPPORTED). */
+TDM_API tdm_status gemm_f32_ex(const float* A, const float* B, tdm_layout layout, float* C,
+                               int64_t M, int64_t N, int64_t K, void* stream);
+TDM_API tdm_status tdm_gemm_f32_ex_path(const float* A, const float* B, tdm_layout layout,
+                                        float* C, int64_t M, int64_t N, int64_t K,
+                                        tdm_path path, void* stream);
+
 /* gemm_bf16_ex that allocates nothing and keeps no per-stream state, for
  * callers that cannot allocate device memory at call time: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.

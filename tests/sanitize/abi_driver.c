@@ -65,6 +65,15 @@ int main(void) {
   EXPECT(tdm_select_path_ex(TDM_KIND_BF16_F32ACC, TDM_LAYOUT_KN, 16, 8192, 8192) ==
          TDM_PATH_SKINNY);
   EXPECT(tdm_select_path_ex(TDM_KIND_F32, (tdm_layout)3, 64, 64, 64) == TDM_PATH_EDGE);
+  for (int l = 0; l < 4; ++l)
+    EXPECT(gemm_f32_ex(P(A), P(B), (tdm_layout)l, P(C), 64, 64, 64, NULL) == ND);
+  EXPECT(gemm_f32_ex(P(A), P(B), (tdm_layout)4, P(C), 64, 64, 64, NULL) == INV);
+  EXPECT(gemm_f32_ex(P(A), P(B), TDM_LAYOUT_NK, P(A + 8), 4, 4, 4, NULL) == INV);
+  EXPECT(tdm_gemm_f32_ex_path(P(A), P(B), TDM_LAYOUT_KM_KN, P(C), 64, 64, 64, TDM_PATH_VALU,
+                              NULL) == NS);
+  EXPECT(tdm_gemm_f32_ex_path(P(A), P(B), TDM_LAYOUT_KM_NK, P(C), 64, 64, 64, (tdm_path)9,
+                              NULL) == INV);
+  EXPECT(tdm_select_path_ex(TDM_KIND_F32, TDM_LAYOUT_KM_NK, 4096, 4096, 4096) == TDM_PATH_MFMA);
   /* FP8 */
   EXPECT(gemm_fp8(P(A), TDM_FP8_E4M3, NULL, P(B), TDM_FP8_E5M2, NULL, P(C), TDM_DTYPE_F32, NULL,
                   NULL, 0, 64, 64, 96, NULL) == ND);

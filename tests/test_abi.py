@@ -273,11 +273,41 @@ def test_layouts_of_a_and_b():
     assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.MFMA, 256, 257, 520)
     assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.MFMA, 33, 64, 64)
     assert not tdm.tdm_path_supports_ex(K_, L.KM_KN, P.SKINNY, 16, 1024, 2048)
-    assert not tdm.tdm_path_supports_ex(tdm.Kind.F32, L.KM_KN, P.EDGE, 64, 64, 64)
     assert tdm.tdm_select_path_ex(K_, L.KM_KN, 16, 8192, 8192) == P.MFMA
     assert tdm.tdm_select_path_ex(K_, L.KM_NK, 8192, 8192, 8192) == P.MFMA
     assert tdm.tdm_select_path_ex(K_, L.KM_KN, 33, 65, 17) == P.EDGE
     assert tdm.tdm_select_path_ex(K_, L.KN, 16, 8192, 8192) == P.SKINNY
+
+
+def test_f32_layouts():
+    """gemm_f32_ex takes the four layouts (another value is rejected); a
+    transposed operand runs on the fp32 matrix cores or the edge kernel,
+    never on the vector-ALU kernel; the matrix cores want K, and N (B stored
+    K x N) or M (A stored K x M), multiples of 4."""
+    lib = tdm.load()
+    S, P, L, F = tdm.Status, tdm.Path, tdm.Layout, tdm.Kind.F32
+    f, fp = lib.gemm_f32_ex, lib.tdm_gemm_f32_ex_path
+    for bad in (4, -1, 7):
+        assert f(FAKE, FAKE_B, bad, FAKE_C, 64, 64, 64, None) == S.ERROR_INVALID_VALUE
+        assert fp(FAKE, FAKE_B, bad, FAKE_C, 64, 64, 64, P.EDGE, None) == S.ERROR_INVALID_VALUE
+    for layout in (L.NK, L.KM_KN, L.KM_NK):
+        assert fp(FAKE, FAKE_B, layout, FAKE_C, 256, 256, 256, P.VALU, None) == \
+            S.ERROR_NOT_SUPPORTED
+        assert not tdm.tdm_path_supports_ex(F, layout, P.VALU, 4096, 4096, 4096)
+        assert not tdm.tdm_path_supports_ex(F, layout, P.SKINNY, 16, 4096, 4096)
+        assert tdm.tdm_path_supports_ex(F, layout, P.EDGE, 33, 65, 17)
+        assert tdm.tdm_path_supports_ex(F, layout, P.MFMA, 256, 256, 256)
+        assert tdm.tdm_select_path_ex(F, layout, 4096, 4096, 4096) == P.MFMA
+        assert tdm.tdm_select_path_ex(F, layout, 64, 64, 64) == P.EDGE
+        assert not tdm.tdm_path_supports_ex(F, layout, P.MFMA, 256, 256, 258)  # K % 4
+    assert tdm.tdm_path_supports_ex(F, L.NK, P.MFMA, 256, 257, 256)      # any N, B N x K
+    assert not tdm.tdm_path_supports_ex(F, L.KM_KN, P.MFMA, 256, 257, 256)
+    assert tdm.tdm_path_supports_ex(F, L.NK, P.MFMA, 257, 256, 256)      # any M, A M x K
+    assert not tdm.tdm_path_supports_ex(F, L.KM_NK, P.MFMA, 258, 256, 256)
+    assert tdm.tdm_select_path_ex(F, L.KN, 4096, 4096, 4096) == P.MFMA
+    # the plain product through the new entry point keeps gemm_f32's validation
+    assert f(None, FAKE_B, L.KN, FAKE_C, 64, 64, 64, None) == S.ERROR_INVALID_VALUE
+    assert f(FAKE, FAKE_B, L.NK, FAKE, 64, 64, 64, None) == S.ERROR_INVALID_VALUE  # C overlaps A
 
 
 def test_epilogue_in_place_residual_and_k_zero_pass_validation():

@@ -47,7 +47,14 @@ CASES = [
     ("bf16_skinny", P.AUTO), ("bf16_skinny_nk", P.AUTO),
     # the linear layer's shape with B stored N x K, plain fp32 output
     ("bf16_linear_gelu", P.AUTO),
+    # the fp32 4096^3 product with B stored N x K, and with A stored K x M
+    ("f32_4096_nk", P.AUTO), ("f32_4096_tn", P.AUTO),
 ]
+
+
+def _layout(w):
+    return tdm.Layout((tdm.Layout.NK if w.b_layout == "nk" else 0)
+                      | (tdm.Layout.KM_KN if w.a_layout == "km" else 0))
 
 
 def _ids():
@@ -57,9 +64,11 @@ def _ids():
 def product(w, A, B, path):
     """The GPU product of (A, B) for workload w through the C ABI, fp32."""
     Ad, Bd = to_device(A), to_device(B)
-    if w.b_layout == "nk":
-        C = tdm.tdm_gemm_bf16_ex_path(Ad, Bd, tdm.Layout.NK, out_dtype=torch.float32,
-                                      path=path)
+    layout = _layout(w)
+    if layout != tdm.Layout.KN and w.kind == "f32":
+        C = tdm.tdm_gemm_f32_ex_path(Ad, Bd, layout, path=path)
+    elif layout != tdm.Layout.KN:
+        C = tdm.tdm_gemm_bf16_ex_path(Ad, Bd, layout, out_dtype=torch.float32, path=path)
     else:
         C = run(w.kind, Ad, Bd, path)
     torch.cuda.synchronize()
@@ -70,14 +79,16 @@ def product(w, A, B, path):
 
 
 def reference(w, A, B):
-    """The oracle's fp64 product (B in its stored layout)."""
+    """The oracle's fp64 product (A and B in their stored layouts)."""
+    if w.a_layout == "km":
+        return oracle.gemm_tn(A, B) if w.b_layout == "kn" else \
+            oracle.gemm(np.ascontiguousarray(A.T), np.ascontiguousarray(B.T))
     return oracle.gemm_nt(A, B) if w.b_layout == "nk" else oracle.gemm(A, B)
 
 
 def path_taken(w, path):
     kind = tdm.Kind.F32 if w.kind == "f32" else tdm.Kind.BF16_F32ACC
-    layout = tdm.Layout.NK if w.b_layout == "nk" else tdm.Layout.KN
-    return path if path != P.AUTO else tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K)
+    return path if path != P.AUTO else tdm.tdm_select_path_ex(kind, _layout(w), w.M, w.N, w.K)
 
 
 @pytest.mark.parametrize("name,path", CASES, ids=_ids())

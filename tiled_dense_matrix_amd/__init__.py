@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     gemm_bf16_ex_noalloc,
     gemm_bf16_f32acc,
     gemm_f32,
+    gemm_f32_ex,
     gemm_fp8,
     gemm_roofline,
     load,
@@ -29,6 +30,7 @@ from ._lib import (  # noqa: F401
     tdm_gemm_bf16_ex_path,
     tdm_gemm_bf16_f32acc_path,
     tdm_fp8_supports,
+    tdm_gemm_f32_ex_path,
     tdm_gemm_f32_path,
     tdm_path_supports,
     tdm_path_supports_ex,

@@ -32,6 +32,9 @@ SIGNATURES = {
     "gemm_roofline": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, ctypes.POINTER(Roofline)]),
     "tdm_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "tdm_gemm_f32_path": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]),
+    "gemm_f32_ex": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, _i64, _i64, _i64, _p]),
+    "tdm_gemm_f32_ex_path": (ctypes.c_int, [_p, _p, ctypes.c_int, _p, _i64, _i64, _i64,
+                                            ctypes.c_int, _p]),
     "tdm_gemm_bf16_f32acc_path": (ctypes.c_int, [_p, _p, _p, _i64, _i64, _i64, ctypes.c_int, _p]),
     "tdm_path_supports": (ctypes.c_int, [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int]),
@@ -245,6 +248,60 @@ def tdm_gemm_f32_path(A, B, C=None, path=Path.AUTO, stream=None):
     torch = _torch()
     M, N, K, C = _prep(A, B, C, (torch.float32,))
     return _call("tdm_gemm_f32_path", A, B, C, M, N, K, stream, path)
+
+
+def _prep_layout(A, B, C, layout, in_dtypes):
+    """Shapes of op(A) @ op(B) for A, B stored as `layout` says; returns
+    (M, N, K, C)."""
+    torch = _torch()
+    layout = Layout(layout)
+    _check_matrix("A", A, in_dtypes)
+    K, M = A.shape if layout & Layout.KM_KN else A.shape[::-1]
+    if layout & Layout.NK:
+        _check_matrix("B", B, in_dtypes, cols=K)
+        N = B.shape[0]
+    else:
+        _check_matrix("B", B, in_dtypes, rows=K)
+        N = B.shape[1]
+    if A.device != B.device:
+        raise ValueError("A and B are on different devices")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    else:
+        _check_matrix("C", C, (torch.float32,), rows=M, cols=N)
+        if C.device != A.device:
+            raise ValueError("C is on another device than A and B")
+    return M, N, K, C
+
+
+def _call_layout(fname: str, A, B, layout, C, M, N, K, stream, path=None):
+    torch = _torch()
+    fn = getattr(load(), fname)
+    with torch.cuda.device(A.device):
+        args = [A.data_ptr() or None, B.data_ptr() or None, int(layout), C.data_ptr() or None,
+                M, N, K]
+        if path is not None:
+            args.append(int(path))
+        args.append(_stream_handle(stream))
+        st = fn(*args)
+    if st != Status.SUCCESS:
+        raise TdmError(st, fname)
+    return C
+
+
+def gemm_f32_ex(A, B, layout=Layout.KN, C=None, stream=None):
+    """C = op(A) @ op(B) for fp32 A, B: op(A) = A.T when A is stored K x M
+    (Layout.KM_KN, Layout.KM_NK), op(B) = B.T when B is stored N x K
+    (Layout.NK, Layout.KM_NK). Returns C (M x N, fp32)."""
+    torch = _torch()
+    M, N, K, C = _prep_layout(A, B, C, layout, (torch.float32,))
+    return _call_layout("gemm_f32_ex", A, B, layout, C, M, N, K, stream)
+
+
+def tdm_gemm_f32_ex_path(A, B, layout=Layout.KN, C=None, path=Path.AUTO, stream=None):
+    torch = _torch()
+    M, N, K, C = _prep_layout(A, B, C, layout, (torch.float32,))
+    return _call_layout("tdm_gemm_f32_ex_path", A, B, layout, C, M, N, K, stream, path)
 
 
 def tdm_gemm_bf16_f32acc_path(A, B, C=None, path=Path.AUTO, stream=None):

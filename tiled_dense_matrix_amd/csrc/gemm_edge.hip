@@ -133,6 +133,15 @@ hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,
   return launch_edge<float, false, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
+hipError_t launch_edge_f32_layout(const float* A, const float* B, bool b_nk, bool a_km, float* C,
+                                  int M, int N, int K, hipStream_t s) {
+  if (a_km)
+    return b_nk ? launch_edge<float, false, true, true>(A, B, C, M, N, K, Epilogue{}, s)
+                : launch_edge<float, false, false, true>(A, B, C, M, N, K, Epilogue{}, s);
+  if (b_nk) return launch_edge<float, false, true>(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_edge<float, false, false>(A, B, C, M, N, K, Epilogue{}, s);
+}
+
 hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s) {
   return launch_edge<uint16_t, false, false>(A, B, C, M, N, K, Epilogue{}, s);

@@ -27,6 +27,14 @@
 // Each output is a sum over k in fp32; the order of the terms differs from a
 // plain k-ascending loop only by rounding.
 //
+// Transposed operands (CS336 Lecture 5 GPU notes, review question 5 and the
+// §4.1 warning: a transposed operand is another memory layout). A B stored
+// N x K has k-contiguous rows like A, so its tile is staged and read as A's
+// is (one 16-byte read per lane and group); an A stored K x M has rows of k
+// like B, so its tile is staged and read as B's is (four single floats).
+// Either way a tile holds the same BK x BM (or BK x BN) elements, so the
+// ring's size does not change.
+//
 // Partial tiles in M or N load clamped (in-bounds) rows/columns whose
 // products only reach outputs that are not stored. A K that is not a
 // multiple of 32 has its last step loaded through registers with the
@@ -48,17 +56,21 @@ constexpr int kGroupM = 4;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
-template <int BM_, int BN_, int WM_, int WN_, int STAGES_>
+// BNK_: B is stored N x K (C = A * B^T); AKM_: A is stored K x M (C = A^T * B).
+template <int BM_, int BN_, int WM_, int WN_, int STAGES_, bool BNK_ = false, bool AKM_ = false>
 struct Cfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = 32;
+  static constexpr bool kBNK = BNK_, kAKM = AKM_;
   static constexpr int kStages = STAGES_;
   static constexpr int kWaves = WM * WN, kThreads = 64 * kWaves;
-  static constexpr int kRowA = BK * 4;   // bytes per LDS row of A
-  static constexpr int kChunksA = BK / 4;
-  static constexpr int kRowB = BN * 4;   // bytes per LDS row of B
-  static constexpr int kChunksB = BN / 4;
-  static constexpr int kStageA = BM * kRowA;
-  static constexpr int kStageB = BK * kRowB;
+  // Bytes per LDS row: a k-contiguous row holds BK floats, a row of k holds
+  // the tile's BM (A) or BN (B) floats.
+  static constexpr int kRowA = kAKM ? BM * 4 : BK * 4;
+  static constexpr int kChunksA = kRowA / 16;
+  static constexpr int kRowB = kBNK ? BK * 4 : BN * 4;
+  static constexpr int kChunksB = kRowB / 16;
+  static constexpr int kStageA = BM * BK * 4;
+  static constexpr int kStageB = BN * BK * 4;
   static constexpr int kStage = kStageA + kStageB;
   static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kWaveM = BM / WM, kWaveN = BN / WN;
@@ -70,10 +82,11 @@ struct Cfg {
   static constexpr int kRowsPerCopyB = 1024 / kRowB;
   static constexpr int kGroups = BK / 8;                 // 8-k groups per step
   static constexpr int kMfmas = 4 * kFragM * kFragN;     // MFMAs per group
-  static constexpr int kReads = kFragM + 4 * kFragN;     // LDS reads per group
+  static constexpr int kReads = (kAKM ? 4 : 1) * kFragM + (kBNK ? 1 : 4) * kFragN;  // per group
   static_assert(kCopyA * kWaves * 1024 == kStageA && kCopyB * kWaves * 1024 == kStageB,
                 "each wave copies whole 1 KB blocks");
-  static_assert(kRowsPerCopyB >= 1 && BN % 64 == 0, "B rows of 256 or 512 bytes and more");
+  static_assert(kRowsPerCopyA >= 1 && kRowsPerCopyB >= 1 && BM % 64 == 0 && BN % 64 == 0,
+                "LDS rows of 1 KB or less that divide a 1 KB copy");
   static_assert(kStageA % (16 * kThreads) == 0 && kStageB % (16 * kThreads) == 0,
                 "masked copy: whole 16-byte chunks per lane");
   static_assert(kGroups % 2 == 0, "fragment double buffer alternates per group");
@@ -84,8 +97,28 @@ struct Cfg {
 __device__ __forceinline__ int swz_a(int m) { return (m >> 1) & 7; }
 __device__ __forceinline__ int swz_b(int k) { return ((k >> 2) & 1) << 3; }
 
-// Per-lane byte offsets of this wave's copies, relative to the tile's first
-// row of A (A + m0*K + k0) and to B + k0*N + n0.
+// Byte offset of a lane's 16-byte chunk in copy `copy` of one operand's
+// tile, relative to the tile's first element at k0. kKMajor: the operand is
+// stored K x ext (rows of k; the lane takes 4 columns, clamped to the last
+// whole group of 4 below ext); else it is stored ext x K (k-contiguous rows
+// of the tile's `rows` rows, clamped to ext - 1). o0: the tile's first
+// row/column; ld: the stored row length.
+template <bool kKMajor, int kRowsPerCopy, int kChunks>
+__device__ __forceinline__ uint32_t plan_off(int copy, int lane, int o0, int ext, int ld) {
+  const int row = copy * kRowsPerCopy + lane / kChunks;
+  if constexpr (kKMajor) {
+    const int c = (lane % kChunks) ^ swz_b(row);
+    const int d = min(o0 + c * 4, ext - 4) - o0;
+    return static_cast<uint32_t>((static_cast<int64_t>(row) * ld + d) * 4);
+  } else {
+    const int c = (lane % kChunks) ^ swz_a(row);
+    const int d = min(o0 + row, ext - 1) - o0;
+    return static_cast<uint32_t>((static_cast<int64_t>(d) * ld + c * 4) * 4);
+  }
+}
+
+// Per-lane byte offsets of this wave's copies, relative to each operand
+// tile's first element at k0 (tile_a / tile_b below).
 template <class T>
 struct CopyPlan {
   uint32_t a[T::kCopyA];
@@ -97,28 +130,32 @@ __device__ __forceinline__ CopyPlan<T> make_plan(int M, int N, int K, int m0, in
                                                  int lane) {
   CopyPlan<T> p;
 #pragma unroll
-  for (int j = 0; j < T::kCopyA; ++j) {
-    const int row = (wave * T::kCopyA + j) * T::kRowsPerCopyA + lane / T::kChunksA;
-    const int c = (lane % T::kChunksA) ^ swz_a(row);
-    const int dm = min(m0 + row, M - 1) - m0;
-    p.a[j] = static_cast<uint32_t>((static_cast<int64_t>(dm) * K + c * 4) * 4);
-  }
+  for (int j = 0; j < T::kCopyA; ++j)
+    p.a[j] = plan_off<T::kAKM, T::kRowsPerCopyA, T::kChunksA>(wave * T::kCopyA + j, lane, m0, M,
+                                                              T::kAKM ? M : K);
 #pragma unroll
-  for (int j = 0; j < T::kCopyB; ++j) {
-    const int row = (wave * T::kCopyB + j) * T::kRowsPerCopyB + lane / T::kChunksB;
-    const int c = (lane % T::kChunksB) ^ swz_b(row);
-    const int dn = min(n0 + c * 4, N - 4) - n0;
-    p.b[j] = static_cast<uint32_t>((static_cast<int64_t>(row) * N + dn) * 4);
-  }
+  for (int j = 0; j < T::kCopyB; ++j)
+    p.b[j] = plan_off<!T::kBNK, T::kRowsPerCopyB, T::kChunksB>(wave * T::kCopyB + j, lane, n0, N,
+                                                               T::kBNK ? K : N);
   return p;
 }
 
+// First element of each operand's tile at k0.
 template <class T>
-__device__ __forceinline__ void copy_step_dma(const float* a_tile, const float* b_tile, int N,
-                                              int k0, int wave, const CopyPlan<T>& p,
-                                              uint32_t stage) {
-  const float* a_base = a_tile + k0;
-  const float* b_base = b_tile + static_cast<int64_t>(k0) * N;
+__device__ __forceinline__ const float* tile_a(const float* A, int M, int K, int m0, int k0) {
+  return T::kAKM ? A + static_cast<int64_t>(k0) * M + m0 : A + static_cast<int64_t>(m0) * K + k0;
+}
+template <class T>
+__device__ __forceinline__ const float* tile_b(const float* B, int N, int K, int n0, int k0) {
+  return T::kBNK ? B + static_cast<int64_t>(n0) * K + k0 : B + static_cast<int64_t>(k0) * N + n0;
+}
+
+template <class T>
+__device__ __forceinline__ void copy_step_dma(const float* A, const float* B, int M, int N, int K,
+                                              int m0, int n0, int k0, int wave,
+                                              const CopyPlan<T>& p, uint32_t stage) {
+  const float* a_base = tile_a<T>(A, M, K, m0, k0);
+  const float* b_base = tile_b<T>(B, N, K, n0, k0);
 #pragma unroll
   for (int j = 0; j < T::kCopyA; ++j)
     dma16(a_base, p.a[j], stage + (wave * T::kCopyA + j) * 1024);
@@ -127,54 +164,71 @@ __device__ __forceinline__ void copy_step_dma(const float* a_tile, const float* 
     dma16(b_base, p.b[j], stage + T::kStageA + (wave * T::kCopyB + j) * 1024);
 }
 
-// Same layout, through registers, with zeros beyond K (the partial last step).
+// One operand's tile through registers, with zeros beyond K (the partial
+// last step), in the layout the copies give it (plan_off).
+template <bool kKMajor, int kStage, int kRow, int kChunks, int kThreads>
+__device__ __forceinline__ void masked_tile(const float* __restrict__ X, int o0, int ext, int K,
+                                            int k0, int tid, LDS_PTR(uint8_t) dst) {
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < kStage / 16 / kThreads; ++i) {
+    const int id = tid + kThreads * i;
+    const int row = id / kChunks, c = id % kChunks;
+    f32x4 v = zero;
+    if constexpr (kKMajor) {  // row = k, 4 columns
+      const int gk = k0 + row, g = min(o0 + c * 4, ext - 4);
+      if (gk < K) v = *reinterpret_cast<const f32x4*>(X + static_cast<int64_t>(gk) * ext + g);
+      *(LDS_PTR(f32x4))(dst + row * kRow + ((c ^ swz_b(row)) << 4)) = v;
+    } else {  // row of the operand, 4 k
+      const int gk = k0 + c * 4, g = min(o0 + row, ext - 1);
+      if (gk < K) v = *reinterpret_cast<const f32x4*>(X + static_cast<int64_t>(g) * K + gk);
+      *(LDS_PTR(f32x4))(dst + row * kRow + ((c ^ swz_a(row)) << 4)) = v;
+    }
+  }
+}
+
 template <class T>
 __device__ __forceinline__ void copy_step_masked(const float* __restrict__ A,
                                                  const float* __restrict__ B, int M, int N, int K,
                                                  int m0, int n0, int k0, int tid,
                                                  LDS_PTR(uint8_t) stage) {
-  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < T::kStageA / 16 / T::kThreads; ++i) {
-    const int id = tid + T::kThreads * i;
-    const int row = id / T::kChunksA, c = id % T::kChunksA;
-    const int gk = k0 + c * 4;
-    const int gm = min(m0 + row, M - 1);
-    f32x4 v = zero;
-    if (gk < K) v = *reinterpret_cast<const f32x4*>(A + static_cast<int64_t>(gm) * K + gk);
-    *(LDS_PTR(f32x4))(stage + row * T::kRowA + ((c ^ swz_a(row)) << 4)) = v;
-  }
-  LDS_PTR(uint8_t) sb = stage + T::kStageA;
-#pragma unroll
-  for (int i = 0; i < T::kStageB / 16 / T::kThreads; ++i) {
-    const int id = tid + T::kThreads * i;
-    const int row = id / T::kChunksB, c = id % T::kChunksB;
-    const int gk = k0 + row;
-    const int gn = min(n0 + c * 4, N - 4);
-    f32x4 v = zero;
-    if (gk < K) v = *reinterpret_cast<const f32x4*>(B + static_cast<int64_t>(gk) * N + gn);
-    *(LDS_PTR(f32x4))(sb + row * T::kRowB + ((c ^ swz_b(row)) << 4)) = v;
-  }
+  masked_tile<T::kAKM, T::kStageA, T::kRowA, T::kChunksA, T::kThreads>(A, m0, M, K, k0, tid, stage);
+  masked_tile<!T::kBNK, T::kStageB, T::kRowB, T::kChunksB, T::kThreads>(B, n0, N, K, k0, tid,
+                                                                      stage + T::kStageA);
 }
 
-// k = 8q + 4*(lane/32) + 0..3 of row `row` of A.
+// k = 8q + 4*(lane/32) + 0..3 of row `row` of a k-contiguous tile: one
+// 16-byte read.
+template <int kRow>
+__device__ __forceinline__ f32x4 read_rows(LDS_PTR(const uint8_t) s, int row, int q, int lg) {
+  const int chunk = 2 * q + lg;
+  return *(LDS_PTR(const f32x4))(s + row * kRow + ((chunk ^ swz_a(row)) << 4));
+}
+
+// Rows k = 8q + 4*(lane/32) + 0..3 of column `col` of a tile of k rows:
+// four single floats.
+template <int kRow>
+__device__ __forceinline__ f32x4 read_cols(LDS_PTR(const uint8_t) s, int col, int q, int lg) {
+  const int k = 8 * q + 4 * lg;
+  LDS_PTR(const uint8_t) p = s + (((col >> 2) ^ swz_b(k)) << 4) + ((col & 3) << 2);
+  f32x4 v;
+  v.x = *(LDS_PTR(const float))(p + (k + 0) * kRow);
+  v.y = *(LDS_PTR(const float))(p + (k + 1) * kRow);
+  v.z = *(LDS_PTR(const float))(p + (k + 2) * kRow);
+  v.w = *(LDS_PTR(const float))(p + (k + 3) * kRow);
+  return v;
+}
+
+// The lane's four k of row `row` of op(A) / column `col` of op(B).
 template <class T>
 __device__ __forceinline__ f32x4 read_a(LDS_PTR(const uint8_t) sa, int row, int q, int lg) {
-  const int chunk = 2 * q + lg;
-  return *(LDS_PTR(const f32x4))(sa + row * T::kRowA + ((chunk ^ swz_a(row)) << 4));
+  if constexpr (T::kAKM) return read_cols<T::kRowA>(sa, row, q, lg);
+  return read_rows<T::kRowA>(sa, row, q, lg);
 }
-
-// Rows k = 8q + 4*(lane/32) + 0..3 of column `col` of B.
 template <class T>
 __device__ __forceinline__ f32x4 read_b(LDS_PTR(const uint8_t) sb, int col, int q, int lg) {
-  const int k = 8 * q + 4 * lg;
-  LDS_PTR(const uint8_t) p = sb + (((col >> 2) ^ swz_b(k)) << 4) + ((col & 3) << 2);
-  f32x4 v;
-  v.x = *(LDS_PTR(const float))(p + (k + 0) * T::kRowB);
-  v.y = *(LDS_PTR(const float))(p + (k + 1) * T::kRowB);
-  v.z = *(LDS_PTR(const float))(p + (k + 2) * T::kRowB);
-  v.w = *(LDS_PTR(const float))(p + (k + 3) * T::kRowB);
-  return v;
+  if constexpr (T::kBNK) return read_rows<T::kRowB>(sb, col, q, lg);
+  return read_cols<T::kRowB>(sb, col, q, lg);
 }
 
 // One read of the next group's operands after each MFMA, leftovers after.
@@ -221,13 +275,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_f32_kernel(
   const int steps = (K + T::BK - 1) / T::BK;
   const int full_steps = K / T::BK;
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
-  const float* a_tile = A + static_cast<int64_t>(m0) * K;
-  const float* b_tile = B + n0;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane(lds_offset(lds));
 
   auto issue = [&](int st, int slot) {
     if (st < full_steps)
-      copy_step_dma<T>(a_tile, b_tile, N, st * T::BK, wave, plan, lds0 + slot * T::kStage);
+      copy_step_dma<T>(A, B, M, N, K, m0, n0, st * T::BK, wave, plan, lds0 + slot * T::kStage);
     else if (st < steps)
       copy_step_masked<T>(A, B, M, N, K, m0, n0, st * T::BK, tid, lds + slot * T::kStage);
   };
@@ -319,24 +371,46 @@ hipError_t launch_tile(const float* A, const float* B, float* C, int M, int N, i
                 A, B, C, M, N, K, tiles_m, tiles_n);
 }
 
-using LargeTile = Cfg<256, 256, 2, 4, 2>;
-using SmallTile = Cfg<128, 128, 2, 4, 4>;
+template <bool BNK, bool AKM>
+using LargeTile = Cfg<256, 256, 2, 4, 2, BNK, AKM>;
+template <bool BNK, bool AKM>
+using SmallTile = Cfg<128, 128, 2, 4, 4, BNK, AKM>;
+
+template <bool BNK, bool AKM>
+hipError_t launch_layout(const float* A, const float* B, float* C, int M, int N, int K,
+                         hipStream_t s) {
+  if (use_large_tiles(M, N, kLargeTileFillF32))
+    return launch_tile<LargeTile<BNK, AKM>>(A, B, C, M, N, K, s);
+  return launch_tile<SmallTile<BNK, AKM>>(A, B, C, M, N, K, s);
+}
 
 }  // namespace
 
-bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b, int mis_c) {
-  (void)M;
+bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b, int mis_c,
+                       bool b_nk, bool a_km) {
   (void)mis_c;
-  // 32-bit per-lane copy offsets: 256 rows of A and 32 rows of B stay below
-  // 4 GiB from the tile's first element.
-  return K % 4 == 0 && N % 4 == 0 && K >= 4 && K < (1 << 22) && N < (1 << 25) && mis_a == 0 &&
-         mis_b == 0;
+  // 16-byte chunks along K of k-contiguous rows, along N or M of rows of k;
+  // 32-bit per-lane copy offsets: 256 k-contiguous rows (K floats each) or
+  // 32 rows of k (N or M floats each) stay below 4 GiB from a tile's first
+  // element.
+  if (K % 4 != 0 || K < 4 || K >= (1 << 22) || mis_a != 0 || mis_b != 0) return false;
+  if (!b_nk && (N % 4 != 0 || N >= (1 << 25))) return false;
+  if (a_km && (M % 4 != 0 || M >= (1 << 25))) return false;
+  return true;
 }
 
 hipError_t launch_mfma_f32(const float* A, const float* B, float* C, int M, int N, int K,
                            hipStream_t s) {
-  if (use_large_tiles(M, N, kLargeTileFillF32)) return launch_tile<LargeTile>(A, B, C, M, N, K, s);
-  return launch_tile<SmallTile>(A, B, C, M, N, K, s);
+  return launch_layout<false, false>(A, B, C, M, N, K, s);
+}
+
+hipError_t launch_mfma_f32_layout(const float* A, const float* B, bool b_nk, bool a_km, float* C,
+                                  int M, int N, int K, hipStream_t s) {
+  if (a_km)
+    return b_nk ? launch_layout<true, true>(A, B, C, M, N, K, s)
+                : launch_layout<false, true>(A, B, C, M, N, K, s);
+  return b_nk ? launch_layout<true, false>(A, B, C, M, N, K, s)
+              : launch_layout<false, false>(A, B, C, M, N, K, s);
 }
 
 }  // namespace tdm

@@ -58,13 +58,12 @@ tdm_status check_device() {
 }
 
 // Shape/alignment admission of each path for one kind; b_nk: B is stored
-// N x K, a_km: A is stored K x M (bf16 only).
+// N x K, a_km: A is stored K x M (the vector-ALU kernel takes neither).
 bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
               int ma, int mb, int mc, bool b_nk = false, bool a_km = false) {
   const bool kind_ok =
-      (path != TDM_PATH_VALU || kind == TDM_KIND_F32) &&
-      (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC) &&
-      (!(b_nk || a_km) || kind == TDM_KIND_BF16_F32ACC);
+      (path != TDM_PATH_VALU || (kind == TDM_KIND_F32 && !b_nk && !a_km)) &&
+      (path != TDM_PATH_SKINNY || kind == TDM_KIND_BF16_F32ACC);
   if (!kind_ok) return false;
   if (M == 0 || N == 0 || K == 0) return true;  // nothing to run, or a zero fill
   switch (path) {
@@ -74,7 +73,7 @@ bool supports(tdm_kind kind, tdm_path path, int64_t M, int64_t N, int64_t K,
     case TDM_PATH_VALU:
       return kind == TDM_KIND_F32 && tdm::valu_f32_supports(M, N, K, ma, mb, mc);
     case TDM_PATH_MFMA:
-      if (kind == TDM_KIND_F32) return tdm::mfma_f32_supports(M, N, K, ma, mb, mc);
+      if (kind == TDM_KIND_F32) return tdm::mfma_f32_supports(M, N, K, ma, mb, mc, b_nk, a_km);
       if (a_km) return tdm::mfma_bf16_akm_supports(M, N, K, b_nk, ma, mb, mc);
       return b_nk ? tdm::mfma_bf16_nk_supports(M, N, K, ma, mb, mc)
                   : tdm::mfma_bf16_supports(M, N, K, ma, mb, mc);
@@ -111,8 +110,8 @@ tdm_path choose(tdm_kind kind, int64_t M, int64_t N, int64_t K, int ma, int mb, 
   // at every measured size; the VALU kernel takes what they cannot.
   const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
   if (tiles128 < 16) return TDM_PATH_EDGE;
-  if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc)) return TDM_PATH_MFMA;
-  if (supports(kind, TDM_PATH_VALU, M, N, K, ma, mb, mc)) return TDM_PATH_VALU;
+  if (supports(kind, TDM_PATH_MFMA, M, N, K, ma, mb, mc, b_nk, a_km)) return TDM_PATH_MFMA;
+  if (supports(kind, TDM_PATH_VALU, M, N, K, ma, mb, mc, b_nk, a_km)) return TDM_PATH_VALU;
   return TDM_PATH_EDGE;
 }
 
@@ -138,22 +137,27 @@ tdm_status validate(const T* A, const T* B, const float* C, int64_t M, int64_t N
   return TDM_SUCCESS;
 }
 
-tdm_status run_f32(const float* A, const float* B, float* C, int64_t M, int64_t N,
+// layout: how A and B are stored (tdm_layout, checked by the caller).
+tdm_status run_f32(const float* A, const float* B, int layout, float* C, int64_t M, int64_t N,
                    int64_t K, tdm_path path, void* stream) {
   tdm_status st = validate(A, B, C, M, N, K);
   if (st != TDM_SUCCESS || M == 0 || N == 0) return st;
+  const bool b_nk = (layout & TDM_LAYOUT_NK) != 0, a_km = (layout & TDM_LAYOUT_KM_KN) != 0;
   const int ma = misalign(A), mb = misalign(B), mc = misalign(C);
-  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_F32, path, M, N, K, ma, mb, mc))
+  if (path != TDM_PATH_AUTO && !supports(TDM_KIND_F32, path, M, N, K, ma, mb, mc, b_nk, a_km))
     return TDM_ERROR_NOT_SUPPORTED;
   if ((st = check_device()) != TDM_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) return to_status(tdm::launch_fill_zero_f32(C, M * N, s));  // empty sum
-  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_F32, M, N, K, ma, mb, mc);
+  if (path == TDM_PATH_AUTO) path = choose(TDM_KIND_F32, M, N, K, ma, mb, mc, b_nk, a_km);
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
   switch (path) {
     case TDM_PATH_VALU: return to_status(tdm::launch_valu_f32(A, B, C, m, n, k, s));
-    case TDM_PATH_MFMA: return to_status(tdm::launch_mfma_f32(A, B, C, m, n, k, s));
-    default: return to_status(tdm::launch_edge_f32(A, B, C, m, n, k, s));
+    case TDM_PATH_MFMA:
+      return to_status(tdm::launch_mfma_f32_layout(A, B, b_nk, a_km, C, m, n, k, s));
+    default:
+      if (!b_nk && !a_km) return to_status(tdm::launch_edge_f32(A, B, C, m, n, k, s));
+      return to_status(tdm::launch_edge_f32_layout(A, B, b_nk, a_km, C, m, n, k, s));
   }
 }
 
@@ -338,7 +342,7 @@ int tdm_fp8_supports(int64_t M, int64_t N, int64_t K, int misalign_a, int misali
 
 tdm_status gemm_f32(const float* A, const float* B, float* C, int64_t M, int64_t N,
                     int64_t K, void* stream) {
-  return run_f32(A, B, C, M, N, K, TDM_PATH_AUTO, stream);
+  return run_f32(A, B, TDM_LAYOUT_KN, C, M, N, K, TDM_PATH_AUTO, stream);
 }
 
 tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C, int64_t M,
@@ -349,7 +353,19 @@ tdm_status gemm_bf16_f32acc(const uint16_t* A, const uint16_t* B, float* C, int6
 tdm_status tdm_gemm_f32_path(const float* A, const float* B, float* C, int64_t M,
                              int64_t N, int64_t K, tdm_path path, void* stream) {
   if (!valid_path(raw(path))) return TDM_ERROR_INVALID_VALUE;
-  return run_f32(A, B, C, M, N, K, path, stream);
+  return run_f32(A, B, TDM_LAYOUT_KN, C, M, N, K, path, stream);
+}
+
+tdm_status gemm_f32_ex(const float* A, const float* B, tdm_layout layout, float* C, int64_t M,
+                       int64_t N, int64_t K, void* stream) {
+  if (!valid_layout(raw(layout))) return TDM_ERROR_INVALID_VALUE;
+  return run_f32(A, B, raw(layout), C, M, N, K, TDM_PATH_AUTO, stream);
+}
+
+tdm_status tdm_gemm_f32_ex_path(const float* A, const float* B, tdm_layout layout, float* C,
+                                int64_t M, int64_t N, int64_t K, tdm_path path, void* stream) {
+  if (!valid_path(raw(path)) || !valid_layout(raw(layout))) return TDM_ERROR_INVALID_VALUE;
+  return run_f32(A, B, raw(layout), C, M, N, K, path, stream);
 }
 
 tdm_status tdm_gemm_bf16_f32acc_path(const uint16_t* A, const uint16_t* B, float* C,
@@ -451,7 +467,6 @@ int tdm_path_supports_ex(tdm_kind kind, tdm_layout layout, tdm_path path, int64_
 tdm_path tdm_select_path_ex(tdm_kind kind, tdm_layout layout, int64_t M, int64_t N,
                             int64_t K) {
   if (!valid_kind(raw(kind)) || !valid_layout(raw(layout))) return TDM_PATH_EDGE;
-  if (layout != TDM_LAYOUT_KN && kind != TDM_KIND_BF16_F32ACC) return TDM_PATH_EDGE;
   return choose(kind, M, N, K, 0, 0, 0, (layout & TDM_LAYOUT_NK) != 0,
                 (layout & TDM_LAYOUT_KM_KN) != 0);
 }

@@ -73,9 +73,10 @@ inline bool edge_supports(int64_t, int64_t, int64_t) { return true; }
 bool valu_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
                        int mis_c);
 
-// fp32 MFMA kernel: 16-byte chunks along K and N.
+// fp32 MFMA kernel: 16-byte chunks along K, and along N (B stored K x N) or
+// M (A stored K x M).
 bool mfma_f32_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
-                       int mis_c);
+                       int mis_c, bool b_nk = false, bool a_km = false);
 
 // bf16 MFMA kernel: 16-byte chunks (8 elements) along K and N.
 bool mfma_bf16_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b,
@@ -112,6 +113,9 @@ hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s);
 
 hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s);
+// b_nk: B is stored N x K; a_km: A is stored K x M.
+hipError_t launch_edge_f32_layout(const float* A, const float* B, bool b_nk, bool a_km, float* C,
+                                  int M, int N, int K, hipStream_t s);
 hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s);
 
@@ -120,6 +124,8 @@ hipError_t launch_valu_f32(const float* A, const float* B, float* C, int M,
 
 hipError_t launch_mfma_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s);
+hipError_t launch_mfma_f32_layout(const float* A, const float* B, bool b_nk, bool a_km, float* C,
+                                  int M, int N, int K, hipStream_t s);
 
 hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
                             int M, int N, int K, hipStream_t s);

@@ -104,6 +104,10 @@ WORKLOADS = {
     for w in (
         Workload("f32_256", "f32", 256, 256, 256, 0, "uniform"),
         Workload("f32_4096", "f32", 4096, 4096, 4096, 1, "uniform"),
+        # The fp32 4096^3 product with a transposed operand: B stored N x K,
+        # and A stored K x M.
+        Workload("f32_4096_nk", "f32", 4096, 4096, 4096, 11, "uniform", b_layout="nk"),
+        Workload("f32_4096_tn", "f32", 4096, 4096, 4096, 12, "uniform", a_layout="km"),
         Workload("bf16_4096", "bf16", 4096, 4096, 4096, 2, "normal"),
         Workload("bf16_8192", "bf16", 8192, 8192, 8192, 2, "normal"),
         Workload("bf16_mlp", "bf16", 8192, 14336, 4096, 3, "normal", 1.0, 0.02),
@@ -170,8 +174,8 @@ def make_inputs(w: Workload | str):
     if w.kind == "f32":
         if w.dist != "uniform":
             raise ValueError(w.dist)
-        A = uniform_fp32(rng, (w.M, w.K))
-        B = uniform_fp32(rng, (w.K, w.N))
+        A = uniform_fp32(rng, (w.K, w.M) if w.a_layout == "km" else (w.M, w.K))
+        B = uniform_fp32(rng, (w.N, w.K) if w.b_layout == "nk" else (w.K, w.N))
     elif w.kind == "bf16":
         if w.dist != "normal":
             raise ValueError(w.dist)
