@@ -73,3 +73,48 @@ def test_special_values_land_where_the_definition_puts_them(kind, shape, path):
     mb = float(np.abs(Bw[np.isfinite(Bw)]).max())
     err = float(np.abs(C[fin] - R[fin]).max()) / (ma * mb * K)
     assert err <= (TOL_F32 if kind == "f32" else TOL_BF16), (path.name, err)
+
+
+L = tdm.Layout
+LAYOUT_SHAPES = [("f32", (132, 200, 136)), ("f32", (300, 520, 96)), ("bf16", (136, 200, 136)),
+                 ("bf16", (304, 520, 96)), ("bf16", (16, 512, 1024))]
+
+
+def _layout_cases():
+    for kind, shape in LAYOUT_SHAPES:
+        for layout in (L.NK, L.KM_KN, L.KM_NK):
+            for p in (P.AUTO, P.EDGE, P.MFMA, P.SKINNY):
+                if tdm.tdm_path_supports_ex(KIND[kind], layout, p, *shape):
+                    yield pytest.param(kind, shape, layout, p,
+                                       id=f"{kind}-{layout.name}-{shape[0]}x{shape[1]}x{shape[2]}"
+                                          f"-{p.name}")
+
+
+@pytest.mark.parametrize("kind,shape,layout,path", list(_layout_cases()))
+def test_special_values_with_a_transposed_operand(kind, shape, layout, path):
+    """The same planted values in op(A) and op(B), stored transposed as the
+    layout says (A K x M, B N x K): they must land where the definition
+    applied to op(A) and op(B) puts them."""
+    M, N, K = shape
+    log(f"case special values {kind} {layout.name} {shape} path={path.name}")
+    A, B = planted_inputs(kind, M, N, K, seed=M + 2 * N + K)
+    As = np.ascontiguousarray(A.T) if layout & L.KM_KN else A
+    Bs = np.ascontiguousarray(B.T) if layout & L.NK else B
+    if kind == "f32":
+        C = tdm.tdm_gemm_f32_ex_path(to_device(As), to_device(Bs), layout, path=path)
+    else:
+        C = tdm.tdm_gemm_bf16_ex_path(to_device(As), to_device(Bs), layout,
+                                      out_dtype=torch.float32, path=path)
+    torch.cuda.synchronize()
+    C = C.cpu().numpy().astype(np.float64)
+    R = oracle.gemm(A, B)
+    assert np.isnan(R).any() and np.isinf(R).any()
+    assert np.array_equal(np.isnan(C), np.isnan(R)), path.name
+    assert np.array_equal(np.isposinf(C), np.isposinf(R)), path.name
+    assert np.array_equal(np.isneginf(C), np.isneginf(R)), path.name
+    fin = np.isfinite(R)
+    Aw, Bw = oracle.widen(A), oracle.widen(B)
+    ma = float(np.abs(Aw[np.isfinite(Aw)]).max())
+    mb = float(np.abs(Bw[np.isfinite(Bw)]).max())
+    err = float(np.abs(C[fin] - R[fin]).max()) / (ma * mb * K)
+    assert err <= (TOL_F32 if kind == "f32" else TOL_BF16), (path.name, err)
