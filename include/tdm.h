@@ -221,8 +221,10 @@ TDM_API tdm_status gemm_bf16_ex_noalloc(const uint16_t* A, const uint16_t* B,
                                         int64_t M, int64_t N, int64_t K, void* stream);
 
 /* Host-only: tdm_path_supports / tdm_select_path for given layouts of A and
- * B (layouts other than TDM_LAYOUT_KN: bf16 only; 0 / TDM_PATH_EDGE for an
- * unknown layout). */
+ * B (0 / TDM_PATH_EDGE for an unknown layout or kind). Layouts other than
+ * TDM_LAYOUT_KN: bf16 on every path but the small-M one for an A stored
+ * K x M; fp32 on the matrix cores and the edge kernel, never the vector
+ * ALU. */
 TDM_API int tdm_path_supports_ex(tdm_kind kind, tdm_layout layout, tdm_path path, int64_t M,
                                  int64_t N, int64_t K, int misalign_a, int misalign_b,
                                  int misalign_c);
