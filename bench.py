@@ -709,11 +709,19 @@ def cpu_baseline_fp8(w, A, B, sa, sb, C_gpu, target_s: float):
     import oracle
     fa, fb = w.fp8
     threads = oracle.default_threads()
-    rows = min(w.M, threads)
-    t0 = time.perf_counter()
-    oracle.gemm_fp8(A[:rows], fa, B, fb, None if sa is None else sa[:rows], sb, threads)
-    per_row = max(time.perf_counter() - t0, 1e-6) / rows
-    rows = int(max(1, min(w.M, math.floor(target_s / per_row))))
+
+    def timed_rows(r):
+        t0 = time.perf_counter()
+        oracle.gemm_fp8(A[:r], fa, B, fb, None if sa is None else sa[:r], sb, threads)
+        return time.perf_counter() - t0
+
+    # Each call also decodes all of B, a fixed cost: calibrate on two sample
+    # sizes and size the sample from the cost per added row.
+    r1, r2 = min(w.M, threads), min(w.M, 4 * threads)
+    t1, t2 = timed_rows(r1), timed_rows(r2)
+    per_row = max((t2 - t1) / max(r2 - r1, 1), 1e-6)
+    fixed = max(t1 - r1 * per_row, 0.0)
+    rows = int(max(1, min(w.M, math.floor((target_s - fixed) / per_row))))
     if rows >= threads:
         rows -= rows % threads
     t0 = time.perf_counter()
@@ -837,27 +845,35 @@ def main_fp8(args, w):
 
 
 def cpu_baseline_attention(w, Q, K, V, O_gpu, target_s: float):
-    """Time the attention oracle on the first query rows of head 0; also
-    check them against the GPU output."""
+    """Time the attention oracle on whole heads (batch-major order) for about
+    target_s; also check them against the GPU output."""
     import oracle
-    rows = 16
+    heads_total = w.batch * w.heads
+    r = np.arange(w.seq)
     t0 = time.perf_counter()
-    oracle.attention_rows(Q[0, 0], K[0, 0], V[0, 0], np.arange(rows), w.scale, w.causal)
-    per_row = max(time.perf_counter() - t0, 1e-6) / rows
-    rows = int(max(1, min(w.seq, math.floor(target_s / per_row))))
-    r = np.arange(rows)
+    oracle.attention_rows(Q[0, 0], K[0, 0], V[0, 0], r, w.scale, w.causal)
+    per_head = max(time.perf_counter() - t0, 1e-6)
+    heads = int(max(1, min(heads_total, math.floor(target_s / per_head))))
     t0 = time.perf_counter()
-    R, _ = oracle.attention_rows(Q[0, 0], K[0, 0], V[0, 0], r, w.scale, w.causal)
+    outs = []
+    for i in range(heads):
+        b, h = divmod(i, w.heads)
+        outs.append(oracle.attention_rows(Q[b, h], K[b, h], V[b, h], r, w.scale, w.causal)[0])
     dt = time.perf_counter() - t0
-    visible = (r + 1).sum() if w.causal else rows * w.seq
-    flops = 4.0 * w.head_dim * visible
-    got = oracle.widen(O_gpu[0, 0][:rows])
-    rel = float(np.linalg.norm(got - R) / max(np.linalg.norm(R), 1e-300))
+    visible = (r + 1).sum() if w.causal else w.seq * w.seq
+    flops = 4.0 * w.head_dim * visible * heads
+    num = den = 0.0
+    for i, R in enumerate(outs):
+        b, h = divmod(i, w.heads)
+        got = oracle.widen(O_gpu[b, h])
+        num += float(np.linalg.norm(got - R) ** 2)
+        den += float(np.linalg.norm(R) ** 2)
+    rel = (num / max(den, 1e-300)) ** 0.5
     return {
         "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.default_threads(),
         "kind": "oracle",
-        "sample": f"query rows 0..{rows - 1} of head 0 ({flops / 1e9:.2f} GFLOP) in {dt:.1f} s: "
-                  "fp64 scores, softmax and P V with NumPy",
+        "sample": f"{heads} of {heads_total} heads, all {w.seq} query rows ({flops / 1e9:.1f} "
+                  f"GFLOP) in {dt:.1f} s: fp64 scores, softmax and P V with NumPy",
         "sample_parity": {"rel_fro": float(f"{rel:.3e}")},
     }
 
