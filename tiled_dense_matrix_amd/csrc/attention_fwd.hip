@@ -14,7 +14,9 @@
 //   2. online softmax per query, in base 2 (scores times scale * log2 e):
 //      block maximum over the lane's 32 values and its partner lane l^32,
 //      m_new = max(m, block max), alpha = 2^(m - m_new), p = 2^(s - m_new),
-//      l = l * alpha + sum p, O *= alpha;
+//      l = l * alpha + sum p, O *= alpha (blocks without masked keys take
+//      the maximum of the raw scores and fold the scale into p's exponent,
+//      one FMA per score);
 //   3. O^T += V^T P^T: the p values, rounded to bf16, already sit where the
 //      MFMA's B operand wants them, for the key order of step 1 (within a
 //      16-key window lane l holds keys 4*(l/32) + 0..3 and 8 + 4*(l/32) +
@@ -44,6 +46,8 @@
 // diagonal are skipped, and the query blocks run heaviest first (work_item).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "lds_copy.h"
 #include "tdm_internal.h"
@@ -158,6 +162,12 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
 #pragma unroll
     for (int ks = 0; ks < T::kKSteps; ++ks)
       qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * lg));
+    // Take delivery of Q here. Left to itself the compiler waits for these
+    // loads at their first use inside the key loop, on every iteration, and
+    // since memory operations complete in issue order that wait also holds
+    // each block until the next block's K and V copies have landed.
+#pragma unroll
+    for (int ks = 0; ks < T::kKSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
   }
 
   // Keys this workgroup visits: all, or (causal) up to its last query.
@@ -181,6 +191,15 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     if (t >= blocks) return;
     const int kb0 = t * kBKV;
     const uint32_t stage = lds0 + slot * T::kStage;
+    if (kb0 + kBKV <= n_kv) {  // every row in range
+#pragma unroll
+      for (int j = 0; j < T::kCopies; ++j) {
+        dma16(Kh + static_cast<int64_t>(kb0) * D, off_k[j], stage + (wave + kWaves * j) * 1024);
+        dma16(Vh + static_cast<int64_t>(kb0) * D, off_v[j],
+              stage + T::kBlock + (wave + kWaves * j) * 1024);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < T::kCopies; ++j) {
       const int r = (wave + kWaves * j) * T::kRowsPerCopy + crow;
@@ -220,8 +239,11 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
   float m_run = -INFINITY, l_run = 0.f;
 
   issue(0, 0);
-  for (int t = 0; t < blocks; ++t) {
-    const int cur = t & 1;
+  // One key block; the ring slot is a compile-time constant, so the LDS
+  // reads take it in their immediate offsets (the loop runs two blocks per
+  // iteration).
+  auto step = [&](const int t, auto slot) __attribute__((always_inline)) {
+    constexpr int cur = decltype(slot)::value;
     wait_vm<0>();
     __syncthreads();  // block t landed; every wave is done with block t-1's slot
     issue(t + 1, cur ^ 1);
@@ -261,48 +283,83 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     }
 
     __builtin_amdgcn_s_setprio(0);
-    // 2. Online softmax (base 2). Masked scores are -inf; the mask is one
-    // uniform branch (the last key block, and blocks on the causal diagonal).
+    // 2. Online softmax (base 2). Blocks with masked keys (the last key
+    // block, blocks on the causal diagonal) and a negative scale take the
+    // general form; the others a shorter one (below). Both tests are uniform
+    // over the wave.
+    const bool general =
+        !(scale_log2 >= 0.f) || kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
+    constexpr float kSlack = 8.0f;
+    float psum = 0.f, alpha = 1.f, m_new = m_run;
+    bf16x8 pop[4];  // p in bf16 (v_cvt_pk_bf16_f32: nearest even), window w16 = keys 16*w16 ..
+    // p = 2^(x - m) for the block's scores, their sum over this lane, and the
+    // bf16 operands of step 3.
+    auto exps = [&](float m_use, bool raw) __attribute__((always_inline)) {
+      psum = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int w16 = 0; w16 < 4; ++w16)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[h][v] *= scale_log2;
-    if (kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave)) {
-      const int lim = causal ? min(n_kv - 1, query) : n_kv - 1;  // last visible key
+        for (int e = 0; e < 8; ++e) {
+          const float x = s[w16 >> 1][8 * (w16 & 1) + e];
+          const float p = __builtin_amdgcn_exp2f(raw ? __builtin_fmaf(x, scale_log2, -m_use) : x - m_use);
+          psum += p;
+          pop[w16][e] = static_cast<__bf16>(p);
+        }
+    };
+    // The reference maximum m moves only when the block's maximum exceeds it
+    // by more than 8 (in log2 units): until then p = 2^(x - m) stays at or
+    // below 256, which fp32 sums and bf16 operands carry without loss, and O
+    // and l remain scaled by the same m, so the result is the exact softmax.
+    auto rebase = [&](float bmax, bool raw) __attribute__((always_inline)) {
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      m_new = bmax > m_run + kSlack ? bmax : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far
+      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      exps(m_use, raw);
+    };
+    if (general) {
+      // Scale every score, set masked ones to -inf, take the maximum.
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
-          s[h][v] = key > lim ? -INFINITY : s[h][v];
-        }
-    }
-    float bmax = -INFINITY;
+        for (int v = 0; v < 16; ++v) s[h][v] *= scale_log2;
+      if (kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave)) {
+        const int lim = causal ? min(n_kv - 1, query) : n_kv - 1;  // last visible key
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    // The reference maximum moves only when the block's maximum exceeds it
-    // by more than 8 (in log2 units): until then p = 2^(x - m) stays below
-    // 256, which fp32 sums and bf16 operands carry without loss, and O and l
-    // remain scaled by the same m, so the result is unchanged. O is then
-    // rescaled in few blocks instead of most (with 32 queries per wave, one
-    // of them raises its exact maximum in most blocks).
-    constexpr float kSlack = 8.0f;
-    const float m_new = bmax > m_run + kSlack ? bmax : m_run;
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(s[h][v] - m_use);
-        s[h][v] = p;
-        psum += p;
+          for (int v = 0; v < 16; ++v) {
+            const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
+            s[h][v] = key > lim ? -INFINITY : s[h][v];
+          }
       }
-    psum += __shfl_xor(psum, 32);
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
+      rebase(bmax, false);
+    } else {
+      // No masked key and a scale >= 0: first try the current m, with the
+      // scale folded into the exponent's argument (one FMA per score). Every
+      // p is at most the lane's sum, so a sum of at most 256 on every lane
+      // shows that no score exceeds m by more than 8 and m stays. Otherwise
+      // (the first block, where m = -inf makes every p infinite, and blocks
+      // whose scores reach past m + 8 or crowd near it) take the maximum of
+      // the raw scores, scale only that (exact: rounding is monotonic) and
+      // redo the block.
+      exps(m_run, true);
+      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
+        float bmax = -INFINITY;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
+        rebase(bmax * scale_log2, true);
+      }
+    }
+    // l is kept per lane (this lane's keys of the row) and the two halves of
+    // a row are added at the end; alpha is the row's, so both scale alike.
     l_run = l_run * alpha + psum;
     m_run = m_new;
     // Rescale O only when some query of the wave raised its maximum (after
@@ -318,11 +375,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int w16 = 0; w16 < 4; ++w16) {
-      const int h = w16 >> 1, e0 = 8 * (w16 & 1);
-      // fp32 -> bf16 (v_cvt_pk_bf16_f32: nearest even, two per instruction).
-      bf16x8 pop;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pop[e] = static_cast<__bf16>(s[h][e0 + e]);
+
       // Transposing reads: in each 16-lane group G, lane i points at key row
       // base + i/4 and d columns 4*(i%4)..+3 of its 16-column half; lane j
       // gets 4 consecutive keys of column j (rows of the window, then 8
@@ -334,15 +387,20 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
         const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 8 * T::kRow));
         const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
         const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop,
+        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop[w16],
                                                             acc_o[db], 0, 0, 0);
       }
     }
+  };
+  for (int t = 0; t < blocks; t += 2) {
+    step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < blocks) step(t + 1, std::integral_constant<int, 1>{});
   }
 
   __builtin_amdgcn_s_setprio(0);
   // O = acc / l (bf16), lse = (m + log2 l) * ln 2. Lane l holds query lr,
   // d = 32*db + 8*(v/4) + 4*lg + v%4: four consecutive d per 8-byte store.
+  l_run += __shfl_xor(l_run, 32);  // the row's two halves
   if (query < n_q) {
     const float inv = 1.0f / l_run;
     uint16_t* orow = O + bh * n_q * D + static_cast<int64_t>(query) * D;
