@@ -5,7 +5,7 @@
 // the three steps fused in one kernel so S and P never reach HBM; GPU/
 // attention notes, "online softmax" and "why FlashAttention saves memory").
 //
-// Per (batch*head, 128-query block) one workgroup of four waves; wave w owns
+// Per (batch*head, 256-query block) one workgroup of eight waves; wave w owns
 // queries q0 + 32w .. q0 + 32w + 31 and walks the keys in blocks of 64:
 //   1. S^T = K Q^T on v_mfma_f32_32x32x16_bf16, keys as rows: A = 32 rows of
 //      the K block (16-byte LDS reads), B = the wave's queries, held in
@@ -14,18 +14,26 @@
 //   2. online softmax per query, in base 2 (scores times scale * log2 e):
 //      block maximum over the lane's 32 values and its partner lane l^32,
 //      m_new = max(m, block max), alpha = 2^(m - m_new), p = 2^(s - m_new),
-//      l = l * alpha + sum p, O *= alpha (blocks without masked keys take
-//      the maximum of the raw scores and fold the scale into p's exponent,
-//      one FMA per score);
+//      l = l * alpha + sum p, O *= alpha (blocks without masked keys first
+//      try the current m, with the scale folded into p's exponent, one FMA
+//      per score, and fall back to the block maximum only when a sum shows
+//      that some score passed m + 8);
 //   3. O^T += V^T P^T: the p values, rounded to bf16, already sit where the
 //      MFMA's B operand wants them, for the key order of step 1 (within a
 //      16-key window lane l holds keys 4*(l/32) + 0..3 and 8 + 4*(l/32) +
 //      0..3); the A operand V^T is read from the row-major V block with two
 //      ds_read_b64_tr_b16 that return exactly those keys for row d = l%32.
 //      Any key order works as long as both operands share it.
-// K and V blocks are double-buffered in LDS by global_load_lds copies. At
-// the end O = O / l is stored in bf16 and lse = (m + log2 l) * ln 2 (the
-// natural-log logsumexp of the scaled scores) in fp32.
+// The waves form two groups, waves 0-3 and 4-7 (wave w runs on SIMD w % 4,
+// so each SIMD holds one of each). Each block takes two phases separated by
+// workgroup barriers: while one group issues the MFMAs of steps 3 (previous
+// block) and 1 (this block), the other runs a softmax on the vector units,
+// then they swap, so a SIMD's matrix core and vector unit work side by side
+// (the FlashAttention-3 "ping-pong" arrangement). K and V blocks sit in a
+// three-slot LDS ring (block t's K is read in phases 2t and 2t+1, its V in
+// 2t+2 and 2t+3), filled by global_load_lds copies a block ahead. At the end
+// O = O / l is stored in bf16 and lse = (m + log2 l) * ln 2 (the natural-log
+// logsumexp of the scaled scores) in fp32.
 //
 // LDS rows are head_dim * 2 bytes. K: 16-byte chunk c of row r sits at
 // c ^ f(r), f(r) = 2*(r % 8) + (r / 8) % 2 (d = 128) or (r >> 1) & 7
@@ -42,12 +50,11 @@
 // (score -inf; their V rows are zeroed in LDS, so an infinite value in row
 // n_kv - 1 cannot turn into NaN through a zero probability); query rows past
 // n_q load row n_q - 1 and are not stored.
-// Causal (key j > query i masked; n_q == n_kv): key blocks wholly above the
-// diagonal are skipped, and the query blocks run heaviest first (work_item).
+// Causal (key j > query i masked; n_q == n_kv): key blocks wholly above a
+// wave's queries are skipped by that wave, and the query blocks run
+// heaviest first (work_item).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
-
-#include <type_traits>
 
 #include "lds_copy.h"
 #include "tdm_internal.h"
@@ -61,7 +68,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4, kThreads = 64 * kWaves;
+constexpr int kWaves = 8, kThreads = 64 * kWaves;
+constexpr int kStages = 3;
 constexpr int kBQ = 32 * kWaves;  // queries per workgroup
 constexpr int kBKV = 64;          // keys per block
 
@@ -71,7 +79,7 @@ struct AttnCfg {
   static constexpr int kChunks = kRow / 16;
   static constexpr int kBlock = kBKV * kRow;   // one K or V block
   static constexpr int kStage = 2 * kBlock;    // K block, then V block
-  static constexpr int kLdsBytes = 2 * kStage;
+  static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kRowsPerCopy = 1024 / kRow;
   static constexpr int kCopies = kBlock / 1024 / kWaves;  // per wave, per operand
   static constexpr int kKSteps = D / 16;       // MFMA k-steps of Q K^T
@@ -133,7 +141,7 @@ __device__ __forceinline__ void work_item(int id, int n_qblocks, int n_heads, in
 }
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
+__global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O, float* __restrict__ lse, int n_q,
     int n_kv, int n_heads, float scale_log2, int causal) {
@@ -238,78 +246,93 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
     for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  issue(0, 0);
-  // One key block; the ring slot is a compile-time constant, so the LDS
-  // reads take it in their immediate offsets (the loop runs two blocks per
-  // iteration).
-  auto step = [&](const int t, auto slot) __attribute__((always_inline)) {
-    constexpr int cur = decltype(slot)::value;
-    wait_vm<0>();
-    __syncthreads();  // block t landed; every wave is done with block t-1's slot
-    issue(t + 1, cur ^ 1);
-    LDS_PTR(const uint8_t) kblk = lds + cur * T::kStage;
-    LDS_PTR(const uint8_t) vblk = kblk + T::kBlock;
-    const int kb0 = t * kBKV;
-    if (kb0 + kBKV > n_kv) {
-      // The block's rows past n_kv hold copies of row n_kv - 1. Their
-      // probabilities are 0, but 0 times an infinite value of V would be
-      // NaN, so their V rows are zeroed (whole rows: the swizzle only
-      // permutes chunks within a row).
-      const int first = n_kv - kb0;
-      LDS_PTR(uint8_t) vw = lds + cur * T::kStage + T::kBlock;
-      const u32x4 zero = {0u, 0u, 0u, 0u};
-      for (int i = tid; i < (kBKV - first) * (T::kRow / 16); i += kThreads)
-        *(LDS_PTR(u32x4))(vw + (first + i / (T::kRow / 16)) * T::kRow +
-                          (i % (T::kRow / 16)) * 16) = zero;
-      __syncthreads();
-    }
+  // Keys this wave needs: with the mask, blocks past its last query are
+  // skipped (the workgroup still walks them for the copies and barriers).
+  const int wave_blocks =
+      causal ? min(blocks, (q0 + 32 * wave + 32 + kBKV - 1) / kBKV) : blocks;
+  const int group = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
+  constexpr float kSlack = 8.0f;
+  f32x16 s[2];
+  bf16x8 pop[4];  // p of the last softmax phase in bf16, window w16 = keys 16*w16 ..
 
-    // 1. S^T for the two 32-key halves. The wave issues its MFMA sections
-    // at raised priority and its softmax at normal priority, so that on a
-    // SIMD shared by two waves the matrix core is served first (1.5-2.3%
-    // faster on 4 x 32 x 4096 x 128; results unchanged).
+  // Matrix phase for block t: O^T += V^T P^T of block t-1, then S^T of block
+  // t, at raised issue priority so the SIMD serves the MFMAs first.
+  auto matrix = [&](int t) __attribute__((always_inline)) {
     __builtin_amdgcn_s_setprio(1);
-    f32x16 s[2];
+    if (t >= 1 && t <= wave_blocks) {
+      LDS_PTR(const uint8_t) vblk = lds + ((t - 1) % kStages) * T::kStage + T::kBlock;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+      for (int w16 = 0; w16 < 4; ++w16) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < T::kKSteps; ++ks) {
-        const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 32 * h * T::kRow + koff[ks]);
-        s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
-                                                       0, 0, 0);
+        for (int db = 0; db < T::kDBlocks; ++db) {
+          LDS_PTR(const uint8_t) vw = vblk + 16 * w16 * T::kRow + voff[db];
+          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 8 * T::kRow));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
+          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop[w16],
+                                                              acc_o[db], 0, 0, 0);
+        }
       }
+      // V reads eight ahead of the MFMAs that use them.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int g = 0; g < 4 * T::kDBlocks - 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
-
+    if (t < wave_blocks) {
+      LDS_PTR(const uint8_t) kblk = lds + (t % kStages) * T::kStage;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < T::kKSteps; ++ks) {
+          const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 32 * h * T::kRow + koff[ks]);
+          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
+                                                         0, 0, 0);
+        }
+      }
+      // K reads eight ahead.
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int g = 0; g < 2 * T::kKSteps - 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
     __builtin_amdgcn_s_setprio(0);
-    // 2. Online softmax (base 2). Blocks with masked keys (the last key
-    // block, blocks on the causal diagonal) and a negative scale take the
-    // general form; the others a shorter one (below). Both tests are uniform
-    // over the wave.
+  };
+
+  // Softmax phase for block t (online softmax in base 2, as before).
+  auto softmax = [&](int t) __attribute__((always_inline)) {
+    if (t < 0 || t >= wave_blocks) return;
+    const int kb0 = t * kBKV;
     const bool general =
         !(scale_log2 >= 0.f) || kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
-    constexpr float kSlack = 8.0f;
     float psum = 0.f, alpha = 1.f, m_new = m_run;
-    bf16x8 pop[4];  // p in bf16 (v_cvt_pk_bf16_f32: nearest even), window w16 = keys 16*w16 ..
-    // p = 2^(x - m) for the block's scores, their sum over this lane, and the
-    // bf16 operands of step 3.
     auto exps = [&](float m_use, bool raw) __attribute__((always_inline)) {
-      psum = 0.f;
+      // Exponents, exponentials, then four partial sums: independent work
+      // in each stage, so one wave alone on its SIMD keeps issuing.
+      float p[32];
 #pragma unroll
-      for (int w16 = 0; w16 < 4; ++w16)
+      for (int i = 0; i < 32; ++i) {
+        const float x = s[i >> 4][i & 15];
+        p[i] = raw ? __builtin_fmaf(x, scale_log2, -m_use) : x - m_use;
+      }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float x = s[w16 >> 1][8 * (w16 & 1) + e];
-          const float p = __builtin_amdgcn_exp2f(raw ? __builtin_fmaf(x, scale_log2, -m_use) : x - m_use);
-          psum += p;
-          pop[w16][e] = static_cast<__bf16>(p);
-        }
+      for (int i = 0; i < 32; ++i) p[i] = __builtin_amdgcn_exp2f(p[i]);
+      float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) part[i & 3] += p[i];
+      psum = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) pop[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
     };
-    // The reference maximum m moves only when the block's maximum exceeds it
-    // by more than 8 (in log2 units): until then p = 2^(x - m) stays at or
-    // below 256, which fp32 sums and bf16 operands carry without loss, and O
-    // and l remain scaled by the same m, so the result is the exact softmax.
     auto rebase = [&](float bmax, bool raw) __attribute__((always_inline)) {
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
       m_new = bmax > m_run + kSlack ? bmax : m_run;
@@ -318,18 +341,22 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
       exps(m_use, raw);
     };
     if (general) {
-      // Scale every score, set masked ones to -inf, take the maximum.
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[h][v] *= scale_log2;
       if (kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave)) {
         const int lim = causal ? min(n_kv - 1, query) : n_kv - 1;  // last visible key
+        // This lane's first key of the block, made here (an opaque value), so
+        // the 32 per-score key offsets are not kept in registers across the
+        // loop.
+        int key0 = kb0 + 4 * lg;
+        asm volatile("" : "+v"(key0));
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int key = kb0 + 32 * h + 8 * (v >> 2) + 4 * lg + (v & 3);
+            const int key = key0 + 32 * h + 8 * (v >> 2) + (v & 3);
             s[h][v] = key > lim ? -INFINITY : s[h][v];
           }
       }
@@ -340,14 +367,6 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
         for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
       rebase(bmax, false);
     } else {
-      // No masked key and a scale >= 0: first try the current m, with the
-      // scale folded into the exponent's argument (one FMA per score). Every
-      // p is at most the lane's sum, so a sum of at most 256 on every lane
-      // shows that no score exceeds m by more than 8 and m stays. Otherwise
-      // (the first block, where m = -inf makes every p infinite, and blocks
-      // whose scores reach past m + 8 or crowd near it) take the maximum of
-      // the raw scores, scale only that (exact: rounding is monotonic) and
-      // redo the block.
       exps(m_run, true);
       if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
         float bmax = -INFINITY;
@@ -358,43 +377,52 @@ __global__ __launch_bounds__(kThreads, 2) void attention_fwd_kernel(
         rebase(bmax * scale_log2, true);
       }
     }
-    // l is kept per lane (this lane's keys of the row) and the two halves of
-    // a row are added at the end; alpha is the row's, so both scale alike.
     l_run = l_run * alpha + psum;
     m_run = m_new;
-    // Rescale O only when some query of the wave raised its maximum (after
-    // the first blocks most do not).
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
       for (int db = 0; db < T::kDBlocks; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
     }
+  };
 
-    // 3. O^T += V^T P^T over the four 16-key windows.
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int w16 = 0; w16 < 4; ++w16) {
-
-      // Transposing reads: in each 16-lane group G, lane i points at key row
-      // base + i/4 and d columns 4*(i%4)..+3 of its 16-column half; lane j
-      // gets 4 consecutive keys of column j (rows of the window, then 8
-      // rows further).
-#pragma unroll
-      for (int db = 0; db < T::kDBlocks; ++db) {
-        LDS_PTR(const uint8_t) vw = vblk + 16 * w16 * T::kRow + voff[db];
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 8 * T::kRow));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
-        acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop[w16],
-                                                            acc_o[db], 0, 0, 0);
-      }
+  // Two phases per block. Group 0 runs block t's matrix phase while group 1
+  // runs the softmax of block t-1, then the roles swap, so each SIMD holds
+  // one wave issuing MFMAs and one issuing vector work at any time. Block t
+  // lives in slot t % 3: its K is read in phases 2t and 2t+1, its V in
+  // phases 2t+2 and 2t+3, and block t+3's copy starts at phase 2t+4.
+  issue(0, 0);
+  auto phase_start = [&](int t) __attribute__((always_inline)) {
+    wait_vm<0>();
+    __syncthreads();  // block t landed; phase 2t begins
+    issue(t + 1, (t + 1) % kStages);
+    const int kb0 = t * kBKV;
+    if (t < blocks && kb0 + kBKV > n_kv) {
+      // Rows past n_kv hold copies of row n_kv - 1: zero their V rows (read
+      // from phase 2t+2 on), so 0 * inf cannot make NaN.
+      const int first = n_kv - kb0;
+      LDS_PTR(uint8_t) vw = lds + (t % kStages) * T::kStage + T::kBlock;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      for (int i = tid; i < (kBKV - first) * (T::kRow / 16); i += kThreads)
+        *(LDS_PTR(u32x4))(vw + (first + i / (T::kRow / 16)) * T::kRow + (i % (T::kRow / 16)) * 16) = zero;
     }
   };
-  for (int t = 0; t < blocks; t += 2) {
-    step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < blocks) step(t + 1, std::integral_constant<int, 1>{});
+  // The two groups run the same barriers (two per block) in their own loops.
+  if (group == 0) {
+    for (int t = 0; t <= blocks; ++t) {
+      phase_start(t);
+      matrix(t);
+      __syncthreads();  // phase 2t+1
+      softmax(t);
+    }
+  } else {
+    for (int t = 0; t <= blocks; ++t) {
+      phase_start(t);
+      softmax(t - 1);
+      __syncthreads();  // phase 2t+1
+      matrix(t);
+    }
   }
 
   __builtin_amdgcn_s_setprio(0);
