@@ -70,6 +70,9 @@ SHAPES = [  # batch, heads, n_q, n_kv, head_dim, causal
     (1, 1, 1, 1, 64, False), (1, 2, 37, 53, 64, False), (2, 3, 128, 128, 128, True),
     (1, 2, 300, 300, 128, True), (1, 1, 129, 65, 128, False), (1, 2, 1000, 777, 64, False),
     (2, 2, 256, 256, 64, True), (1, 1, 64, 4096, 128, False), (1, 1, 200, 1, 128, False),
+    # a second 256-query workgroup holding one query; causal diagonals that
+    # cross the waves of several workgroups
+    (1, 2, 257, 700, 128, False), (1, 1, 520, 520, 64, True), (1, 1, 513, 513, 128, True),
 ]
 
 
@@ -123,6 +126,23 @@ def test_large_scores_stay_finite():
     O, L = run(Q, K, V, False)
     assert np.isfinite(O).all() and np.isfinite(L).all() and np.abs(L).max() > 100
     check(Q, K, V, False, 64 ** -0.5, O, L)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rising_scores_move_the_maximum_in_many_blocks(causal):
+    """Keys that grow along the sequence make later blocks' scores pass the
+    running maximum again and again, so most blocks redo their
+    probabilities from the new maximum and rescale O and l."""
+    rng = np.random.default_rng(6)
+    n, d = 900, 128
+    Q = inputs.normal_bf16(rng, (1, 2, n, d), 1.0)
+    grow = (0.25 + np.arange(n) / 60.0).reshape(1, 1, n, 1)
+    K = inputs.fp32_to_bf16_bits(
+        (inputs.bf16_bits_to_fp32(inputs.normal_bf16(rng, (1, 2, n, d), 1.0)) * grow).astype(np.float32))
+    V = inputs.normal_bf16(rng, (1, 2, n, d), 1.0)
+    O, L = run(Q, K, V, causal)
+    assert np.isfinite(O).all() and np.isfinite(L).all()
+    check(Q, K, V, causal, d ** -0.5, O, L)
 
 
 @pytest.mark.parametrize("causal", [False, True])
