@@ -286,16 +286,18 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     if (t < wave_blocks) {
       LDS_PTR(const uint8_t) kblk = lds + (t % kStages) * T::kStage;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
+      // The two halves' accumulator chains alternate.
 #pragma unroll
-        for (int ks = 0; ks < T::kKSteps; ++ks) {
+      for (int ks = 0; ks < T::kKSteps; ++ks)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
           const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 32 * h * T::kRow + koff[ks]);
           s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
                                                          0, 0, 0);
         }
-      }
       // K reads eight ahead.
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
