@@ -68,6 +68,8 @@ PEAK = {
 }
 KERNEL = {  # path -> (dominant kernel, source file, every kernel one call launches)
     "edge": ("edge_kernel", "gemm_edge.hip", ["edge_kernel"]),
+    # small fp32 products on the edge path (M, N, K <= 512, K and N multiples of 4)
+    "edge_small": ("small_f32_kernel", "gemm_edge.hip", ["small_f32_kernel"]),
     "valu": ("valu_f32_kernel", "gemm_valu_f32.hip", ["valu_f32_kernel"]),
     "mfma": ("mfma_bf16_kernel", "gemm_mfma_bf16.hip", ["mfma_bf16_kernel"]),
     "mfma_f32": ("mfma_f32_kernel", "gemm_mfma_f32.hip", ["mfma_f32_kernel"]),
@@ -236,6 +238,9 @@ def workload_kernels(name: str, path=None):
         pname = "mfma_f32"
     if pname == "skinny" and w.b_layout == "nk":
         pname = "skinny_nk"
+    if (pname == "edge" and w.kind == "f32" and int(layout) == 0 and max(w.M, w.N, w.K) <= 512
+            and w.K % 4 == 0 and w.N % 4 == 0 and w.N >= 4 and w.K >= 4):
+        pname = "edge_small"
     return KERNEL[pname]
 
 

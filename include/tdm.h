@@ -88,7 +88,7 @@ typedef enum tdm_kind {
 /* Kernel families behind the GEMM calls. */
 typedef enum tdm_path {
   TDM_PATH_AUTO = 0,   /* let the dispatcher choose (what gemm_* do)        */
-  TDM_PATH_EDGE = 1,   /* 32x32 LDS-tiled kernel: any shape and alignment    */
+  TDM_PATH_EDGE = 1,   /* LDS-tiled kernels for any shape and alignment      */
   TDM_PATH_VALU = 2,   /* fp32 only: register- and LDS-tiled vector FMA      */
   TDM_PATH_MFMA = 3,   /* matrix cores: bf16 or fp32 in, fp32 accumulate     */
   TDM_PATH_SKINNY = 4  /* bf16 only, M <= 16: streams B once at HBM rate     */

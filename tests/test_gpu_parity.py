@@ -100,6 +100,25 @@ def test_ragged(kind, shape, path):
     check_full(kind, A, B, gpu_product(kind, A, B, path), f"{kind}/{shape}/{path.name}")
 
 
+# Small fp32 products, which the edge path runs on 16 x 16 tiles with whole
+# K panels in LDS (M and N up to 512, K up to 512, K and N multiples of 4,
+# 16-byte aligned rows): ragged tiles, the largest K, K = 4.
+SMALL_F32 = [(1, 4, 4), (17, 20, 4), (15, 16, 12), (256, 256, 256), (200, 100, 500),
+             (511, 508, 512), (512, 512, 512)]
+
+
+@pytest.mark.parametrize("shape", SMALL_F32, ids=[f"{m}x{n}x{k}" for m, n, k in SMALL_F32])
+def test_small_f32_products(shape):
+    M, N, K = shape
+    log(f"case small f32 {shape}")
+    A, B = random_inputs("f32", M, N, K, seed=M + 3 * N + 5 * K)
+    check_full("f32", A, B, gpu_product("f32", A, B, P.EDGE), f"small f32 {shape}")
+    rng = np.random.default_rng(M + N + K)
+    A = inputs.small_int_matrix(rng, (M, K), kind="f32")
+    B = inputs.small_int_matrix(rng, (K, N), kind="f32")
+    assert np.array_equal(gpu_product("f32", A, B, P.EDGE).astype(np.float64), oracle.gemm(A, B))
+
+
 # Shapes large enough that the matrix-core kernels take their 256 x 256 tiles
 # (the last round of tiles over the 256 CUs is at least 70% full for bf16,
 # 90% for fp32), with partial tiles in M, N and K.

@@ -10,6 +10,14 @@
 //
 // This kernel carries the ragged remainders the fast paths leave, tiny
 // products, and any call whose pointers are not 16-byte aligned.
+//
+// Small fp32 products (M and N up to 512, K up to 512, A M x K and B K x N,
+// 16-byte rows): the kernel above walks K in eight or more dependent steps,
+// each waiting on a global load, and puts few workgroups on the CUs (8 x 8
+// for 256^3). small_f32_kernel instead gives each workgroup a 16 x 16 tile
+// of C, loads its whole 16 x K panel of A and K x 16 panel of B into LDS at
+// once (all loads in flight together), lets its four waves take every
+// fourth k, and adds the four partial sums in wave order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -101,6 +109,91 @@ __global__ __launch_bounds__(kThreads) void edge_kernel(
   put(r1, c1, acc11);
 }
 
+constexpr int kSmallT = 16;       // small_f32_kernel: C tile edge
+constexpr int kSmallMaxMN = 512;  // largest M and N it takes
+constexpr int kSmallMaxK = 512;   // largest K (the panels fill 66 KB of LDS)
+
+// LDS: A panel [16][K + 4] (the row pad puts the 16 rows in different banks),
+// then B panel [K][16].
+__global__ __launch_bounds__(kThreads) void small_f32_kernel(
+    const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M,
+    int N, int K, int tiles_n) {
+  extern __shared__ __attribute__((aligned(16))) float small_lds[];
+  const int tid = threadIdx.x;
+  const int tm = blockIdx.x / tiles_n;
+  const int tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * kSmallT, n0 = tn * kSmallT;
+  const int lda = K + 4;
+  float* As = small_lds;
+  float* Bs = small_lds + kSmallT * lda;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  const f4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // Panels: rows past M and columns past N load as zero. K and N are
+  // multiples of 4 and the rows 16-byte aligned, so every float4 lies wholly
+  // inside a row, and wholly inside or outside the matrix.
+  const int k4 = K / 4;
+#pragma unroll 8
+  for (int i = tid; i < kSmallT * k4; i += kThreads) {
+    const int r = i / k4, c = i - r * k4;
+    const f4 v = m0 + r < M
+                     ? *reinterpret_cast<const f4*>(A + static_cast<int64_t>(m0 + r) * K + 4 * c)
+                     : zero;
+    *reinterpret_cast<f4*>(As + r * lda + 4 * c) = v;
+  }
+#pragma unroll 8
+  for (int i = tid; i < K * (kSmallT / 4); i += kThreads) {
+    const int k = i / (kSmallT / 4), c = i - k * (kSmallT / 4);
+    const int n = n0 + 4 * c;
+    const f4 v = n < N ? *reinterpret_cast<const f4*>(B + static_cast<int64_t>(k) * N + n) : zero;
+    *reinterpret_cast<f4*>(Bs + k * kSmallT + 4 * c) = v;
+  }
+  __syncthreads();
+
+  // Wave w takes k = w, w+4, ...; lane l the outputs (l/4, 4(l%4) .. +3).
+  const int wave = tid >> 6, lane = tid & 63;
+  const int r = lane >> 2, c = 4 * (lane & 3);
+  f4 acc = zero;
+  for (int k = wave; k < K; k += 4) {
+    const float a = As[r * lda + k];
+    const f4 b = *reinterpret_cast<const f4*>(Bs + k * kSmallT + c);
+    acc.x = fmaf(a, b.x, acc.x);
+    acc.y = fmaf(a, b.y, acc.y);
+    acc.z = fmaf(a, b.z, acc.z);
+    acc.w = fmaf(a, b.w, acc.w);
+  }
+  __syncthreads();  // every wave is done with the panels
+  float* red = small_lds;  // [wave][16 x 16], over the panels
+  *reinterpret_cast<f4*>(red + wave * kSmallT * kSmallT + r * kSmallT + c) = acc;
+  __syncthreads();
+  const int orow = tid / kSmallT, ocol = tid % kSmallT;
+  float sum = 0.f;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) sum += red[w * kSmallT * kSmallT + tid];
+  if (m0 + orow < M && n0 + ocol < N) C[static_cast<int64_t>(m0 + orow) * N + n0 + ocol] = sum;
+}
+
+bool small_f32_fits(const float* A, const float* B, int M, int N, int K) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(A) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+  return aligned && K % 4 == 0 && N % 4 == 0 && K >= 4 && K <= kSmallMaxK && M >= 1 &&
+         M <= kSmallMaxMN && N >= 4 && N <= kSmallMaxMN;
+}
+
+hipError_t launch_small_f32(const float* A, const float* B, float* C, int M, int N, int K,
+                            hipStream_t s) {
+  static std::atomic<uint64_t> lds_ok{0};  // devices already opted in
+  // The panels, or the four waves' 16 x 16 partial sums if K is tiny.
+  const int lds_bytes = max((kSmallT * (K + 4) + K * kSmallT) * 4, 4 * kSmallT * kSmallT * 4);
+  hipError_t e = allow_lds(lds_ok, reinterpret_cast<const void*>(small_f32_kernel),
+                           (kSmallT * (kSmallMaxK + 4) + kSmallMaxK * kSmallT) * 4);
+  if (e != hipSuccess) return e;
+  const int tiles_m = (M + kSmallT - 1) / kSmallT;
+  const int tiles_n = (N + kSmallT - 1) / kSmallT;
+  return launch(small_f32_kernel, dim3(tiles_m * tiles_n), dim3(kThreads), lds_bytes, s, A, B, C,
+                M, N, K, tiles_n);
+}
+
 __global__ void fill_zero_kernel(float* __restrict__ C, int64_t count) {
   const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -130,6 +223,7 @@ hipError_t launch_fill_zero_f32(float* C, int64_t count, hipStream_t s) {
 
 hipError_t launch_edge_f32(const float* A, const float* B, float* C, int M,
                            int N, int K, hipStream_t s) {
+  if (small_f32_fits(A, B, M, N, K)) return launch_small_f32(A, B, C, M, N, K, s);
   return launch_edge<float, false, false>(A, B, C, M, N, K, Epilogue{}, s);
 }
 
@@ -139,7 +233,7 @@ hipError_t launch_edge_f32_layout(const float* A, const float* B, bool b_nk, boo
     return b_nk ? launch_edge<float, false, true, true>(A, B, C, M, N, K, Epilogue{}, s)
                 : launch_edge<float, false, false, true>(A, B, C, M, N, K, Epilogue{}, s);
   if (b_nk) return launch_edge<float, false, true>(A, B, C, M, N, K, Epilogue{}, s);
-  return launch_edge<float, false, false>(A, B, C, M, N, K, Epilogue{}, s);
+  return launch_edge_f32(A, B, C, M, N, K, s);
 }
 
 hipError_t launch_edge_bf16(const uint16_t* A, const uint16_t* B, float* C,
