@@ -454,8 +454,7 @@ def main():
     chosen = tdm.tdm_select_path_ex(kind, layout, w.M, w.N, w.K) if path == tdm.Path.AUTO \
         else path
     pname = tdm.path_name(chosen)
-    kernel, ksrc, kernels = KERNEL["mfma_f32" if (pname == "mfma" and w.kind == "f32") else
-                                   "skinny_nk" if (pname == "skinny" and nk) else pname]
+    kernel, ksrc, kernels = workload_kernels(w.name, pname)
 
     A, B = inputs.make_inputs(w)
 

@@ -131,22 +131,38 @@ __global__ __launch_bounds__(kThreads) void small_f32_kernel(
 
   // Panels: rows past M and columns past N load as zero. K and N are
   // multiples of 4 and the rows 16-byte aligned, so every float4 lies wholly
-  // inside a row, and wholly inside or outside the matrix.
+  // inside a row, and wholly inside or outside the matrix. Every load of the
+  // thread is issued before the first is used (addresses clamped inside the
+  // matrix, unused values replaced by zero), so the panels cost one memory
+  // latency rather than one per load.
+  // A: thread t loads row t/16, float4 columns t%16 + 16j (16 lanes cover
+  // 256 contiguous bytes of a row). B: row t/4 + 64j, float4 column t%4.
+  constexpr int kJ = kSmallMaxK / 64;  // loads per thread and panel at the largest K
   const int k4 = K / 4;
-#pragma unroll 8
-  for (int i = tid; i < kSmallT * k4; i += kThreads) {
-    const int r = i / k4, c = i - r * k4;
-    const f4 v = m0 + r < M
-                     ? *reinterpret_cast<const f4*>(A + static_cast<int64_t>(m0 + r) * K + 4 * c)
-                     : zero;
-    *reinterpret_cast<f4*>(As + r * lda + 4 * c) = v;
+  const int ar = tid >> 4, ac = tid & 15;
+  const int arow = min(m0 + ar, M - 1);
+  f4 va[kJ], vb[kJ];
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int c = min(ac + 16 * j, k4 - 1);
+    va[j] = *reinterpret_cast<const f4*>(A + static_cast<int64_t>(arow) * K + 4 * c);
   }
-#pragma unroll 8
-  for (int i = tid; i < K * (kSmallT / 4); i += kThreads) {
-    const int k = i / (kSmallT / 4), c = i - k * (kSmallT / 4);
-    const int n = n0 + 4 * c;
-    const f4 v = n < N ? *reinterpret_cast<const f4*>(B + static_cast<int64_t>(k) * N + n) : zero;
-    *reinterpret_cast<f4*>(Bs + k * kSmallT + 4 * c) = v;
+  const int bc = tid & 3, bk0 = tid >> 2;
+  const int bn = min(n0 + 4 * bc, N - 4);
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int k = min(bk0 + 64 * j, K - 1);
+    vb[j] = *reinterpret_cast<const f4*>(B + static_cast<int64_t>(k) * N + bn);
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int c = ac + 16 * j;
+    if (c < k4) *reinterpret_cast<f4*>(As + ar * lda + 4 * c) = m0 + ar < M ? va[j] : zero;
+  }
+#pragma unroll
+  for (int j = 0; j < kJ; ++j) {
+    const int k = bk0 + 64 * j;
+    if (k < K) *reinterpret_cast<f4*>(Bs + k * kSmallT + 4 * bc) = n0 + 4 * bc < N ? vb[j] : zero;
   }
   __syncthreads();
 
@@ -154,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void small_f32_kernel(
   const int wave = tid >> 6, lane = tid & 63;
   const int r = lane >> 2, c = 4 * (lane & 3);
   f4 acc = zero;
+#pragma unroll 4
   for (int k = wave; k < K; k += 4) {
     const float a = As[r * lda + k];
     const f4 b = *reinterpret_cast<const f4*>(Bs + k * kSmallT + c);
