@@ -127,6 +127,10 @@ def parse():
     ap.add_argument("--traffic-json", metavar="FILE", default=None,
                     help="with --summarize-counters over FETCH_SIZE and WRITE_SIZE runs: write "
                          "the kernel's HBM bytes per launch as the record bench.py reads")
+    ap.add_argument("--sample-power", action="store_true",
+                    help="sample the socket power and engine clock (amd-smi) every ~0.25 s over "
+                         "the timed region and add their medians to the line as `power`; give "
+                         "it enough --steps for a few seconds")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the product, run a plain device copy of this many MiB "
                          "(reference for HBM byte counters)")
@@ -169,6 +173,62 @@ class ProfilerRegion:
 
 
 REGION = None
+
+
+class PowerSampler:
+    """Socket power and engine clock as `amd-smi metric -p -c` reports them,
+    sampled from a thread between start() and stop()."""
+
+    CMD = ["amd-smi", "metric", "-p", "-c"]
+
+    def __init__(self, interval_s: float = 0.25):
+        self.interval_s = interval_s
+        self.samples = []  # (watts, MHz)
+        self._stop = None
+        self._thread = None
+
+    def _one(self):
+        import re
+        import subprocess
+        try:
+            r = subprocess.run(self.CMD, capture_output=True, text=True, timeout=10)
+        except (OSError, subprocess.SubprocessError):
+            return None
+        p = re.search(r"SOCKET_POWER:\s*([0-9.]+)", r.stdout)
+        c = re.search(r"^\s*CLK:\s*([0-9.]+)", r.stdout, re.M)
+        return (float(p.group(1)), float(c.group(1))) if p and c else None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._one()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.interval_s)
+
+    def start(self):
+        import threading
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        import statistics
+        if not self.samples:
+            return {"samples": 0, "tool": " ".join(self.CMD)}
+        w = [x for x, _ in self.samples]
+        c = [y for _, y in self.samples]
+        return {"samples": len(self.samples), "tool": " ".join(self.CMD),
+                "socket_w_median": statistics.median(w), "socket_w_min": min(w),
+                "socket_w_max": max(w), "sclk_mhz_median": statistics.median(c),
+                "sclk_mhz_min": min(c), "sclk_mhz_max": max(c)}
+
+
+POWER = None  # a PowerSampler over the timed region, with --sample-power
 
 
 def timed_region():
@@ -426,6 +486,9 @@ def cpu_baseline(w, A, B, C_gpu, target_s: float, bias=None):
 
 def main():
     args = parse()
+    global POWER
+    if args.sample_power:
+        POWER = PowerSampler()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
@@ -513,6 +576,8 @@ def main():
         region = timed_region() if profiled else None
         if region:
             region.resume()
+            if POWER:
+                POWER.start()
         start.record(stream)
         for i in range(args.steps):
             step(args.warmup + i)
@@ -520,6 +585,8 @@ def main():
         torch.cuda.synchronize()
         if region:
             region.pause()
+            if POWER:
+                POWER.stop()
         return start.elapsed_time(end) / args.steps
 
     profiled = True  # only the main measurement is the profiler's region
@@ -678,6 +745,8 @@ def main():
         B_kn = np.ascontiguousarray(B.T) if nk else B  # the oracle takes B as K x N
         A_mk = np.ascontiguousarray(A.T) if km else A  # ... and A as M x K
         line["cpu_baseline"] = cpu_baseline(w, A_mk, B_kn, C_gpu, args.cpu_seconds, bias_np)
+    if POWER:
+        line["power"] = POWER.summary()
     print(json.dumps(line), flush=True)
 
 
@@ -707,6 +776,8 @@ def time_calls(step, warmup: int, steps: int, stream, profiled: bool = False) ->
     region = timed_region() if profiled else None
     if region:
         region.resume()
+        if POWER:
+            POWER.start()
     start.record(stream)
     for i in range(steps):
         step(warmup + i)
@@ -714,6 +785,8 @@ def time_calls(step, warmup: int, steps: int, stream, profiled: bool = False) ->
     torch.cuda.synchronize()
     if region:
         region.pause()
+        if POWER:
+            POWER.stop()
     return start.elapsed_time(end) / steps
 
 
@@ -855,6 +928,8 @@ def main_fp8(args, w):
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_fp8(w, A, B, sa, sb, C_gpu, args.cpu_seconds)
+    if POWER:
+        line["power"] = POWER.summary()
     print(json.dumps(line), flush=True)
 
 
@@ -978,6 +1053,8 @@ def main_attention(args, w):
         line["vendor_blas"] = vendor
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_attention(w, Q, K, V, O_gpu, args.cpu_seconds)
+    if POWER:
+        line["power"] = POWER.summary()
     print(json.dumps(line), flush=True)
 
 

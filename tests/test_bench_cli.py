@@ -161,3 +161,25 @@ def test_traffic_record_from_byte_counters(tmp_path):
     assert rec["kernel"] == "mfma_bf16_kernel" and rec["workload"] == "bf16_8192"
     assert rec["hbm_bytes_per_launch"] == (1000.0 * 2.0 + 300.0) * 1024
     assert rec["source"] == "gemm_mfma_bf16.hip" and len(rec["source_sha"]) == 16
+
+
+def test_power_sampler_reads_socket_power_and_the_first_engine_clock(monkeypatch):
+    """--sample-power parses amd-smi's socket power and the first GFX clock
+    (not MIN_CLK / MAX_CLK) and reports medians over its samples."""
+    sys.path.insert(0, ROOT)
+    import bench
+
+    out = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1401 W\n    CLOCK:\n        GFX_0:\n"
+           "            CLK: 1687 MHz\n            MIN_CLK: 500 MHz\n            MAX_CLK: 2400 MHz\n"
+           "        GFX_1:\n            CLK: 1690 MHz\n")
+
+    class R:
+        stdout = out
+
+    monkeypatch.setattr(subprocess, "run", lambda *a, **k: R())
+    p = bench.PowerSampler(interval_s=0.01)
+    assert p._one() == (1401.0, 1687.0)
+    p.samples = [(1400.0, 1690.0), (1390.0, 1700.0), (1401.0, 1680.0)]
+    s = p.summary()
+    assert s["samples"] == 3 and s["socket_w_median"] == 1400.0 and s["sclk_mhz_median"] == 1690.0
+    assert s["socket_w_min"] == 1390.0 and s["sclk_mhz_max"] == 1700.0
