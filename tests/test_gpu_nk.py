@@ -152,3 +152,28 @@ def test_full_size_linear_gelu():
         worst = max(worst, float((np.abs(got[r:r + 32, c:c + 32] - E) / tol).max()))
     assert worst <= 1.0, worst
     log(f"  {w.name}: worst err/bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("shape", [(4000, 3900, 200), (5000, 4600, 200), (5000, 4600, 4096)])
+def test_large_tiles_in_one_round_and_in_several(shape):
+    """256 x 256 tiles with B stored N x K: 4000 x 3900 fills exactly one
+    round of the CUs (64 k per step over two slots), 5000 x 4600 two rounds
+    (32 k per step over four slots, the ping-pong schedule); partial tiles
+    in M and N, and a partial last K step (K = 200) or none (K = 4096)."""
+    M, N, K = shape
+    log(f"case nk large tiles {shape}")
+    rng = np.random.default_rng(M + N + K + 7)
+    A = inputs.small_int_matrix(rng, (M, K), kind="bf16")
+    Bt = inputs.small_int_matrix(rng, (N, K), kind="bf16")
+    if K <= 256:
+        assert np.array_equal(run_nk(A, Bt, P.MFMA).astype(np.float64), oracle.gemm_nt(A, Bt))
+    else:  # sampled tiles keep the oracle's share to seconds
+        got = run_nk(A, Bt, P.MFMA)
+        tiles = _tiles(M, N)
+        for (r, c), Rt in zip(tiles, oracle.gemm_nt_tiles(A, Bt, tiles)):
+            assert np.array_equal(got[r:r + 32, c:c + 32].astype(np.float64), Rt), (r, c)
+    A = inputs.normal_bf16(rng, (M, K), 1.0)
+    Bt = inputs.normal_bf16(rng, (N, K), 1.0)
+    if K <= 256:
+        p = oracle.parity(run_nk(A, Bt, P.MFMA), oracle.gemm_nt(A, Bt), max_abs(A), max_abs(Bt), K)
+        assert p["norm_max_err"] <= TOL_BF16 and p["rel_fro"] <= TOL_FRO, p

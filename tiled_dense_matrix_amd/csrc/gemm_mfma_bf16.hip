@@ -11,15 +11,18 @@
 //     into LDS with 16-byte row-contiguous loads that write LDS directly
 //     (global_load_lds), so the copy costs no registers and no LDS stores;
 //   * eight waves (2 x 4) each hold a (BM/2) x (BN/4) block of C in registers
-//     as 32 x 32 accumulators fed by v_mfma_f32_32x32x16_bf16; two waves per
-//     SIMD let one issue matrix instructions while the other waits;
+//     as 32 x 32 accumulators fed by v_mfma_f32_32x32x16_bf16; each SIMD
+//     holds two waves, one of each half of the workgroup;
 //   * LDS holds a ring of STAGES steps: the copy of step t+STAGES-1 is issued
 //     while the waves multiply step t, so a copy has STAGES-1 steps to land
 //     (data that misses the XCD's L2 comes from the last-level cache or HBM,
-//     whose latency one step does not cover); one barrier per step;
-//   * the fragments of the next sub-step are read while the current one is
-//     multiplied, across the step boundary too: the first reads of step t+1
-//     follow the barrier and overlap the last MFMAs of step t;
+//     whose latency one step does not cover);
+//   * the two halves of the workgroup take turns (ping-pong): while waves
+//     0-3 run a step's MFMAs on fragments already in registers, waves 4-7
+//     read theirs from LDS and issue their copies, then they swap, with a
+//     workgroup barrier between phases. Rings of two slots and a partial
+//     last K step use one loop per wave instead, which reads the next
+//     sub-step's fragments while the current one is multiplied;
 //   * C is written through LDS in row-contiguous groups of four, where the
 //     optional fused epilogue (bias, GELU, residual, bf16 output; §4.3
 //     operator fusion) finishes each output.
@@ -323,7 +326,11 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
   // channels; a small stagger spreads them while workgroups that share
   // operand rows stay within a few steps of each other, which keeps their
   // reuse in L2 (a stagger over the whole K range loses it and is slower).
-  const int rot = full_steps > 0
+  // When every tile of a K x N product is resident at once (one round of
+  // workgroups), a common start is faster (4096^3: 109.9 against 111.2 us);
+  // N x K and K x M operands keep the stagger.
+  const bool stagger = T::kBNK || T::kAKM || gridDim.x > static_cast<unsigned>(kCUs);
+  const int rot = stagger && full_steps > 0
                       ? static_cast<int>(((blockIdx.x >> 3) & 15u) % static_cast<unsigned>(full_steps))
                       : 0;
   const CopyPlan<T> plan = make_plan<T>(M, N, K, m0, n0, wave, lane);
@@ -356,48 +363,120 @@ __global__ __launch_bounds__(T::kThreads, 1) void mfma_bf16_kernel(
   wait_step(0);
   __syncthreads();
 
-  bf16x8 a[2][T::kFragM], b[2][T::kFragN];
+  // Ping-pong between the two halves of the workgroup (waves 0-3 and 4-7;
+  // wave w runs on SIMD w % 4, so each SIMD holds one wave of each). Every K
+  // step takes two phases separated by workgroup barriers: in one, a group
+  // issues its share of the copies and reads all of the step's fragments
+  // from LDS into registers; in the next, it runs the step's MFMAs while the
+  // other group does its reads. The matrix core of a SIMD is then fed by one
+  // wave whose operands are already in registers, and LDS reads never stall
+  // its issue. Step t's slot is read in phases 2t (group 0) and 2t+1 (group
+  // 1) and refilled from phase 2t+2 on, so its copies still have S-1 steps
+  // to land. Measured on 8192^3 and 4096^3 (the same sums, bit for bit):
+  // 844 / 111.8 us against 869 / 115.2 us for the interleaved loop below,
+  // which remains for a partial last step and for two-slot rings.
+  constexpr bool kPingPong = T::WM == 2 && T::WN == 4 && T::kSub == 2 && S >= 3;
+  if (kPingPong && steps == full_steps) {
+    if constexpr (kPingPong) {
+      const int group = wave >> 2;
+      bf16x8 fa[T::kSub][T::kFragM], fb[T::kSub][T::kFragN];
+      auto load_frags = [&](int slot) __attribute__((always_inline)) {
+        LDS_PTR(const uint8_t) pa = lds + slot * T::kStage;
+        LDS_PTR(const uint8_t) pb = pa + T::kStageA;
 #pragma unroll
-  for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lane);
+        for (int s = 0; s < T::kSub; ++s) {
 #pragma unroll
-  for (int j = 0; j < T::kFragN; ++j) b[0][j] = read_b<T>(lds + T::kStageA, col_b + 32 * j, 0, lane);
-
-  int cur = 0;  // ring slot of step t
-  for (int t = 0; t < steps; ++t) {
-    const int nxt = cur + 1 == S ? 0 : cur + 1;
-    issue(t + S - 1, cur == 0 ? S - 1 : cur - 1);  // the slot step t-1 used
-    LDS_PTR(const uint8_t) sa = lds + cur * T::kStage;
-    LDS_PTR(const uint8_t) sb = sa + T::kStageA;
+          for (int i = 0; i < T::kFragM; ++i) fa[s][i] = read_a<T>(pa, row_a + 32 * i, s, lane);
 #pragma unroll
-    for (int s = 0; s < T::kSub; ++s) {
-      const int c = s & 1, n = c ^ 1;
-      if (s + 1 < T::kSub) {
+          for (int j = 0; j < T::kFragN; ++j) fb[s][j] = read_b<T>(pb, col_b + 32 * j, s, lane);
+        }
+      };
+      auto multiply = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, s + 1, lane);
+        for (int s = 0; s < T::kSub; ++s)
 #pragma unroll
-        for (int j = 0; j < T::kFragN; ++j) b[n][j] = read_b<T>(sb, col_b + 32 * j, s + 1, lane);
-      } else {
-        // Step t+1's copies land and every wave is done with the slot the
-        // next issue overwrites; then its first fragments are read while the
-        // last MFMAs of step t run. After the last step these reads fetch
-        // stale values that are never used.
-        wait_step(t + 1);
+          for (int i = 0; i < T::kFragM; ++i)
+#pragma unroll
+            for (int j = 0; j < T::kFragN; ++j)
+              acc[i][j] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+      };
+      // A workgroup barrier the scheduler moves nothing across (it had
+      // hoisted an MFMA of the next phase above it).
+      auto phase_end = []() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
         __syncthreads();
-        LDS_PTR(const uint8_t) na = lds + nxt * T::kStage;
-#pragma unroll
-        for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lane);
-#pragma unroll
-        for (int j = 0; j < T::kFragN; ++j)
-          b[n][j] = read_b<T>(na + T::kStageA, col_b + 32 * j, 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // Both groups pass 2*steps barriers here, then meet again at the
+      // first barrier of the store.
+      if (group == 0) {
+        for (int t = 0; t < steps; ++t) {
+          issue(t + S - 1, (t + S - 1) % S);  // into the slot step t-1 used
+          load_frags(t % S);
+          phase_end();  // phase 2t: reads
+          multiply();
+          wait_step(t + 1);
+          phase_end();  // phase 2t+1: MFMAs
+        }
+      } else {
+        phase_end();  // phase 0: group 0's first reads
+        for (int t = 0; t < steps; ++t) {
+          issue(t + S - 1, (t + S - 1) % S);
+          load_frags(t % S);
+          wait_step(t + 1);
+          phase_end();  // phase 2t+1: reads
+          multiply();   // phase 2t+2: MFMAs
+          if (t + 1 < steps) phase_end();
+        }
       }
-#pragma unroll
-      for (int i = 0; i < T::kFragM; ++i)
-#pragma unroll
-        for (int j = 0; j < T::kFragN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
-      interleave_hint<T>();
     }
-    cur = nxt;
+  } else {
+    bf16x8 a[2][T::kFragM], b[2][T::kFragN];
+#pragma unroll
+    for (int i = 0; i < T::kFragM; ++i) a[0][i] = read_a<T>(lds, row_a + 32 * i, 0, lane);
+#pragma unroll
+    for (int j = 0; j < T::kFragN; ++j)
+      b[0][j] = read_b<T>(lds + T::kStageA, col_b + 32 * j, 0, lane);
+
+    int cur = 0;  // ring slot of step t
+    for (int t = 0; t < steps; ++t) {
+      const int nxt = cur + 1 == S ? 0 : cur + 1;
+      issue(t + S - 1, cur == 0 ? S - 1 : cur - 1);  // the slot step t-1 used
+      LDS_PTR(const uint8_t) sa = lds + cur * T::kStage;
+      LDS_PTR(const uint8_t) sb = sa + T::kStageA;
+#pragma unroll
+      for (int s = 0; s < T::kSub; ++s) {
+        const int c = s & 1, n = c ^ 1;
+        if (s + 1 < T::kSub) {
+#pragma unroll
+          for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(sa, row_a + 32 * i, s + 1, lane);
+#pragma unroll
+          for (int j = 0; j < T::kFragN; ++j) b[n][j] = read_b<T>(sb, col_b + 32 * j, s + 1, lane);
+        } else {
+          // Step t+1's copies land and every wave is done with the slot the
+          // next issue overwrites; then its first fragments are read while the
+          // last MFMAs of step t run. After the last step these reads fetch
+          // stale values that are never used.
+          wait_step(t + 1);
+          __syncthreads();
+          LDS_PTR(const uint8_t) na = lds + nxt * T::kStage;
+#pragma unroll
+          for (int i = 0; i < T::kFragM; ++i) a[n][i] = read_a<T>(na, row_a + 32 * i, 0, lane);
+#pragma unroll
+          for (int j = 0; j < T::kFragN; ++j)
+            b[n][j] = read_b<T>(na + T::kStageA, col_b + 32 * j, 0, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < T::kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < T::kFragN; ++j)
+            acc[i][j] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+        interleave_hint<T>();
+      }
+      cur = nxt;
+    }
   }
 
   // Writing C. Each wave stages its block through its share of the (now
@@ -486,11 +565,16 @@ bool mfma_bf16_nk_supports(int64_t M, int64_t N, int64_t K, int mis_a, int mis_b
   return K % 8 == 0 && K >= 8 && mis_a == 0 && mis_b == 0;
 }
 
-// An N x K B takes 64 k per step, double-buffered: 128-byte row pieces of
-// both operands (one cache line each) instead of 64-byte halves measured 2-9%
-// faster there; a K x N B keeps 32 k per step and four stages.
+// A K x N B takes 32 k per step over four slots (the ping-pong schedule). An
+// N x K B does too when the tiles take several rounds of the CUs (8192^3:
+// 899.6 against 926.5 us for 64 k per step, double-buffered, without the
+// ping-pong); in a single round it takes 64 k per step over two slots, whose
+// 128-byte row pieces of both operands (one cache line each) are faster
+// there (4096^3: 114.1 against 115.7 us).
 template <bool BNK, bool AKM>
-using LargeTile = Cfg<256, 256, 2, 4, BNK ? 64 : 32, BNK ? 2 : 4, BNK, AKM>;
+using LargeTile = Cfg<256, 256, 2, 4, 32, 4, BNK, AKM>;
+template <bool AKM>
+using LargeTileNkOneRound = Cfg<256, 256, 2, 4, 64, 2, true, AKM>;
 template <bool BNK, bool AKM>
 using SmallTile = Cfg<128, 128, 2, 4, 32, 4, BNK, AKM>;
 
@@ -505,9 +589,13 @@ hipError_t launch_mfma_bf16(const uint16_t* A, const uint16_t* B, float* C,
 template <bool BNK, bool AKM>
 hipError_t launch_layout(const uint16_t* A, const uint16_t* B, void* D, int M, int N, int K,
                          const Epilogue& e, hipStream_t s) {
-  return use_large_tiles(M, N, kLargeTileFillBf16)
-             ? launch_tile<LargeTile<BNK, AKM>>(A, B, D, M, N, K, e, s)
-             : launch_tile<SmallTile<BNK, AKM>>(A, B, D, M, N, K, e, s);
+  if (!use_large_tiles(M, N, kLargeTileFillBf16))
+    return launch_tile<SmallTile<BNK, AKM>>(A, B, D, M, N, K, e, s);
+  if constexpr (BNK) {
+    const int64_t tiles = ((M + 255) / 256) * static_cast<int64_t>((N + 255) / 256);
+    if (tiles <= kCUs) return launch_tile<LargeTileNkOneRound<AKM>>(A, B, D, M, N, K, e, s);
+  }
+  return launch_tile<LargeTile<BNK, AKM>>(A, B, D, M, N, K, e, s);
 }
 
 hipError_t launch_mfma_bf16_epi(const uint16_t* A, const uint16_t* B, bool b_nk, bool a_km,
