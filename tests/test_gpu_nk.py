@@ -157,9 +157,9 @@ def test_full_size_linear_gelu():
 @pytest.mark.parametrize("shape", [(4000, 3900, 200), (5000, 4600, 200), (5000, 4600, 4096)])
 def test_large_tiles_in_one_round_and_in_several(shape):
     """256 x 256 tiles with B stored N x K: 4000 x 3900 fills exactly one
-    round of the CUs (64 k per step over two slots), 5000 x 4600 two rounds
-    (32 k per step over four slots, the ping-pong schedule); partial tiles
-    in M and N, and a partial last K step (K = 200) or none (K = 4096)."""
+    round of the CUs, 5000 x 4600 two rounds; partial tiles in M and N, and
+    a partial last K step (K = 200: the interleaved loop) or none (K = 4096:
+    the ping-pong schedule)."""
     M, N, K = shape
     log(f"case nk large tiles {shape}")
     rng = np.random.default_rng(M + N + K + 7)
