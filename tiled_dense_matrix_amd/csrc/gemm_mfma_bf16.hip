@@ -111,24 +111,28 @@ struct Cfg {
   static_assert(kLdsBytes <= 160 * 1024, "LDS per workgroup");
 };
 
-// Row m of A, chunk c (8 k values) is stored at chunk c ^ swz_a(m): the rows
-// one 16-byte read instruction touches then cover every bank once. With
-// 64-byte rows, four rows share a 256-byte bank window, so rows that differ
-// in bits 2-3 take different chunks (measured conflict-free with rocprof's
-// SQ_LDS_BANK_CONFLICT; a swizzle on bits 1 and 3 was not).
+// Row m of A, chunk c (8 k values) is stored at chunk c ^ swz_a(m). A
+// fragment read takes 16 rows x 4 chunks (lane l: row l%16, chunk l/16);
+// with 64-byte rows a probe counting SQ_LDS_BANK_CONFLICT found this pattern
+// conflict-free with the swizzle on row bits 1-2, and twice the cycles with
+// it on bits 2-3 (right for a 32-row x 2-chunk pattern) or on bits 0-1.
 template <int kChunks>
 __device__ __forceinline__ int swz_a(int m) {
   if constexpr (kChunks == 8)
     return (m ^ (m >> 3)) & 7;
   else
-    return (m >> 2) & 3;
+    return (m >> 1) & 3;
 }
 // Row k of a k-major tile (B stored K x N, or A stored K x M), chunk c at
-// c ^ swz_b(k). One transposing read of 32 lanes touches 16 columns (two
-// chunks) of rows k..k+3 and k+8..k+11: bits 0-1 of k spread the four rows
-// four chunks apart, bit 3 moves the second four by two, so the 32 lanes
-// cover every bank once.
-__device__ __forceinline__ int swz_b(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
+// c ^ swz_b(k). A transposing read serves 16 lanes (128 bytes) at a time;
+// each 16-lane group touches 16 columns (two chunks) of rows k..k+3, which
+// bits 0-1 of k place in four different chunk pairs of one 128-byte bank
+// window. The groups reading rows k and k+8 differ in bit 3, which moves
+// the second to the other half of a 256-byte window. (Without the bit-1
+// term, rows k and k+2 shared banks: 40% of the LDS cycles were conflicts.)
+__device__ __forceinline__ int swz_b(int k) {
+  return ((k & 3) << 2) ^ (((k >> 1) & 1) << 1) ^ (((k >> 3) & 1) << 3);
+}
 
 // Per-lane byte offsets of this wave's copy instructions; the K step only
 // moves the scalar base pointers.
