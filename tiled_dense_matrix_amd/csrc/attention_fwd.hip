@@ -6,24 +6,28 @@
 // attention notes, "online softmax" and "why FlashAttention saves memory").
 //
 // Per (batch*head, 256-query block) one workgroup of eight waves; wave w owns
-// queries q0 + 32w .. q0 + 32w + 31 and walks the keys in blocks of 64:
-//   1. S^T = K Q^T on v_mfma_f32_32x32x16_bf16, keys as rows: A = 32 rows of
-//      the K block (16-byte LDS reads), B = the wave's queries, held in
-//      registers for the whole kernel. Lane l then holds query l%32 and, of
-//      each 32-key half, keys 8*(v/4) + 4*(l/32) + v%4 (v = 0..15);
+// queries q0 + 32w .. q0 + 32w + 31, as two groups of 16 (qg), and walks the
+// keys in blocks of 64, on v_mfma_f32_16x16x32_bf16 (at the part's power
+// limit a loop of these sustains 13% more FLOPs than one of 32x32x16 on
+// random operands; this kernel: 955 -> 927 us, causal 550 -> 540 us):
+//   1. S^T = K Q^T, keys as rows, in 16 x 16 tiles: A = 16 rows of the K
+//      block (16-byte LDS reads), B = 16 queries, held in registers for the
+//      whole kernel. Lane l then holds, for query 16*qg + l%16, keys
+//      16*kt + 4*(l/16) + v of the block (kt, v = 0..3): a query's 64 scores
+//      sit in four lanes, 16 each;
 //   2. online softmax per query, in base 2 (scores times scale * log2 e):
-//      block maximum over the lane's 32 values and its partner lane l^32,
+//      block maximum over the lane's 16 values and lanes l^16, l^32,
 //      m_new = max(m, block max), alpha = 2^(m - m_new), p = 2^(s - m_new),
 //      l = l * alpha + sum p, O *= alpha (blocks without masked keys first
 //      try the current m, with the scale folded into p's exponent, one FMA
 //      per score, and fall back to the block maximum only when a sum shows
 //      that some score passed m + 8);
-//   3. O^T += V^T P^T: the p values, rounded to bf16, already sit where the
-//      MFMA's B operand wants them, for the key order of step 1 (within a
-//      16-key window lane l holds keys 4*(l/32) + 0..3 and 8 + 4*(l/32) +
-//      0..3); the A operand V^T is read from the row-major V block with two
-//      ds_read_b64_tr_b16 that return exactly those keys for row d = l%32.
-//      Any key order works as long as both operands share it.
+//   3. O^T += V^T P^T over 32 keys at a time: the p values, rounded to bf16,
+//      already sit where the MFMA's B operand wants them (element e of lane
+//      l: key 16*(2pp + e/4) + 4*(l/16) + e%4); the A operand V^T is read
+//      from the row-major V block with two ds_read_b64_tr_b16 that return
+//      exactly those keys for d = 16*dt + l%16. Any key order works as long
+//      as both operands share it.
 // The waves form two groups, waves 0-3 and 4-7 (wave w runs on SIMD w % 4,
 // so each SIMD holds one of each). Each block takes two phases separated by
 // workgroup barriers: while one group issues the MFMAs of steps 3 (previous
@@ -35,16 +39,10 @@
 // O = O / l is stored in bf16 and lse = (m + log2 l) * ln 2 (the natural-log
 // logsumexp of the scaled scores) in fp32.
 //
-// LDS rows are head_dim * 2 bytes. K: 16-byte chunk c of row r sits at
-// c ^ f(r), f(r) = 2*(r % 8) + (r / 8) % 2 (d = 128) or (r >> 1) & 7
-// (d = 64): the 16 rows one 16-byte read phase touches fall in 16
-// different chunks, and so do rows r..r+7 read at chunks c and c+1. V:
-// chunk c of row r at c ^ 4*(r % 4) (d = 128) or c ^ 4*((r / 2) % 2)
-// (d = 64): the four rows and four chunks that 32 lanes of a transposing
-// read touch land in 16 distinct chunks of the bank space (with
-// c ^ 2*(r % 4), rows r and r+1 shared a chunk set: rocprof counted
-// 6.7e7 bank-conflict cycles per call at sequence 4096, 32% of the LDS
-// active cycles; now 0).
+// LDS rows are head_dim * 2 bytes; the swizzles (swz_k, swz_v) were each
+// checked with a probe counting bank conflicts for the exact read pattern
+// (with the swizzles of the earlier 32 x 32 layout, half of these reads
+// conflicted); the kernel counts none.
 //
 // Ragged sizes: key rows past n_kv load row n_kv - 1 and are masked out
 // (score -inf; their V rows are zeroed in LDS, so an infinite value in row
@@ -63,7 +61,8 @@ namespace tdm {
 namespace {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -82,28 +81,31 @@ struct AttnCfg {
   static constexpr int kLdsBytes = kStages * kStage;
   static constexpr int kRowsPerCopy = 1024 / kRow;
   static constexpr int kCopies = kBlock / 1024 / kWaves;  // per wave, per operand
-  static constexpr int kKSteps = D / 16;       // MFMA k-steps of Q K^T
-  static constexpr int kDBlocks = D / 32;      // 32-row blocks of O^T
+  static constexpr int kKSteps = D / 32;       // MFMA k-steps of K Q^T
+  static constexpr int kDTiles = D / 16;       // 16-row tiles of O^T
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
   static_assert(kCopies * kWaves * 1024 == kBlock, "whole 1 KB copies");
 };
 
+// LDS swizzles (16-byte chunk c of row r at c ^ swz(r)), each measured with
+// a probe counting SQ_LDS_BANK_CONFLICT for exactly the read pattern below.
+// K rows are read 16 rows x 4 chunks per instruction (lane l: row l%16,
+// chunk 4ks + l/16); V rows by transposing reads, 4 rows x 2 chunks per
+// 16 lanes (rows 4(l/16) + 0..3). Both depend on the row modulo 8 only.
 template <int D>
 __device__ __forceinline__ int swz_k(int r) {
   if constexpr (D == 128)
-    return ((r & 7) << 1) | ((r >> 3) & 1);
+    return 4 * (r & 3) + ((r >> 1) & 3);
   else
-    return (r >> 1) & 7;
+    return 5 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1);
 }
 template <int D>
 __device__ __forceinline__ int swz_v(int r) {
   if constexpr (D == 128)
-    return (r & 3) << 2;
+    return ((r & 3) << 2) ^ (((r >> 1) & 1) << 1) ^ (((r >> 2) & 1) << 3);
   else
-    return ((r >> 1) & 1) << 2;
+    return ((r & 1) << 2) ^ (((r >> 1) & 1) << 1) ^ (((r >> 2) & 1) << 2);
 }
-
-typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
 
 // Workgroup id -> (query block, head). Without the mask every workgroup does
 // the same work; the query blocks of a head share its K and V, so they go to
@@ -152,7 +154,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int lr = lane & 31, lg = lane >> 5;
+  const int lq = lane & 15, lg = lane >> 4;
   const int n_qblocks = (n_q + kBQ - 1) / kBQ;
   int qb, head;
   work_item(static_cast<int>(blockIdx.x), n_qblocks, n_heads, causal, qb, head);
@@ -162,27 +164,33 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   const uint16_t* Kh = K + bh * n_kv * D;
   const uint16_t* Vh = V + bh * n_kv * D;
 
-  // This lane's query and its Q operand: d = 16*ks + 8*lg + 0..7.
-  const int query = q0 + 32 * wave + lr;
-  bf16x8 qf[T::kKSteps];
-  {
-    const uint16_t* qrow = Qh + static_cast<int64_t>(min(query, n_q - 1)) * D;
+  // The wave's 32 queries form two groups of 16 (qg); lane l holds query
+  // 16*qg + l%16 of each. Its Q operand for k-step ks: d = 32*ks + 8*(l/16)
+  // + 0..7.
+  const int qbase = q0 + 32 * wave + lq;  // + 16 qg
+  bf16x8 qf[2][T::kKSteps];
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg) {
+    const uint16_t* qrow = Qh + static_cast<int64_t>(min(qbase + 16 * qg, n_q - 1)) * D;
 #pragma unroll
     for (int ks = 0; ks < T::kKSteps; ++ks)
-      qf[ks] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 16 * ks + 8 * lg));
-    // Take delivery of Q here. Left to itself the compiler waits for these
-    // loads at their first use inside the key loop, on every iteration, and
-    // since memory operations complete in issue order that wait also holds
-    // each block until the next block's K and V copies have landed.
-#pragma unroll
-    for (int ks = 0; ks < T::kKSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
+      qf[qg][ks] =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + 32 * ks + 8 * lg));
   }
+  // Take delivery of Q here. Left to itself the compiler waits for these
+  // loads at their first use inside the key loop, on every iteration, and
+  // since memory operations complete in issue order that wait also holds
+  // each block until the next block's K and V copies have landed.
+#pragma unroll
+  for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+    for (int ks = 0; ks < T::kKSteps; ++ks) asm volatile("" ::"v"(qf[qg][ks]));
 
   // Keys this workgroup visits: all, or (causal) up to its last query.
   const int kv_end = causal ? min(n_kv, q0 + kBQ) : n_kv;
   const int blocks = (kv_end + kBKV - 1) / kBKV;
 
-  // Copy plan: copy j of this wave fills rows (wave + 4j) * kRowsPerCopy ..
+  // Copy plan: copy j of this wave fills rows (wave + 8j) * kRowsPerCopy ..
   // of the block; lane L takes row +L/kChunks, LDS chunk L%kChunks.
   uint32_t off_k[T::kCopies], off_v[T::kCopies];
   const int crow = lane / T::kChunks, cslot = lane % T::kChunks;
@@ -219,32 +227,33 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     }
   };
 
-  // Per-lane LDS offsets, fixed for the whole kernel: the K reads of k-step
-  // ks (row lr of a 32-row half; the other half is 32 rows further) and the
-  // transposing V reads of d-block db (key rows 4*(G/2) + i/4 of a 16-key
-  // window; the window and the +8 rows of the second read are further
-  // rows). The swizzles see only the row modulo 16, so these offsets hold
-  // for every half and window (computing them per read cost 4%).
-  int koff[T::kKSteps], voff[T::kDBlocks];
+  // Per-lane LDS offsets, fixed for the whole kernel. K read of k-step ks:
+  // row l%16 of a 16-key tile, chunk 4ks + l/16. Transposing V reads of
+  // d-tile dt: key rows 4*(l/16) + (l%16)/4 of a 16-key tile, columns
+  // 16dt + 4*(l%4) .. +3; lane l receives, for its d = 16dt + l%16, the four
+  // keys 4*(l/16) + 0..3. The swizzles see only the row modulo 8, so the
+  // tiles' other rows add constant offsets.
+  int koff[T::kKSteps], voff[T::kDTiles];
 #pragma unroll
   for (int ks = 0; ks < T::kKSteps; ++ks)
-    koff[ks] = lr * T::kRow + (((2 * ks + lg) ^ swz_k<D>(lr)) << 4);
+    koff[ks] = lq * T::kRow + (((4 * ks + lg) ^ swz_k<D>(lq)) << 4);
   {
-    const int G = lane >> 4, i = lane & 15;
-    const int r = 4 * (G >> 1) + (i >> 2);
+    const int r = 4 * lg + (lq >> 2);
 #pragma unroll
-    for (int db = 0; db < T::kDBlocks; ++db) {
-      const int col = 32 * db + 16 * (G & 1) + 4 * (i & 3);
-      voff[db] = r * T::kRow + (((col >> 3) ^ swz_v<D>(r)) << 4) + ((col & 7) << 1);
+    for (int dt = 0; dt < T::kDTiles; ++dt) {
+      const int col = 16 * dt + 4 * (lq & 3);
+      voff[dt] = r * T::kRow + (((col >> 3) ^ swz_v<D>(r)) << 4) + ((col & 7) << 1);
     }
   }
 
-  f32x16 acc_o[T::kDBlocks];
+  f32x4 acc_o[2][T::kDTiles];
 #pragma unroll
-  for (int db = 0; db < T::kDBlocks; ++db)
+  for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc_o[db][v] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+    for (int dt = 0; dt < T::kDTiles; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc_o[qg][dt][v] = 0.f;
+  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
   // Keys this wave needs: with the mask, blocks past its last query are
   // skipped (the workgroup still walks them for the copies and barriers).
@@ -252,8 +261,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
       causal ? min(blocks, (q0 + 32 * wave + 32 + kBKV - 1) / kBKV) : blocks;
   const int group = wave >> 2;  // 0: waves 0-3, 1: waves 4-7 (one of each per SIMD)
   constexpr float kSlack = 8.0f;
-  f32x16 s[2];
-  bf16x8 pop[4];  // p of the last softmax phase in bf16, window w16 = keys 16*w16 ..
+  // Scores of the block: s[qg][kt][v] = key 16*kt + 4*(lane/16) + v, query
+  // 16*qg + lane%16 (a 16 x 16 accumulator, keys as rows).
+  f32x4 s[2][4];
+  // p of the last softmax phase in bf16, the B operand of O^T += V^T P^T for
+  // the 32 keys of tiles 2pp and 2pp+1: element e = key 16*(2pp + e/4) +
+  // 4*(lane/16) + e%4, the key order the V reads use.
+  bf16x8 pop[2][2];
 
   // Matrix phase for block t: O^T += V^T P^T of block t-1, then S^T of block
   // t, at raised issue priority so the SIMD serves the MFMAs first.
@@ -262,130 +276,146 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
     if (t >= 1 && t <= wave_blocks) {
       LDS_PTR(const uint8_t) vblk = lds + ((t - 1) % kStages) * T::kStage + T::kBlock;
 #pragma unroll
-      for (int w16 = 0; w16 < 4; ++w16) {
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-        for (int db = 0; db < T::kDBlocks; ++db) {
-          LDS_PTR(const uint8_t) vw = vblk + 16 * w16 * T::kRow + voff[db];
+        for (int dt = 0; dt < T::kDTiles; ++dt) {
+          LDS_PTR(const uint8_t) vw = vblk + 32 * pp * T::kRow + voff[dt];
           const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 8 * T::kRow));
+          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_PTR(s16x4))(vw + 16 * T::kRow));
           const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const u32x4 av = {l2.x, l2.y, h2.x, h2.y};
-          acc_o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), pop[w16],
-                                                              acc_o[db], 0, 0, 0);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, u32x4{l2.x, l2.y, h2.x, h2.y});
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg)
+            acc_o[qg][dt] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pop[qg][pp], acc_o[qg][dt], 0, 0, 0);
         }
-      }
-      // V reads eight ahead of the MFMAs that use them.
+      // V reads four fragments ahead of the MFMAs that use them.
+      constexpr int kFrags = 2 * T::kDTiles;
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int g = 0; g < 4 * T::kDBlocks - 4; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int g = 0; g < kFrags - 4; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     }
     if (t < wave_blocks) {
       LDS_PTR(const uint8_t) kblk = lds + (t % kStages) * T::kStage;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[h][v] = 0.f;
-      // The two halves' accumulator chains alternate.
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s[qg][kt][v] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < T::kKSteps; ++ks)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 32 * h * T::kRow + koff[ks]);
-          s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[ks], s[h],
-                                                         0, 0, 0);
+        for (int kt = 0; kt < 4; ++kt) {
+          const u32x4 a = *(LDS_PTR(const u32x4))(kblk + 16 * kt * T::kRow + koff[ks]);
+#pragma unroll
+          for (int qg = 0; qg < 2; ++qg)
+            s[qg][kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                               qf[qg][ks], s[qg][kt], 0, 0, 0);
         }
       // K reads eight ahead.
+      constexpr int kReads = 4 * T::kKSteps;
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int g = 0; g < 2 * T::kKSteps - 8; ++g) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      for (int g = 0; g < kReads - 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // Softmax phase for block t (online softmax in base 2, as before).
+  // Softmax phase for block t (online softmax in base 2), for both query
+  // groups. A query's 64 scores sit in four lanes (l%16 equal), 16 each.
   auto softmax = [&](int t) __attribute__((always_inline)) {
     if (t < 0 || t >= wave_blocks) return;
     const int kb0 = t * kBKV;
-    const bool general =
-        !(scale_log2 >= 0.f) || kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
-    float psum = 0.f, alpha = 1.f, m_new = m_run;
-    auto exps = [&](float m_use, bool raw) __attribute__((always_inline)) {
+    const bool masked = kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave);
+    const bool general = !(scale_log2 >= 0.f) || masked;
+    float psum[2] = {0.f, 0.f}, alpha[2] = {1.f, 1.f}, m_new[2] = {m_run[0], m_run[1]};
+    auto exps = [&](int qg, float m_use, bool raw) __attribute__((always_inline)) {
       // Exponents, exponentials, then four partial sums: independent work
       // in each stage, so one wave alone on its SIMD keeps issuing.
-      float p[32];
+      float p[16];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float x = s[i >> 4][i & 15];
+      for (int i = 0; i < 16; ++i) {
+        const float x = s[qg][i >> 2][i & 3];
         p[i] = raw ? __builtin_fmaf(x, scale_log2, -m_use) : x - m_use;
       }
 #pragma unroll
-      for (int i = 0; i < 32; ++i) p[i] = __builtin_amdgcn_exp2f(p[i]);
+      for (int i = 0; i < 16; ++i) p[i] = __builtin_amdgcn_exp2f(p[i]);
       float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 32; ++i) part[i & 3] += p[i];
-      psum = (part[0] + part[1]) + (part[2] + part[3]);
+      for (int i = 0; i < 16; ++i) part[i & 3] += p[i];
+      psum[qg] = (part[0] + part[1]) + (part[2] + part[3]);
 #pragma unroll
-      for (int i = 0; i < 32; ++i) pop[i >> 3][i & 7] = static_cast<__bf16>(p[i]);
+      for (int i = 0; i < 16; ++i) pop[qg][i >> 3][i & 7] = static_cast<__bf16>(p[i]);
     };
-    auto rebase = [&](float bmax, bool raw) __attribute__((always_inline)) {
+    auto rebase = [&](int qg, float bmax, bool raw) __attribute__((always_inline)) {
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
       bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-      m_new = bmax > m_run + kSlack ? bmax : m_run;
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // all masked so far
-      alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      exps(m_use, raw);
+      m_new[qg] = bmax > m_run[qg] + kSlack ? bmax : m_run[qg];
+      const float m_use = m_new[qg] == -INFINITY ? 0.f : m_new[qg];  // all masked so far
+      alpha[qg] = __builtin_amdgcn_exp2f(m_run[qg] - m_use);
+      exps(qg, m_use, raw);
+    };
+    auto block_max = [&](int qg) __attribute__((always_inline)) {
+      float bmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) bmax = fmaxf(bmax, s[qg][kt][v]);
+      return bmax;
     };
     if (general) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int qg = 0; qg < 2; ++qg)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) s[h][v] *= scale_log2;
-      if (kb0 + kBKV > n_kv || (causal && kb0 + kBKV - 1 > q0 + 32 * wave)) {
-        const int lim = causal ? min(n_kv - 1, query) : n_kv - 1;  // last visible key
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s[qg][kt][v] *= scale_log2;
+      if (masked) {
         // This lane's first key of the block, made here (an opaque value), so
-        // the 32 per-score key offsets are not kept in registers across the
-        // loop.
+        // the per-score key offsets are not kept in registers across the loop.
         int key0 = kb0 + 4 * lg;
         asm volatile("" : "+v"(key0));
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int qg = 0; qg < 2; ++qg) {
+          const int lim = causal ? min(n_kv - 1, qbase + 16 * qg) : n_kv - 1;  // last visible key
 #pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int key = key0 + 32 * h + 8 * (v >> 2) + (v & 3);
-            s[h][v] = key > lim ? -INFINITY : s[h][v];
-          }
+          for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              s[qg][kt][v] = key0 + 16 * kt + v > lim ? -INFINITY : s[qg][kt][v];
+        }
       }
-      float bmax = -INFINITY;
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
-      rebase(bmax, false);
+      for (int qg = 0; qg < 2; ++qg) rebase(qg, block_max(qg), false);
     } else {
-      exps(m_run, true);
-      if (__builtin_amdgcn_ballot_w64(!(psum <= 256.f)) != 0) {
-        float bmax = -INFINITY;
+      exps(0, m_run[0], true);
+      exps(1, m_run[1], true);
+      if (__builtin_amdgcn_ballot_w64(!(psum[0] <= 256.f) || !(psum[1] <= 256.f)) != 0) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) bmax = fmaxf(bmax, s[h][v]);
-        rebase(bmax * scale_log2, true);
+        for (int qg = 0; qg < 2; ++qg) rebase(qg, block_max(qg) * scale_log2, true);
       }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
 #pragma unroll
-      for (int db = 0; db < T::kDBlocks; ++db)
+    for (int qg = 0; qg < 2; ++qg) {
+      l_run[qg] = l_run[qg] * alpha[qg] + psum[qg];
+      m_run[qg] = m_new[qg];
+    }
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.0f || alpha[1] != 1.0f) != 0) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc_o[db][v] *= alpha;
+      for (int qg = 0; qg < 2; ++qg)
+#pragma unroll
+        for (int dt = 0; dt < T::kDTiles; ++dt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc_o[qg][dt][v] *= alpha[qg];
     }
   };
 
@@ -428,24 +458,27 @@ __global__ __launch_bounds__(kThreads, 1) void attention_fwd_kernel(
   }
 
   __builtin_amdgcn_s_setprio(0);
-  // O = acc / l (bf16), lse = (m + log2 l) * ln 2. Lane l holds query lr,
-  // d = 32*db + 8*(v/4) + 4*lg + v%4: four consecutive d per 8-byte store.
-  l_run += __shfl_xor(l_run, 32);  // the row's two halves
-  if (query < n_q) {
-    const float inv = 1.0f / l_run;
-    uint16_t* orow = O + bh * n_q * D + static_cast<int64_t>(query) * D;
+  // O = acc / l (bf16), lse = (m + log2 l) * ln 2. Lane l holds query
+  // 16*qg + l%16 and d = 16*dt + 4*(l/16) + v: four consecutive d per
+  // 8-byte store. A query's normalizer is the sum over its four lanes.
 #pragma unroll
-    for (int db = 0; db < T::kDBlocks; ++db)
+  for (int qg = 0; qg < 2; ++qg) {
+    float l_all = l_run[qg] + __shfl_xor(l_run[qg], 16);
+    l_all += __shfl_xor(l_all, 32);
+    const int query = qbase + 16 * qg;
+    if (query < n_q) {
+      const float inv = 1.0f / l_all;
+      uint16_t* orow = O + bh * n_q * D + static_cast<int64_t>(query) * D;
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d = 32 * db + 8 * q4 + 4 * lg;
+      for (int dt = 0; dt < T::kDTiles; ++dt) {
         bf16x4 ov;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc_o[db][4 * q4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d) = ov;
+        for (int e = 0; e < 4; ++e) ov[e] = static_cast<__bf16>(acc_o[qg][dt][e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 16 * dt + 4 * lg) = ov;
       }
-    if (lse != nullptr && lg == 0)
-      lse[bh * n_q + query] = (m_run + __log2f(l_run)) * 0.693147180559945309f;
+      if (lse != nullptr && lg == 0)
+        lse[bh * n_q + query] = (m_run[qg] + __log2f(l_all)) * 0.693147180559945309f;
+    }
   }
 }
 
