@@ -143,6 +143,23 @@ def test_large_tile_ragged(kind, shape):
     assert np.array_equal(gpu_product(kind, A, B, P.MFMA).astype(np.float64), oracle.gemm(A, B))
 
 
+@pytest.mark.parametrize("K", [32, 64, 96, 128, 160])
+def test_large_tiles_with_few_k_steps(K):
+    """bf16 256 x 256 tiles (3900 x 4000: one round, partial tiles) with
+    K a multiple of 32 but fewer steps than, or about as many as, the four
+    ring slots: the ping-pong schedule's tail, where later copies are not
+    issued and every wait is for all copies. Integer inputs, bit for bit,
+    and random inputs over the whole output."""
+    M, N = 3900, 4000
+    log(f"case large tiles few k steps bf16 {M}x{N}x{K}")
+    rng = np.random.default_rng(K + 3)
+    A = inputs.small_int_matrix(rng, (M, K), kind="bf16")
+    B = inputs.small_int_matrix(rng, (K, N), kind="bf16")
+    assert np.array_equal(gpu_product("bf16", A, B, P.MFMA).astype(np.float64), oracle.gemm(A, B))
+    A, B = random_inputs("bf16", M, N, K, seed=K + 11)
+    check_full("bf16", A, B, gpu_product("bf16", A, B, P.MFMA), f"bf16/{M}x{N}x{K}/MFMA")
+
+
 @pytest.mark.parametrize("kind,shape,path", list(_ragged_cases()))
 def test_integer_inputs_bit_exact(kind, shape, path):
     """Small integers: every partial sum is an exactly representable integer."""
