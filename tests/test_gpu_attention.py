@@ -152,7 +152,7 @@ def test_run_to_run_bitwise_determinism(causal):
                for _ in range(3))
     log(f"case attention determinism causal={causal}")
     ref = tdm.attention_fwd(Q, K, V, causal=causal).clone()
-    for _ in range(3):
+    for _ in range(100):
         assert torch.equal(tdm.attention_fwd(Q, K, V, causal=causal), ref)
 
 

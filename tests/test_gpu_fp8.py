@@ -349,7 +349,7 @@ def test_run_to_run_bitwise_determinism(shape):
     a, b, s_a, s_b = dev8(A), dev8(B), dev8(sa), dev8(sb)
     log(f"case fp8 determinism {shape}")
     ref = tdm.gemm_fp8(a, b, F.E4M3, F.E4M3, s_a, s_b, out_dtype=torch.float32).clone()
-    for _ in range(3):
+    for _ in range(100):
         again = tdm.gemm_fp8(a, b, F.E4M3, F.E4M3, s_a, s_b, out_dtype=torch.float32)
         assert torch.equal(again, ref)
 
